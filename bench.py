@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the frame-wise Gated DeltaNet forward on one MI355X.
+
+A step is one gdn_fwd over the whole workload (for the streaming workload:
+the chain of gdn_chunk_step calls), inputs already resident in HBM.  Prints
+ONE JSON line: tokens/s per GDN layer, the dominant kernel against the HBM
+roofline (HIP events recorded by the library around each kernel, inside the
+timed region), and the fp64 CPU oracle timed on this host as a baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload clip_241f]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+# Algorithmic bytes per token-head that a kernel must move by the method's own
+# definition (bf16 q/k/v = 224 B each, fp32 g and beta 4 B each, o 448 B fp32 /
+# 224 B bf16, the prep scalars 16 B), and per (batch, head) for state in/out.
+STATE_BYTES = 112 * 112 * 4
+
+
+def stage_algorithmic_bytes(stage: str, o_bytes: int, mfma: bool) -> int:
+    """Per token-head algorithmic bytes of one kernel stage."""
+    if stage == "prep":
+        return 2 * 224 + 8 + 16      # reads q, k, g, beta; writes 4 scalars
+    if stage == "intra":
+        return 224 + 224 + 16 if mfma else 224 + 224 + 12  # reads q, k (+v on portable) and scalars
+    if stage == "state":
+        return (3 * 224 + 16 + o_bytes) if mfma else (224 + 12)  # fused state pass + output on MFMA
+    if stage == "output":
+        return 2 * 224 + 12 + o_bytes
+    raise KeyError(stage)
+
+
+def path_algorithmic_bytes(o_bytes: int) -> int:
+    return 3 * 224 + 8 + o_bytes
+
+
+def flops_per_token_head(C: int = 80, d: int = 112) -> float:
+    """Chunked-form flops per token-head: 6 d^2 + 5 C d + C^2 / 3 (triangles once)."""
+    return 6 * d * d + 5 * C * d + C * C / 3
+
+
+def cpu_baseline(w, max_tokens: int):
+    """fp64 oracle on a bounded sample of the same workload: all heads, the first tokens."""
+    from hybrid_linear_attention_gdn_amd.inputs import make_inputs
+    from oracle.recurrence import default_threads, gdn_recurrence
+    T = min(w.seq_len, max_tokens)
+    inp = make_inputs(w, seq_len=T, frame_tokens=w.frame_tokens)
+    threads = min(default_threads(w.batch * w.heads), 16)
+    t0 = time.perf_counter()
+    gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, nthreads=threads, want_state=True)
+    dt = time.perf_counter() - t0
+    return {"value": w.batch * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: all {w.batch}x{w.heads} (batch, head) units, first {T} of {w.seq_len} tokens "
+                      f"({w.batch * T * w.heads} token-heads, {dt:.2f} s wall, fp64 C recurrence)",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="clip_241f")
+    ap.add_argument("--o-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--portable", action="store_true", help="time the fp32 vector-ALU kernels instead")
+    ap.add_argument("--cpu-tokens", type=int, default=13200, help="tokens of the oracle's CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the GDN forward's (batch, head) units "
+                                   "are independent and would shard without communication; run --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hybrid_linear_attention_gdn_amd import gdn
+    from hybrid_linear_attention_gdn_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    if inp.dtype == "bf16":
+        up = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+        q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(a).to(dev) for a in (inp.q, inp.k, inp.v))
+    g, beta = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
+    s0 = None if inp.state0 is None else torch.from_numpy(inp.state0).to(dev)
+    del inp
+    o_dtype = torch.float32 if args.o_dtype == "fp32" else torch.bfloat16
+    o_bytes = 448 if args.o_dtype == "fp32" else 224
+    B, T, H, d = q.shape
+    calls = w.calls
+    Tc = T // calls
+    o = torch.empty((B, T, H, d), dtype=o_dtype, device=dev)
+    st = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    p = gdn.problem(B, Tc, H, d, d, q.dtype, o_dtype, portable=args.portable)
+    ws = torch.empty(max(gdn.workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
+    mfma = bool(gdn.workspace_layout(p).mfma)
+    stream = torch.cuda.current_stream(dev)
+    if calls > 1:
+        parts = [tuple(t[:, c * Tc:(c + 1) * Tc].contiguous() for t in (q, k, v, g, beta)) for c in range(calls)]
+        o_parts = [torch.empty((B, Tc, H, d), dtype=o_dtype, device=dev) for _ in range(calls)]
+
+    def step():
+        if calls == 1:
+            gdn.gdn_fwd(q, k, v, g, beta, s0, st, o, portable=args.portable, workspace=ws, stream=stream)
+        else:
+            st.copy_(s0)
+            for c in range(calls):
+                gdn.gdn_chunk_step(*parts[c], st, st, o_parts[c], portable=args.portable, workspace=ws,
+                                   stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: B={B} T={T} H={H} d={d} calls={calls} kernels={'mfma' if mfma else 'portable'} "
+          f"warmup done", file=sys.stderr, flush=True)
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gdn.profile_begin()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    stages = gdn.profile_end()
+    ms = start.elapsed_time(end) / args.steps
+    token_heads = B * T * H
+    tokens_per_s = B * T / (ms * 1e-3)
+
+    # dominant kernel against the HBM roofline
+    dom = max(stages, key=lambda s: stages[s][0] * stages[s][1])
+    dom_ms = stages[dom][0]
+    dom_calls_per_step = stages[dom][1] / args.steps
+    launch_th = token_heads / calls
+    dom_bytes = stage_algorithmic_bytes(dom, o_bytes, mfma) * launch_th
+    if dom == "state":
+        dom_bytes += 2 * STATE_BYTES * B * H
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    path_bytes = path_algorithmic_bytes(o_bytes) * token_heads + 2 * STATE_BYTES * B * H * calls
+    path_gbs = path_bytes / (ms * 1e-3) / 1e9
+    tflops = flops_per_token_head() * token_heads / (ms * 1e-3) / 1e12
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
+    if os.path.exists(tpath):
+        try:
+            traffic = json.load(open(tpath)).get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    out = {
+        "metric": "GDN fwd tokens/s per layer (20h×112d, bf16) + % MFMA peak on 1 MI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v/beta logits, frame-wise log-decay -softplus(N(0,1)+2))",
+        "config": {"workload": f"{w.name}: {w.note}", "batch": B, "tokens": T, "heads": H, "head_dim": d,
+                   "calls_per_step": calls, "o_dtype": args.o_dtype, "kernels": "mfma" if mfma else "portable",
+                   "chunk": 80},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel_ms": round(dom_ms, 5), "launches_per_step": dom_calls_per_step},
+        "path_roofline": {"algorithmic_GBps": round(path_gbs, 1), "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+                          "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "stages_ms": {s: round(v[0], 5) for s, v in stages.items()},
+        "gdn_per_dit_forward_ms": {"x20_layers": round(20 * ms, 3), "x15_gdn_layers": round(15 * ms, 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,67 @@
+"""ctypes declarations of the C ABI in include/sanawm_gdn.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsanawm_gdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP, GDN_ERR_INTERNAL = range(6)
+GDN_F32, GDN_BF16 = 0, 1
+GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_PORTABLE_KERNELS = 1, 2, 4
+
+# every symbol include/sanawm_gdn.h declares
+EXPORTED = ("gdn_chunk_len", "gdn_workspace_bytes", "gdn_fwd", "gdn_chunk_step", "gdn_workspace_layout",
+            "gdn_profile_begin", "gdn_profile_end", "gdn_profile_stage_name",
+            "gdn_status_string", "gdn_last_error", "gdn_version")
+NUM_STAGES = 4
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
+                ("o_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [("beta", ctypes.c_size_t), ("rq", ctypes.c_size_t), ("rk", ctypes.c_size_t),
+                ("gcum", ctypes.c_size_t), ("total", ctypes.c_size_t), ("mfma", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Open libsanawm_gdn.so; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m hybrid_linear_attention_gdn_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER(Problem)
+    lib.gdn_chunk_len.restype = ctypes.c_int32
+    lib.gdn_chunk_len.argtypes = []
+    lib.gdn_version.restype = ctypes.c_int32
+    lib.gdn_version.argtypes = []
+    lib.gdn_workspace_bytes.restype = ctypes.c_int
+    lib.gdn_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+    lib.gdn_workspace_layout.restype = ctypes.c_int
+    lib.gdn_workspace_layout.argtypes = [P, ctypes.POINTER(WorkspaceLayout)]
+    for fn in (lib.gdn_fwd, lib.gdn_chunk_step):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_profile_begin.restype = ctypes.c_int
+    lib.gdn_profile_begin.argtypes = []
+    lib.gdn_profile_end.restype = ctypes.c_int
+    lib.gdn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
+    lib.gdn_profile_stage_name.restype = ctypes.c_char_p
+    lib.gdn_profile_stage_name.argtypes = [ctypes.c_int32]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    _lib = lib
+    return lib

@@ -1,0 +1,304 @@
+// Host front-end of libsanawm_gdn: the C ABI declared in include/sanawm_gdn.h.
+//
+// Every check runs on the host before the first launch; the functions only
+// enqueue work on the caller's stream and never synchronise, allocate or free
+// device memory.
+#include "sanawm_gdn.h"
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <mutex>
+#include <vector>
+
+#include "gdn_internal.h"
+
+namespace {
+
+// ---- kernel-level timing (gdn_profile_begin / gdn_profile_end) ----
+struct Profiler {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<hipEvent_t> open[gdn::kNumStages];  // begin events not yet closed, per stage
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> done[gdn::kNumStages];
+};
+Profiler &profiler() {
+  static Profiler p;
+  return p;
+}
+
+}  // namespace
+
+namespace gdn {
+
+void stage_begin(const Args &a, Stage s) {
+  if (!a.profile) return;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEventRecord(e, a.stream);
+  Profiler &P = profiler();
+  std::lock_guard<std::mutex> lk(P.mu);
+  P.open[s].push_back(e);
+}
+
+void stage_end(const Args &a, Stage s) {
+  if (!a.profile) return;
+  Profiler &P = profiler();
+  std::lock_guard<std::mutex> lk(P.mu);
+  if (P.open[s].empty()) return;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEventRecord(e, a.stream);
+  P.done[s].emplace_back(P.open[s].back(), e);
+  P.open[s].pop_back();
+}
+
+}  // namespace gdn
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status_t fail(gdn_status_t s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(size_t a, size_t b, size_t *out) {
+  if (a != 0 && b > std::numeric_limits<size_t>::max() / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Validates the problem descriptor and lays out the workspace.
+gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem descriptor is NULL");
+  if (p->batch < 1 || p->num_heads < 1 || p->seq_len < 0 || p->head_dim_k < 1 || p->head_dim_v < 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "bad shape: batch=%d seq_len=%d heads=%d d_k=%d d_v=%d", p->batch,
+                p->seq_len, p->num_heads, p->head_dim_k, p->head_dim_v);
+  if ((p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16) || (p->o_dtype != GDN_F32 && p->o_dtype != GDN_BF16))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown dtype (qkv=%d, o=%d)", p->qkv_dtype, p->o_dtype);
+  const uint32_t known = GDN_FLAG_BETA_IS_PROB | GDN_FLAG_QK_PRENORMALIZED | GDN_FLAG_PORTABLE_KERNELS;
+  if (p->flags & ~known) return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags & ~known);
+
+  gdn::Plan P;
+  P.B = p->batch;
+  P.T = p->seq_len;
+  P.H = p->num_heads;
+  P.dk = p->head_dim_k;
+  P.dv = p->head_dim_v;
+  P.N = (P.T + gdn::kChunk - 1) / gdn::kChunk;
+  P.qkv_bf16 = p->qkv_dtype == GDN_BF16;
+  P.o_bf16 = p->o_dtype == GDN_BF16;
+  P.flags = p->flags;
+  P.mfma = gdn::kHaveMfmaPath && P.qkv_bf16 && !(p->flags & GDN_FLAG_PORTABLE_KERNELS);
+  if (P.mfma) {
+    if (P.dk != gdn::kMfmaDim || P.dv != gdn::kMfmaDim)
+      return fail(GDN_ERR_UNSUPPORTED, "bf16 MFMA kernels need d_k = d_v = %d (got %d, %d)", gdn::kMfmaDim, P.dk,
+                  P.dv);
+  } else if (P.dk > gdn::kMaxPortableDim || P.dv > gdn::kMaxPortableDim) {
+    return fail(GDN_ERR_UNSUPPORTED, "portable kernels take d_k, d_v <= %d (got %d, %d)", gdn::kMaxPortableDim,
+                P.dk, P.dv);
+  }
+  // grid sizes are 1-D: keep every block count and index product far from overflow
+  const size_t units = size_t(P.B) * size_t(P.H);
+  if (units * size_t(P.N) > (size_t(1) << 31) - 1 || units > (size_t(1) << 24))
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large (B*H*ceil(T/%d) = %zu)", gdn::kChunk, units * P.N);
+
+  size_t off = 0, sz = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  size_t bht;
+  if (!mul_ok(units, size_t(P.T), &bht) || !mul_ok(bht, sizeof(float), &sz))
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+  P.off_beta = take(sz);
+  P.off_rq = take(sz);
+  P.off_rk = take(sz);
+  P.off_gcum = take(sz);
+  const size_t chunks = units * size_t(P.N);
+  if (P.mfma) {
+    P.off_M = take(chunks * gdn::mfma_chunk_bytes_M());
+    P.off_P = take(chunks * gdn::mfma_chunk_bytes_P());
+    P.off_cs = take(chunks * gdn::mfma_chunk_bytes_cs());
+  } else {
+    const size_t rowsk = chunks * gdn::kChunk * size_t(P.dk) * sizeof(float);
+    const size_t rowsv = chunks * gdn::kChunk * size_t(P.dv) * sizeof(float);
+    P.off_W = take(rowsk);
+    P.off_Ut = take(rowsv);
+    P.off_U = take(rowsv);
+    P.off_S0 = take(chunks * size_t(P.dv) * P.dk * sizeof(float));
+  }
+  P.total = P.T == 0 ? 0 : off;
+  *pl = P;
+  return GDN_OK;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
+                 const float *beta, const float *state_in, float *state_out, void *o, void *workspace,
+                 size_t workspace_bytes, void *hip_stream, bool chunk_step) {
+  gdn::Plan P;
+  gdn_status_t s = make_plan(p, &P);
+  if (s != GDN_OK) return s;
+  if (chunk_step) {
+    if (!state_in) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_chunk_step needs a non-NULL state_in");
+    if (P.T % gdn::kChunk)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_chunk_step needs seq_len %% %d == 0 (got %d)", gdn::kChunk, P.T);
+  }
+  const struct {
+    const void *ptr;
+    const char *name;
+  } need[] = {{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {beta, "beta"}, {o, "o"}};
+  if (P.T > 0)
+    for (const auto &n : need) {
+      if (!n.ptr) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is NULL", n.name);
+      if (!aligned16(n.ptr)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n.name);
+    }
+  if (state_in && !aligned16(state_in)) return fail(GDN_ERR_INVALID_ARGUMENT, "state_in is not 16-byte aligned");
+  if (state_out && !aligned16(state_out))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is not 16-byte aligned");
+  if (P.total > 0) {
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", P.total);
+    if (workspace_bytes < P.total)
+      return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, P.total);
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not %zu-byte aligned", kAlign);
+  }
+
+  gdn::Args a{q,
+              k,
+              v,
+              g,
+              beta,
+              state_in,
+              state_out,
+              o,
+              static_cast<char *>(workspace),
+              static_cast<hipStream_t>(hip_stream),
+              profiler().on.load(std::memory_order_relaxed)};
+  hipError_t e;
+  if (P.T == 0) {
+    e = gdn::launch_state_passthrough(P, a);
+  } else {
+    e = gdn::launch_prep(P, a);
+    if (e == hipSuccess) e = P.mfma ? gdn::launch_mfma(P, a) : gdn::launch_portable(P, a);
+  }
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdn_chunk_len(void) { return gdn::kChunk; }
+
+int32_t gdn_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status_t gdn_workspace_bytes(const gdn_problem_t *p, size_t *bytes) {
+  if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  gdn::Plan P;
+  gdn_status_t s = make_plan(p, &P);
+  if (s == GDN_OK) *bytes = P.total;
+  return s;
+}
+
+gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t *layout) {
+  if (!layout) return fail(GDN_ERR_INVALID_ARGUMENT, "layout is NULL");
+  gdn::Plan P;
+  gdn_status_t s = make_plan(p, &P);
+  if (s != GDN_OK) return s;
+  std::memset(layout, 0, sizeof(*layout));
+  layout->beta = P.off_beta;
+  layout->rq = P.off_rq;
+  layout->rk = P.off_rk;
+  layout->gcum = P.off_gcum;
+  layout->total = P.total;
+  layout->mfma = P.mfma ? 1 : 0;
+  return GDN_OK;
+}
+
+gdn_status_t gdn_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const float *state_in, float *state_out, void *o, void *workspace,
+                     size_t workspace_bytes, void *hip_stream) {
+  return run(p, q, k, v, g, beta, state_in, state_out, o, workspace, workspace_bytes, hip_stream, false);
+}
+
+gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *state_in, float *state_out, void *o,
+                            void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return run(p, q, k, v, g, beta, state_in, state_out, o, workspace, workspace_bytes, hip_stream, true);
+}
+
+const char *gdn_status_string(gdn_status_t s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    case GDN_ERR_INTERNAL: return "GDN_ERR_INTERNAL";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char *gdn_last_error(void) { return g_last_error; }
+
+gdn_status_t gdn_profile_begin(void) {
+  Profiler &P = profiler();
+  P.on.store(true);
+  return GDN_OK;
+}
+
+gdn_status_t gdn_profile_end(float *ms, int32_t *calls, int32_t n) {
+  Profiler &P = profiler();
+  P.on.store(false);
+  std::lock_guard<std::mutex> lk(P.mu);
+  gdn_status_t st = GDN_OK;
+  for (int s = 0; s < gdn::kNumStages; ++s) {
+    double sum = 0.0;
+    int cnt = 0;
+    for (auto &pr : P.done[s]) {
+      float t = 0.f;
+      hipError_t e = hipEventSynchronize(pr.second);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, pr.first, pr.second);
+      if (e != hipSuccess && st == GDN_OK) st = fail(GDN_ERR_HIP, "profile events: %s", hipGetErrorString(e));
+      sum += t;
+      ++cnt;
+      hipEventDestroy(pr.first);
+      hipEventDestroy(pr.second);
+    }
+    for (hipEvent_t e : P.open[s]) hipEventDestroy(e);
+    P.open[s].clear();
+    P.done[s].clear();
+    if (s < n) {
+      if (ms) ms[s] = cnt ? float(sum / cnt) : 0.f;
+      if (calls) calls[s] = cnt;
+    }
+  }
+  for (int s = gdn::kNumStages; s < n; ++s) {
+    if (ms) ms[s] = 0.f;
+    if (calls) calls[s] = 0;
+  }
+  return st;
+}
+
+const char *gdn_profile_stage_name(int32_t stage) {
+  static const char *names[gdn::kNumStages] = {"prep", "intra", "state", "output"};
+  return (stage >= 0 && stage < gdn::kNumStages) ? names[stage] : "";
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal declarations shared by the host front-end and the kernel files of
+// libsanawm_gdn.  Not part of the public ABI (include/sanawm_gdn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace gdn {
+
+constexpr int kChunk = 80;        // tokens per chunk (divides the 880-token latent frame)
+constexpr int kMaxPortableDim = 128;
+constexpr int kMfmaDim = 112;     // head_dim of the SANA-WM DiT (20 heads x 112 = 2240)
+constexpr float kLogDecayFloor = -80.0f;
+constexpr bool kHaveMfmaPath = false;
+
+enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kPortable = 4u };
+
+// Everything a launch sequence needs: the problem, the selected kernels and
+// where each intermediate lives inside the caller's workspace.
+struct Plan {
+  int B = 0, T = 0, H = 0, dk = 0, dv = 0, N = 0;  // N = ceil(T / kChunk)
+  int qkv_bf16 = 0, o_bf16 = 0;
+  uint32_t flags = 0;
+  bool mfma = false;
+  // byte offsets into the workspace
+  size_t off_beta = 0, off_rq = 0, off_rk = 0, off_gcum = 0;       // fp32 [B,H,T]
+  size_t off_W = 0, off_Ut = 0, off_U = 0, off_S0 = 0;              // portable path
+  size_t off_M = 0, off_P = 0, off_cs = 0;                           // MFMA path
+  size_t total = 0;
+};
+
+struct Args {
+  const void *q, *k, *v;
+  const float *g, *beta, *state_in;
+  float *state_out;
+  void *o;
+  char *ws;
+  hipStream_t stream;
+  bool profile;  // record timing events around each stage
+};
+
+// Timing stages (see gdn_profile_begin in include/sanawm_gdn.h).
+enum Stage : int { kStagePrep = 0, kStageIntra = 1, kStageState = 2, kStageOutput = 3, kNumStages = 4 };
+void stage_begin(const Args &a, Stage s);
+void stage_end(const Args &a, Stage s);
+
+// Kernel launch sequences (each returns the first launch error, if any).
+hipError_t launch_prep(const Plan &p, const Args &a);
+hipError_t launch_portable(const Plan &p, const Args &a);
+hipError_t launch_mfma(const Plan &p, const Args &a);
+hipError_t launch_state_passthrough(const Plan &p, const Args &a);
+
+// bytes needed by the MFMA path's own intermediates (beyond the prep scalars)
+size_t mfma_chunk_bytes_M();
+size_t mfma_chunk_bytes_P();
+size_t mfma_chunk_bytes_cs();
+
+// ---- small device helpers shared by the kernel files ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T *p, size_t i);
+template <> __device__ __forceinline__ float load_f32<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t *p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+}  // namespace gdn

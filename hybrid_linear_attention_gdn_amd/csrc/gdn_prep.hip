@@ -1,0 +1,98 @@
+// K1 "prep": per token-head scalars of the gated delta rule, shared by both
+// kernel families.
+//
+// For every (b, t, h) it writes, in head-major [B, H, T] fp32 arrays:
+//   beta = sigmoid(beta logit)             (or the input itself: BETA_IS_PROB)
+//   rq   = 1 / max(||q||_2, 1e-6)          (1 with QK_PRENORMALIZED)
+//   rk   = 1 / max(||k||_2, 1e-6)
+//   gcum = inclusive cumulative sum of max(g, -80) within the token's chunk
+// Normalisation, sigmoid and the log-decay are the readings stated in
+// include/sanawm_gdn.h of the gated delta rule the "SANA-WM" cookbook page
+// (table "Architecture & components") names as its attention.  q and k stay
+// raw in HBM: later kernels apply rq / rk as fp32 scales, so the bf16 inputs
+// enter the matrix cores unrounded.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void prep_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                   const float *__restrict__ g,
+                                                   const float *__restrict__ beta, float *__restrict__ o_beta,
+                                                   float *__restrict__ o_rq, float *__restrict__ o_rk,
+                                                   float *__restrict__ o_gcum, int T, int H, int dk, int N,
+                                                   uint32_t flags) {
+  const int b = blockIdx.x / N, c = blockIdx.x % N;
+  const int t0 = c * kChunk;
+  const int n = min(kChunk, T - t0);
+  // one thread per token-head row; consecutive threads read consecutive rows
+  for (int idx = threadIdx.x; idx < n * H; idx += blockDim.x) {
+    const int tt = idx / H, h = idx % H;
+    const size_t th = (size_t(b) * T + t0 + tt) * H + h;
+    float rq = 1.f, rk = 1.f;
+    if (!(flags & kQkPrenormalized)) {
+      float sq = 0.f, sk = 0.f;
+      const size_t row = th * size_t(dk);
+      for (int d = 0; d < dk; ++d) {
+        const float a = load_f32(q, row + d), e = load_f32(k, row + d);
+        sq = fmaf(a, a, sq);
+        sk = fmaf(e, e, sk);
+      }
+      rq = 1.f / fmaxf(sqrtf(sq), 1e-6f);
+      rk = 1.f / fmaxf(sqrtf(sk), 1e-6f);
+    }
+    const float bl = beta[th];
+    const float bt = (flags & kBetaIsProb) ? bl : 1.f / (1.f + expf(-bl));
+    const size_t out = (size_t(b) * H + h) * T + t0 + tt;
+    o_beta[out] = bt;
+    o_rq[out] = rq;
+    o_rk[out] = rk;
+  }
+  // chunk-local inclusive cumsum of the floored log-decay, one thread per head
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float G = 0.f;
+    const size_t out = (size_t(b) * H + h) * T + t0;
+    for (int tt = 0; tt < n; ++tt) {
+      G += fmaxf(g[(size_t(b) * T + t0 + tt) * H + h], kLogDecayFloor);
+      o_gcum[out + tt] = G;
+    }
+  }
+}
+
+// state_out = state_in (or 0) for an empty sequence
+__global__ void state_passthrough_kernel(const float *__restrict__ sin, float *__restrict__ sout, size_t n) {
+  for (size_t i = blockIdx.x * size_t(blockDim.x) + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+    sout[i] = sin ? sin[i] : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_prep(const Plan &p, const Args &a) {
+  float *beta = reinterpret_cast<float *>(a.ws + p.off_beta);
+  float *rq = reinterpret_cast<float *>(a.ws + p.off_rq);
+  float *rk = reinterpret_cast<float *>(a.ws + p.off_rk);
+  float *gc = reinterpret_cast<float *>(a.ws + p.off_gcum);
+  dim3 grid(unsigned(p.B) * unsigned(p.N)), block(256);
+  stage_begin(a, kStagePrep);
+  if (p.qkv_bf16)
+    prep_kernel<uint16_t><<<grid, block, 0, a.stream>>>(static_cast<const uint16_t *>(a.q),
+                                                        static_cast<const uint16_t *>(a.k), a.g, a.beta, beta,
+                                                        rq, rk, gc, p.T, p.H, p.dk, p.N, p.flags);
+  else
+    prep_kernel<float><<<grid, block, 0, a.stream>>>(static_cast<const float *>(a.q),
+                                                     static_cast<const float *>(a.k), a.g, a.beta, beta, rq,
+                                                     rk, gc, p.T, p.H, p.dk, p.N, p.flags);
+  stage_end(a, kStagePrep);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_passthrough(const Plan &p, const Args &a) {
+  if (!a.state_out || a.state_out == a.state_in) return hipSuccess;
+  const size_t n = size_t(p.B) * p.H * p.dv * p.dk;
+  state_passthrough_kernel<<<dim3(unsigned((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256), 0,
+                             a.stream>>>(a.state_in, a.state_out, n);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

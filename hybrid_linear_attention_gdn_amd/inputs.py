@@ -88,11 +88,13 @@ WORKLOADS = {
 
 def round_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
-    b = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
-    nan = np.isnan(np.ascontiguousarray(x, np.float32))
-    r = ((b >> 16) & 1) + 0x7FFF
-    out = ((b + r) >> 16).astype(np.uint16)
-    out[nan] = 0x7FC0
+    xf = np.ascontiguousarray(x, np.float32)
+    b = xf.view(np.uint32)
+    # no uint32 overflow: the largest non-NaN pattern 0xFF800000 plus 0x8000 fits
+    out = ((b + (((b >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+    nan = np.isnan(xf)
+    if nan.any():
+        out[nan] = 0x7FC0
     return out
 
 

@@ -1,0 +1,162 @@
+/*
+ * libsanawm_gdn -- frame-wise Gated DeltaNet (GDN) forward on AMD Instinct
+ * MI355X (CDNA4, gfx950).  Plain C ABI: no HIP, C++ or framework types.
+ *
+ * The operation.  The SGLang-diffusion cookbook page "SANA-WM" (table
+ * "Architecture & components", row "Attention") and the blog post on SANA-WM
+ * (section "core idea / structure") name the DiT's token mixer a frame-wise
+ * Gated DeltaNet whose bounded state carries the causal history across
+ * streaming chunks.  The pages print no formula; this library computes the
+ * published gated delta rule (Yang, Kautz & Hatamizadeh, ICLR 2025), for
+ * every batch row b and head h independently, over tokens t in the order
+ * given (frame-major):
+ *
+ *     S_t = alpha_t * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t * v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * S is a d_v x d_k fp32 matrix (row i = value channel i).  Readings where
+ * the pages are silent:
+ *   - q_t and k_t are L2-normalised inside: x / max(||x||_2, 1e-6);
+ *   - beta_t = sigmoid(beta[t]) (beta holds logits; +-inf give exactly 1, 0);
+ *   - alpha_t = exp(g[t]); g is the per-token log-decay.  "Frame-wise" gating
+ *     is carried by the data: g is non-zero on a frame's first token only.
+ *     g is floored at -80 before use (changes a decay by at most e^-80);
+ *   - the output reads the state after the token's own update, unscaled.
+ *
+ * Layouts (all contiguous, row-major, 16-byte aligned base pointers):
+ *   q, k      [B, T, H, d_k]  qkv_dtype
+ *   v         [B, T, H, d_v]  qkv_dtype
+ *   g, beta   [B, T, H]       fp32
+ *   state     [B, H, d_v, d_k] fp32
+ *   o         [B, T, H, d_v]  o_dtype
+ *
+ * Ownership: the caller owns every buffer, including the workspace (size it
+ * with gdn_workspace_bytes).  The library allocates and frees no device
+ * memory and keeps no pointer after the enqueued work completes.
+ *
+ * Asynchrony: gdn_fwd / gdn_chunk_step validate their arguments on the host,
+ * enqueue kernels on `hip_stream` (a hipStream_t; NULL = the default stream)
+ * and return.  Device faults surface at the caller's next synchronisation.
+ *
+ * Errors: every function returns a status; no exception or abort crosses the
+ * ABI.  All argument checks run before the first launch, so a call that
+ * returns anything but GDN_OK or GDN_ERR_HIP has enqueued nothing.  A
+ * thread-local message with the detail is available from gdn_last_error().
+ *
+ * Determinism: identical inputs give bitwise identical outputs (no atomics,
+ * fixed reduction orders).
+ */
+#ifndef SANAWM_GDN_H
+#define SANAWM_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1, /* NULL/misaligned pointer, bad shape or dtype */
+    GDN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. head size) */
+    GDN_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    GDN_ERR_HIP = 4,              /* a HIP call failed; gdn_last_error has its text */
+    GDN_ERR_INTERNAL = 5
+} gdn_status_t;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+
+enum {
+    GDN_FLAG_BETA_IS_PROB = 1u,     /* beta already holds probabilities: no sigmoid */
+    GDN_FLAG_QK_PRENORMALIZED = 2u, /* q, k already unit length: no normalisation */
+    GDN_FLAG_PORTABLE_KERNELS = 4u  /* force the fp32 vector-ALU kernels for bf16 too */
+};
+
+typedef struct {
+    int32_t batch;      /* B >= 1 */
+    int32_t seq_len;    /* T >= 0 tokens per call */
+    int32_t num_heads;  /* H >= 1 */
+    int32_t head_dim_k; /* d_k */
+    int32_t head_dim_v; /* d_v */
+    int32_t qkv_dtype;  /* gdn_dtype_t of q, k, v */
+    int32_t o_dtype;    /* gdn_dtype_t of o */
+    uint32_t flags;     /* GDN_FLAG_* */
+} gdn_problem_t;
+
+/*
+ * Supported problems.  qkv_dtype = GDN_BF16 with d_k = d_v = 112 (20 x 112 =
+ * the DiT's hidden 2240) runs the MFMA kernels.  qkv_dtype = GDN_F32, or the
+ * PORTABLE flag, runs the fp32 vector-ALU kernels, which take any
+ * 1 <= d_k, d_v <= 128.  Other combinations return GDN_ERR_UNSUPPORTED.
+ */
+
+/* Chunk length of the chunked evaluation (80 tokens: it divides the 880
+ * tokens of a 704 x 1280 latent frame). */
+int32_t gdn_chunk_len(void);
+
+/* Bytes of device workspace that gdn_fwd / gdn_chunk_step need for `p`. */
+gdn_status_t gdn_workspace_bytes(const gdn_problem_t *p, size_t *bytes);
+
+/*
+ * One forward pass over T tokens.
+ *   state_in  NULL = zero initial state.
+ *   state_out NULL = final state not written; may equal state_in (in place).
+ *   o         written for every token.
+ * Same streaming semantics as running the recurrence token by token: a
+ * sequence split into calls, each call's state_out fed as the next call's
+ * state_in, gives the outputs of one pass.
+ */
+gdn_status_t gdn_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, const float *state_in, float *state_out,
+                     void *o, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * One streaming call (a chunk of the causal rollout, e.g. 3 latent frames =
+ * 2,640 tokens): the same mathematics as gdn_fwd, with a stricter contract --
+ * state_in must be non-NULL and seq_len a multiple of gdn_chunk_len(), which
+ * makes a rollout of calls bitwise equal to one gdn_fwd pass over the
+ * concatenation.  state_out may be NULL (a denoising step that must not
+ * commit the state) or equal state_in.
+ */
+gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                            const float *g, const float *beta, const float *state_in,
+                            float *state_out, void *o, void *workspace, size_t workspace_bytes,
+                            void *hip_stream);
+
+/* Where the intermediates live inside the workspace (byte offsets; 0 size =
+ * not used by the selected kernels).  For tests and profiling. */
+typedef struct {
+    size_t beta, rq, rk, gcum;   /* fp32 [B, H, T] each: sigmoid(beta), 1/||q||, 1/||k||,
+                                    chunk-local inclusive cumsum of max(g, -80) */
+    size_t total;                /* == gdn_workspace_bytes */
+    int32_t mfma;                /* 1 = MFMA kernels selected, 0 = portable kernels */
+} gdn_workspace_layout_t;
+gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t *layout);
+
+/*
+ * Kernel-level timing, for benchmarks.  Between gdn_profile_begin and
+ * gdn_profile_end every gdn_fwd / gdn_chunk_step call (from any thread)
+ * records a pair of HIP events around each kernel stage it launches, on the
+ * call's stream.  gdn_profile_end waits for those events, writes the mean
+ * duration in milliseconds of stage i over the recorded calls into ms[i] and
+ * the number of calls that ran stage i into calls[i] (i < n; unused stages get
+ * 0), then releases the events.  Stages: 0 "prep", 1 "intra", 2 "state"
+ * (the fused state pass + output on the MFMA path), 3 "output" (portable
+ * path only).  The events are the only host resources the library creates.
+ */
+gdn_status_t gdn_profile_begin(void);
+gdn_status_t gdn_profile_end(float *ms, int32_t *calls, int32_t n);
+const char *gdn_profile_stage_name(int32_t stage);
+
+const char *gdn_status_string(gdn_status_t s);
+const char *gdn_last_error(void); /* thread-local detail of the last failing call */
+int32_t gdn_version(void);        /* GDN_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANAWM_GDN_H */

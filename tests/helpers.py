@@ -1,0 +1,49 @@
+"""Shared helpers of the GPU tests: upload seeded inputs, run the HIP path,
+run the oracle on the same values, and measure the error the way the
+parity bar is stated (max |o - o_ref| / rms(o_ref))."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from hybrid_linear_attention_gdn_amd.inputs import Inputs
+
+# Parity bars: bf16 inputs with fp32 state, and the fp32 path.
+TOL_BF16 = 1e-2
+TOL_F32 = 1e-4
+
+
+def to_device(inp: Inputs, dev="cuda"):
+    if inp.dtype == "bf16":
+        up = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+        q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(a).to(dev) for a in (inp.q, inp.k, inp.v))
+    g = torch.from_numpy(inp.g).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    s0 = None if inp.state0 is None else torch.from_numpy(inp.state0).to(dev)
+    return q, k, v, g, beta, s0
+
+
+def rel_max_err(x, ref) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(x - ref)) / rms) if ref.size else 0.0
+
+
+def oracle_for(inp: Inputs, heads=None, batches=None, t_end=None):
+    """fp64 oracle on (a subset of) the same values the GPU receives."""
+    from oracle.recurrence import gdn_recurrence
+    sl = lambda a: a  # noqa: E731
+    q, k, v, g, beta, s0 = inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0
+    if t_end is not None:
+        q, k, v, g, beta = (a[:, :t_end] for a in (q, k, v, g, beta))
+    if batches is not None:
+        q, k, v, g, beta = (a[batches] for a in (q, k, v, g, beta))
+        s0 = None if s0 is None else s0[batches]
+    if heads is not None:
+        q, k, v, g, beta = (a[:, :, heads] for a in (q, k, v, g, beta))
+        s0 = None if s0 is None else s0[:, heads]
+    del sl
+    return gdn_recurrence(q, k, v, g, beta, s0)

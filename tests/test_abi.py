@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_linear_attention_gdn_amd import _lib as L
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "sanawm_gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libsanawm_gdn.so is not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = _declared_functions()
+    assert set(decl) == set(L.EXPORTED), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert lib.gdn_version() == 1
+    assert lib.gdn_chunk_len() == 80
+    assert lib.gdn_status_string(L.GDN_ERR_WORKSPACE) == b"GDN_ERR_WORKSPACE"
+
+
+def _p(**kw):
+    d = dict(batch=1, seq_len=160, num_heads=20, head_dim_k=112, head_dim_v=112, qkv_dtype=L.GDN_BF16,
+             o_dtype=L.GDN_F32, flags=0)
+    d.update(kw)
+    return L.Problem(**d)
+
+
+def _ws(lib, p):
+    n = ctypes.c_size_t(123)
+    st = lib.gdn_workspace_bytes(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_bytes(lib):
+    st, n = _ws(lib, _p())
+    assert st == L.GDN_OK and n > 0 and n % 256 == 0
+    st0, n0 = _ws(lib, _p(seq_len=0))
+    assert st0 == L.GDN_OK and n0 == 0
+    st2, n2 = _ws(lib, _p(seq_len=320))
+    assert n2 > n
+    stp, np_ = _ws(lib, _p(qkv_dtype=L.GDN_F32, head_dim_k=64, head_dim_v=32))
+    assert stp == L.GDN_OK and np_ > 0
+    lay = L.WorkspaceLayout()
+    assert lib.gdn_workspace_layout(ctypes.byref(_p()), ctypes.byref(lay)) == L.GDN_OK
+    assert lay.total == n and lay.beta < lay.rq < lay.rk < lay.gcum < lay.total
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), L.GDN_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=-1), L.GDN_ERR_INVALID_ARGUMENT),
+    (dict(num_heads=0), L.GDN_ERR_INVALID_ARGUMENT),
+    (dict(head_dim_k=0), L.GDN_ERR_INVALID_ARGUMENT),
+    (dict(qkv_dtype=7), L.GDN_ERR_INVALID_ARGUMENT),
+    (dict(o_dtype=-1), L.GDN_ERR_INVALID_ARGUMENT),
+    (dict(flags=64), L.GDN_ERR_INVALID_ARGUMENT),
+    (dict(qkv_dtype=L.GDN_F32, head_dim_k=129), L.GDN_ERR_UNSUPPORTED),
+    (dict(flags=L.GDN_FLAG_PORTABLE_KERNELS, head_dim_v=200), L.GDN_ERR_UNSUPPORTED),
+    (dict(batch=1 << 20, num_heads=1 << 10), L.GDN_ERR_UNSUPPORTED),
+])
+def test_bad_problems(lib, kw, status):
+    st, _ = _ws(lib, _p(**kw))
+    assert st == status
+    assert lib.gdn_last_error()
+
+
+def test_null_problem_and_outputs(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_workspace_bytes(None, ctypes.byref(n)) == L.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_workspace_bytes(ctypes.byref(_p()), None) == L.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_workspace_layout(ctypes.byref(_p()), None) == L.GDN_ERR_INVALID_ARGUMENT
+
+
+def _call(lib, fn, p, ptrs=None, ws_bytes=None, **over):
+    # Fake, well-aligned addresses: every call here must fail host validation
+    # before touching them (no HIP call is made on this path).
+    base = dict(q=0x10000, k=0x20000, v=0x30000, g=0x40000, beta=0x50000, state_in=0x60000, state_out=0x70000,
+                o=0x80000, ws=0x100000)
+    base.update(over)
+    st, need = _ws(lib, p)
+    wsb = need if ws_bytes is None else ws_bytes
+    return getattr(lib, fn)(ctypes.byref(p), *(ctypes.c_void_p(base[n]) for n in
+                                               ("q", "k", "v", "g", "beta", "state_in", "state_out", "o", "ws")),
+                            ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("fn", ["gdn_fwd", "gdn_chunk_step"])
+def test_argument_errors_before_launch(lib, fn):
+    p = _p()
+    for name in ("q", "k", "v", "g", "beta", "o"):
+        assert _call(lib, fn, p, **{name: None}) == L.GDN_ERR_INVALID_ARGUMENT
+        assert name.encode() in lib.gdn_last_error()
+        assert _call(lib, fn, p, **{name: 0x10008}) == L.GDN_ERR_INVALID_ARGUMENT  # misaligned
+    assert _call(lib, fn, p, state_out=0x70004) == L.GDN_ERR_INVALID_ARGUMENT
+    assert _call(lib, fn, p, ws=None) == L.GDN_ERR_WORKSPACE
+    _, need = _ws(lib, p)
+    assert _call(lib, fn, p, ws_bytes=need - 1) == L.GDN_ERR_WORKSPACE
+    assert b"too small" in lib.gdn_last_error()
+    assert _call(lib, fn, p, ws=0x100010) == L.GDN_ERR_INVALID_ARGUMENT  # workspace alignment
+
+
+def test_chunk_step_contract(lib):
+    assert _call(lib, "gdn_chunk_step", _p(), state_in=None) == L.GDN_ERR_INVALID_ARGUMENT
+    assert b"state_in" in lib.gdn_last_error()
+    assert _call(lib, "gdn_chunk_step", _p(seq_len=170), q=None) == L.GDN_ERR_INVALID_ARGUMENT
+    assert _call(lib, "gdn_chunk_step", _p(seq_len=170)) == L.GDN_ERR_INVALID_ARGUMENT
+    assert b"seq_len" in lib.gdn_last_error()
+
+
+def test_unsupported_head_dim_on_mfma_path(lib):
+    p = _p(head_dim_k=128, head_dim_v=128)
+    st, _ = _ws(lib, p)
+    mfma = L.WorkspaceLayout()
+    lib.gdn_workspace_layout(ctypes.byref(_p()), ctypes.byref(mfma))
+    if mfma.mfma:
+        assert st == L.GDN_ERR_UNSUPPORTED
+    else:
+        assert st == L.GDN_OK

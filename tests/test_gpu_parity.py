@@ -1,0 +1,220 @@
+"""Parity of the HIP path with the fp64 oracle (needs an MI355X).
+
+Bars: max |o - o_ref| <= 1e-2 * rms(o_ref) for bf16 inputs with fp32 state,
+<= 1e-4 * rms(o_ref) on the fp32 path; the final state against rms(state_ref)
+with the same bars.  Inputs are the seeded synthetic workloads of
+``hybrid_linear_attention_gdn_amd.inputs`` (shapes from the SANA-WM pages).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_linear_attention_gdn_amd import gdn
+from hybrid_linear_attention_gdn_amd.inputs import WORKLOADS, make_inputs
+from tests.helpers import TOL_BF16, TOL_F32, oracle_for, rel_max_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run(inp, *, portable=False, o_dtype=torch.float32, state=True):
+    q, k, v, g, beta, s0 = to_device(inp)
+    o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, "new" if state else None, o_dtype=o_dtype, portable=portable)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), (st.cpu().numpy() if st is not None else None)
+
+
+def _check(inp, o, st, o_ref, s_ref, tol, label):
+    eo = rel_max_err(o, o_ref)
+    es = rel_max_err(st, s_ref) if st is not None else 0.0
+    _say(f"[{label}] max|o-o_ref|/rms = {eo:.3e}   state: {es:.3e}   (bar {tol:g})")
+    assert np.isfinite(o).all()
+    assert eo <= tol, eo
+    assert es <= tol, es
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_tiny_fp32_config(portable):
+    w = WORKLOADS["tiny_fp32"]
+    _say("case tiny_fp32", w)
+    inp = make_inputs(w)
+    o, st = _run(inp, portable=portable)
+    o_ref, s_ref = oracle_for(inp)
+    _check(inp, o, st, o_ref, s_ref, TOL_F32, "tiny_fp32")
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_window_2f_config(portable):
+    w = WORKLOADS["window_2f"]
+    _say("case window_2f portable=", portable)
+    inp = make_inputs(w)
+    o, st = _run(inp, portable=portable)
+    o_ref, s_ref = oracle_for(inp)
+    _check(inp, o, st, o_ref, s_ref, TOL_BF16, "window_2f")
+
+
+@pytest.mark.parametrize("T,B,H", [(1, 1, 2), (79, 1, 3), (81, 2, 2), (250, 1, 4), (400, 2, 3)])
+def test_ragged_and_small(T, B, H):
+    from hybrid_linear_attention_gdn_amd.inputs import Workload
+    w = Workload("ragged", B, H, 1, 10**9, "bf16", 7 + T, state_std=0.05)
+    inp = make_inputs(w, seq_len=T, frame_tokens=97)
+    _say("case ragged", T, B, H)
+    for portable in (False, True):
+        o, st = _run(inp, portable=portable)
+        o_ref, s_ref = oracle_for(inp)
+        _check(inp, o, st, o_ref, s_ref, TOL_BF16, f"ragged T={T} portable={portable}")
+
+
+def test_portable_general_head_dims_fp32():
+    from hybrid_linear_attention_gdn_amd.inputs import Workload
+    w = Workload("dims", 2, 3, 3, 50, "f32", 31, state_std=0.1, head_dim=64)
+    inp = make_inputs(w)
+    inp.v = inp.v[..., :48].copy()
+    inp.state0 = inp.state0[:, :, :48, :].copy()
+    _say("case portable dk=64 dv=48")
+    o, st = _run(inp)
+    o_ref, s_ref = oracle_for(inp)
+    _check(inp, o, st, o_ref, s_ref, TOL_F32, "dk64 dv48 fp32")
+
+
+def test_clip_241f_full_config():
+    w = WORKLOADS["clip_241f"]
+    _say("case clip_241f (27,280 tokens x 20 heads)")
+    inp = make_inputs(w)
+    o, st = _run(inp)
+    o_ref, s_ref = oracle_for(inp)
+    _check(inp, o, st, o_ref, s_ref, TOL_BF16, "clip_241f")
+
+
+def test_streaming_rollout_equals_one_pass():
+    w = WORKLOADS["stream_3f_x10"]
+    _say("case stream_3f_x10: 10 chunk steps of 2,640 tokens")
+    inp = make_inputs(w)
+    q, k, v, g, beta, s0 = to_device(inp)
+    Tc = w.tokens_per_call
+    state = s0.clone()
+    outs = []
+    for c in range(w.calls):
+        sl = slice(c * Tc, (c + 1) * Tc)
+        o, state = gdn.gdn_chunk_step(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(),
+                                      g[:, sl].contiguous(), beta[:, sl].contiguous(), state, state)
+        outs.append(o)
+    o_roll = torch.cat(outs, 1)
+    o_one, s_one = gdn.gdn_fwd(q, k, v, g, beta, s0)
+    torch.cuda.synchronize()
+    assert torch.equal(o_roll, o_one), "rollout differs from one pass"
+    assert torch.equal(state, s_one)
+    o_ref, s_ref = oracle_for(inp)
+    _check(inp, o_one.cpu().numpy(), s_one.cpu().numpy(), o_ref, s_ref, TOL_BF16, "stream_3f_x10")
+
+
+def test_minute_cfg_sampled_heads():
+    """B = 2, 106,480 tokens: the GPU runs the full problem; the oracle checks 6 of the 40 (b, h) units."""
+    w = WORKLOADS["minute_cfg"]
+    _say("case minute_cfg (2 x 106,480 tokens x 20 heads)")
+    inp = make_inputs(w)
+    o, st = _run(inp)
+    for b, heads in ((0, [0, 7, 19]), (1, [3, 11, 16])):
+        o_ref, s_ref = oracle_for(inp, heads=heads, batches=[b])
+        _check(inp, o[[b]][:, :, heads], st[[b]][:, heads], o_ref, s_ref, TOL_BF16, f"minute_cfg b={b} h={heads}")
+    assert np.isfinite(o).all()
+
+
+def test_closed_forms_on_gpu():
+    from hybrid_linear_attention_gdn_amd.inputs import Workload
+    w = Workload("closed", 1, 2, 2, 100, "bf16", 77)
+    inp = make_inputs(w)
+    # beta = 0 (logit -inf), zero state: nothing is written, o = 0 exactly
+    inp.beta[:] = -np.inf
+    for portable in (False, True):
+        o, st = _run(inp, portable=portable)
+        assert not o.any() and not st.any()
+    # alpha = 1, beta = 1, distinct standard-basis keys, every query = key 0: o_t = v_0 for all t
+    T = 112
+    w2 = Workload("basis", 1, 1, 1, T, "bf16", 78)
+    inp2 = make_inputs(w2, seq_len=T)
+    perm = np.random.default_rng(0).permutation(112)
+    inp2.k[:] = 0
+    inp2.k[0, np.arange(T), 0, perm[:T]] = 1.0
+    inp2.q[:] = inp2.k[:, :1]
+    inp2.g[:] = 0
+    inp2.beta[:] = np.inf
+    from hybrid_linear_attention_gdn_amd.inputs import round_bf16_bits
+    inp2.q_bits, inp2.k_bits = round_bf16_bits(inp2.q), round_bf16_bits(inp2.k)
+    for portable in (False, True):
+        o, st = _run(inp2, portable=portable)
+        np.testing.assert_allclose(o[0, :, 0], np.repeat(inp2.v[0, :1, 0], T, 0), rtol=0, atol=1e-5)
+        np.testing.assert_allclose(st[0, 0] @ inp2.k[0, :, 0].T, inp2.v[0, :, 0].T, rtol=0, atol=1e-5)
+
+
+def test_prep_scalars_match_definitions():
+    """K1 outputs (read from the workspace) against their definitions in fp64."""
+    w = WORKLOADS["window_2f"]
+    inp = make_inputs(w, seq_len=250)
+    q, k, v, g, beta, _ = to_device(inp)
+    p = gdn.problem(1, 250, 20, 112, 112, torch.bfloat16, torch.float32)
+    lay = gdn.workspace_layout(p)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
+    gdn.gdn_fwd(q, k, v, g, beta, workspace=ws)
+    torch.cuda.synchronize()
+    f = lambda off: ws[off:off + 4 * 20 * 250].view(torch.float32).view(1, 20, 250).cpu().numpy()  # noqa: E731
+    bt, rq, rk, gc = f(lay.beta), f(lay.rq), f(lay.rk), f(lay.gcum)
+    tr = lambda a: np.transpose(a, (0, 2, 1)).astype(np.float64)  # noqa: E731  [B,T,H] -> [B,H,T]
+    np.testing.assert_allclose(bt, 1 / (1 + np.exp(-tr(inp.beta))), rtol=2e-6)
+    np.testing.assert_allclose(rq, 1 / np.linalg.norm(np.transpose(inp.q, (0, 2, 1, 3)), axis=-1), rtol=2e-6)
+    np.testing.assert_allclose(rk, 1 / np.linalg.norm(np.transpose(inp.k, (0, 2, 1, 3)), axis=-1), rtol=2e-6)
+    G = tr(inp.g).reshape(1, 20, 250)
+    ref = np.concatenate([np.cumsum(G[..., c:c + 80], -1) for c in range(0, 250, 80)], -1)
+    np.testing.assert_allclose(gc, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_determinism_aliasing_and_empty():
+    w = WORKLOADS["window_2f"]
+    inp = make_inputs(w, seq_len=400)
+    inp.state0 = (0.02 * np.random.default_rng(1).standard_normal((1, 20, 112, 112))).astype(np.float32)
+    q, k, v, g, beta, s0 = to_device(inp)
+    o1, st1 = gdn.gdn_fwd(q, k, v, g, beta, s0)
+    o2, st2 = gdn.gdn_fwd(q, k, v, g, beta, s0)
+    s_inplace = s0.clone()
+    o3, _ = gdn.gdn_fwd(q, k, v, g, beta, s_inplace, s_inplace)
+    o4, none = gdn.gdn_fwd(q, k, v, g, beta, s0, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(st1, st2)
+    assert torch.equal(o3, o1) and torch.equal(s_inplace, st1)
+    assert torch.equal(o4, o1) and none is None
+    # empty sequence: state passes through
+    e = lambda t: t[:, :0].contiguous()  # noqa: E731
+    oe, se = gdn.gdn_fwd(e(q), e(k), e(v), e(g), e(beta), s0)
+    oz, sz = gdn.gdn_fwd(e(q), e(k), e(v), e(g), e(beta), None)
+    torch.cuda.synchronize()
+    assert oe.shape == (1, 0, 20, 112) and torch.equal(se, s0) and not sz.any()
+
+
+def test_bf16_output_mode():
+    """bf16 o: the path's own rounding of o (RNE) -- checked against the fp32-o result."""
+    w = WORKLOADS["window_2f"]
+    inp = make_inputs(w)
+    o32, _ = _run(inp)
+    o16, _ = _run(inp, o_dtype=torch.bfloat16)
+    from hybrid_linear_attention_gdn_amd.inputs import round_bf16
+    # rounding fp32 -> bf16 is one ulp at most away from the RNE of the fp32 result
+    ulp = np.abs(round_bf16(o32) - o32).max()
+    assert np.max(np.abs(o16 - round_bf16(o32))) <= 2 * ulp + 1e-30
+
+
+def test_python_binding_rejects_bad_tensors():
+    q = torch.zeros(1, 80, 2, 112, dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros(1, 80, 2, device="cuda")
+    with pytest.raises(ValueError):
+        gdn.gdn_fwd(q, q, q, g[:, :40], g)
+    with pytest.raises(TypeError):
+        gdn.gdn_fwd(q, q.float(), q, g, g)
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_chunk_step(q[:, :50].contiguous(), q[:, :50].contiguous(), q[:, :50].contiguous(),
+                           g[:, :50].contiguous(), g[:, :50].contiguous(), torch.zeros(1, 2, 112, 112, device="cuda"))
