@@ -25,7 +25,8 @@ class Problem(ctypes.Structure):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("beta", ctypes.c_size_t), ("rq", ctypes.c_size_t), ("rk", ctypes.c_size_t),
-                ("gcum", ctypes.c_size_t), ("total", ctypes.c_size_t), ("mfma", ctypes.c_int32)]
+                ("gcum", ctypes.c_size_t), ("mfrag", ctypes.c_size_t), ("pfrag", ctypes.c_size_t),
+                ("cscal", ctypes.c_size_t), ("total", ctypes.c_size_t), ("mfma", ctypes.c_int32)]
 
 
 _lib = None

@@ -226,6 +226,9 @@ gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t
   layout->rq = P.off_rq;
   layout->rk = P.off_rk;
   layout->gcum = P.off_gcum;
+  layout->mfrag = P.mfma ? P.off_M : 0;
+  layout->pfrag = P.mfma ? P.off_P : 0;
+  layout->cscal = P.mfma ? P.off_cs : 0;
   layout->total = P.total;
   layout->mfma = P.mfma ? 1 : 0;
   return GDN_OK;

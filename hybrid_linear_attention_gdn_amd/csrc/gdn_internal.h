@@ -13,7 +13,7 @@ constexpr int kChunk = 80;        // tokens per chunk (divides the 880-token lat
 constexpr int kMaxPortableDim = 128;
 constexpr int kMfmaDim = 112;     // head_dim of the SANA-WM DiT (20 heads x 112 = 2240)
 constexpr float kLogDecayFloor = -80.0f;
-constexpr bool kHaveMfmaPath = false;
+constexpr bool kHaveMfmaPath = true;
 
 enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kPortable = 4u };
 
