@@ -122,16 +122,16 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   size_t bht;
   if (!mul_ok(units, size_t(P.T), &bht) || !mul_ok(bht, sizeof(float), &sz))
     return fail(GDN_ERR_UNSUPPORTED, "problem too large");
-  P.off_beta = take(sz);
-  P.off_rq = take(sz);
-  P.off_rk = take(sz);
-  P.off_gcum = take(sz);
   const size_t chunks = units * size_t(P.N);
-  if (P.mfma) {
+  if (P.mfma) {  // the MFMA path computes its per-token scalars inside the intra kernel
     P.off_M = take(chunks * gdn::mfma_chunk_bytes_M());
     P.off_P = take(chunks * gdn::mfma_chunk_bytes_P());
     P.off_cs = take(chunks * gdn::mfma_chunk_bytes_cs());
   } else {
+    P.off_beta = take(sz);
+    P.off_rq = take(sz);
+    P.off_rk = take(sz);
+    P.off_gcum = take(sz);
     const size_t rowsk = chunks * gdn::kChunk * size_t(P.dk) * sizeof(float);
     const size_t rowsv = chunks * gdn::kChunk * size_t(P.dv) * sizeof(float);
     P.off_W = take(rowsk);
@@ -192,8 +192,12 @@ gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const voi
   if (P.T == 0) {
     e = gdn::launch_state_passthrough(P, a);
   } else {
-    e = gdn::launch_prep(P, a);
-    if (e == hipSuccess) e = P.mfma ? gdn::launch_mfma(P, a) : gdn::launch_portable(P, a);
+    if (P.mfma) {
+      e = gdn::launch_mfma(P, a);
+    } else {
+      e = gdn::launch_prep(P, a);
+      if (e == hipSuccess) e = gdn::launch_portable(P, a);
+    }
   }
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
@@ -222,10 +226,10 @@ gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t
   gdn_status_t s = make_plan(p, &P);
   if (s != GDN_OK) return s;
   std::memset(layout, 0, sizeof(*layout));
-  layout->beta = P.off_beta;
-  layout->rq = P.off_rq;
-  layout->rk = P.off_rk;
-  layout->gcum = P.off_gcum;
+  layout->beta = P.mfma ? 0 : P.off_beta;
+  layout->rq = P.mfma ? 0 : P.off_rq;
+  layout->rk = P.mfma ? 0 : P.off_rk;
+  layout->gcum = P.mfma ? 0 : P.off_gcum;
   layout->mfrag = P.mfma ? P.off_M : 0;
   layout->pfrag = P.mfma ? P.off_P : 0;
   layout->cscal = P.mfma ? P.off_cs : 0;

@@ -1,0 +1,441 @@
+// Kernel "chain" of the MFMA family: the sequential state pass fused with the
+// output, one workgroup (4 waves) per (b, h, 16 columns of d_v).
+//
+// Per chunk (the algebra is in gdn_mfma_common.h):
+//   Y = K S^T,  R = diag(beta) V - diag(beta gamma rk) Y,
+//   O = diag(gamma rq) Q S^T + P' R,   S^T <- gamma_n S^T + M R.
+// The 16 x 112 fp32 state slice S^T lives in accumulator registers as 7 row
+// tiles spread over the waves.  Per chunk, two barriers exchange the bf16
+// hi/lo operands S (after phase 0) and R (after phase A) through LDS.
+//
+// Operand traffic.  K, Q and this workgroup's 16 columns of V are staged in
+// LDS one chunk ahead by all 256 threads with 16-byte row loads (a 224-byte
+// bf16 row is 14 such pieces), double-buffered; each wave then reads its
+// fragments from LDS (rows padded to 232 bytes so the 8-byte fragment reads
+// of 16 consecutive rows fall in distinct banks).  The fragment-ordered M and
+// P' records and the per-token scales are read straight into registers, one
+// chunk ahead: every such load is a contiguous 1 KB per instruction.
+#include "gdn_mfma_common.h"
+
+namespace gdn {
+namespace mfma {
+namespace {
+
+struct Roles {
+  int nY, Y[2];    // token tiles whose Y = K S^T and R this wave computes (phase A)
+  int nQA, QA[1];  // token tiles whose Q S^T it computes in phase A
+  int nQB, QB[2];  // ... in phase B
+  int nO, O[2];    // output tiles it finishes (uses its Q S^T of the same tile)
+  int nS, S[3];    // d_k row tiles of the state it owns
+};
+// Phase A: every wave does 16 MFMAs; phase B is balanced as far as 7 state
+// tiles and 5 token tiles allow.
+__device__ constexpr Roles kRoles[4] = {
+    {1, {0, 0}, 1, {0}, 0, {0, 0}, 1, {0, 0}, 3, {0, 1, 2}},
+    {1, {1, 0}, 1, {1}, 0, {0, 0}, 1, {1, 0}, 2, {3, 4, 0}},
+    {1, {2, 0}, 1, {2}, 0, {0, 0}, 1, {2, 0}, 2, {5, 6, 0}},
+    {2, {3, 4}, 0, {0}, 2, {3, 4}, 2, {3, 4}, 0, {0, 0, 0}},
+};
+
+constexpr int kRowPad = 116;  // bf16 per staged K/Q row (232 B)
+constexpr int kVtPad = 84;    // bf16 per staged V^T row (168 B)
+constexpr int kLdsS = 0;                                 // S operand: hi/lo x (3 x 1 KB + 512 B)
+constexpr int kLdsR = 2 * (3 * 1024 + 512);              // R operand: hi/lo x (2 x 1 KB + 512 B)
+constexpr int kLdsStage = kLdsR + 2 * (2 * 1024 + 512);  // two K/Q/V^T buffers
+constexpr int kStageK = 0;
+constexpr int kStageQ = C * kRowPad * 2;                 // 18,560
+constexpr int kStageV = 2 * C * kRowPad * 2;             // 37,120
+constexpr int kStageBytes = kStageV + 16 * kVtPad * 2;   // 39,808
+constexpr int kLdsChain = kLdsStage + 2 * kStageBytes;   // 91,904
+constexpr int kPieces = 2 * C * 14 + C * 2;              // 16-byte pieces per chunk: K, Q rows, V columns
+constexpr int kPiecesPerThread = (kPieces + 255) / 256;  // 10
+static_assert(kStageBytes % 16 == 0, "stage buffers stay 16-byte aligned");
+
+// Everything one wave reads from global memory for one chunk, besides the
+// staged rows: independent of the state, so the next chunk's set is in flight
+// while the current one is consumed.
+struct ChunkOps {
+  float Aa[2][4], Bb[2][4];  // beta, beta*gamma*rk for the rows of the Y tiles
+  float Cc[2][4];            // gamma*rq for the rows of the output tiles
+  F32 Mf[3][2][2];           // M fragments of the owned state tiles [tile][block][hi/lo]
+  F16 Mt[3][2];
+  F32 Pf[2][2][2];           // P' fragments of the output tiles
+  F16 Pt[2][2];
+  float gC;                  // gamma at the chunk's last token
+};
+
+struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k = d_k)
+  F32 f[3];
+  F16 t;
+};
+
+template <int W, bool kOutBf16>
+__device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                           const uint16_t *__restrict__ v, const char *__restrict__ Mws,
+                                           const char *__restrict__ Pws, const float *__restrict__ CS,
+                                           const float *state_in, float *state_out, void *__restrict__ o, int T,
+                                           int H, int N, int b, int h, int nt, char *lds) {
+  constexpr Roles ro = kRoles[W];
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+  const size_t u = size_t(b) * H + h;
+  const size_t rowstride = size_t(H) * D;
+  char *Slds = lds + kLdsS;
+  char *Rlds = lds + kLdsR;
+
+  // ---- state slice: S^T tile j, accumulator rows d_k = 16j + 4lg + e, column d_v = 16nt + ln
+  f32x4 S[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    S[s] = zero4();
+    if (s < ro.nS && state_in) {
+      const float4 t = *reinterpret_cast<const float4 *>(state_in + (u * D + 16 * nt + ln) * D + 16 * ro.S[s] + 4 * lg);
+      S[s] = f32x4{t.x, t.y, t.z, t.w};
+    }
+  }
+
+  // ---- cooperative staging of K, Q rows and this tile's V columns (all 256 threads)
+  uint4 stage[kPiecesPerThread];
+  auto stage_issue = [&](int c) {
+    const int t0 = c * C, nv = min(C, T - t0);
+    const size_t base = (size_t(b) * T + t0) * rowstride + size_t(h) * D;
+#pragma unroll
+    for (int i = 0; i < kPiecesPerThread; ++i) {
+      const int p = tid + 256 * i;
+      stage[i] = make_uint4(0, 0, 0, 0);
+      if (p < 2 * C * 14) {
+        const int m = p / (C * 14), r = (p % (C * 14)) / 14, c16 = p % 14;
+        if (r < nv) stage[i] = ldg16((m ? q : k) + base + size_t(r) * rowstride + 8 * c16);
+      } else if (p < kPieces) {
+        const int pv = p - 2 * C * 14, r = pv >> 1, half = pv & 1;
+        if (r < nv) stage[i] = ldg16(v + base + size_t(r) * rowstride + 16 * nt + 8 * half);
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+    char *sb = lds + kLdsStage + buf * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kPiecesPerThread; ++i) {
+      const int p = tid + 256 * i;
+      if (p < 2 * C * 14) {
+        const int m = p / (C * 14), r = (p % (C * 14)) / 14, c16 = p % 14;
+        uint2 *dst = reinterpret_cast<uint2 *>(sb + (m ? kStageQ : kStageK) + r * (kRowPad * 2) + 16 * c16);
+        dst[0] = make_uint2(stage[i].x, stage[i].y);
+        dst[1] = make_uint2(stage[i].z, stage[i].w);
+      } else if (p < kPieces) {
+        const int pv = p - 2 * C * 14, r = pv >> 1, half = pv & 1;
+        uint16_t *vt = reinterpret_cast<uint16_t *>(sb + kStageV);
+        const uint32_t w[4] = {stage[i].x, stage[i].y, stage[i].z, stage[i].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vt[(8 * half + j) * kVtPad + r] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
+      }
+    }
+  };
+  // A-operand fragments of a 16-row tile of the staged K (m = 0) or Q (m = 1), "pair" k-order
+  auto rows_frag = [&](int buf, int m, int tile) {
+    const char *rowp = lds + kLdsStage + buf * kStageBytes + (m ? kStageQ : kStageK) + (16 * tile + ln) * (kRowPad * 2);
+    RowFrags rf;
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) {
+      const uint2 x0 = *reinterpret_cast<const uint2 *>(rowp + 64 * kb + 8 * lg);
+      const uint2 x1 = *reinterpret_cast<const uint2 *>(rowp + 64 * kb + 32 + 8 * lg);
+      rf.f[kb] = F32{{x0.x, x0.y, x1.x, x1.y}};
+    }
+    const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 192 + 8 * lg);
+    rf.t = F16{{x2.x, x2.y}};
+    return rf;
+  };
+
+  auto load_ops = [&](ChunkOps &op, int c) {
+    const float *cs = CS + (u * N + c) * kCsFloats;
+    const char *Mr = Mws + (u * N + c) * size_t(kMBytes);
+    const char *Pr = Pws + (u * N + c) * size_t(kPBytes);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < ro.nY) {
+        const int tile = ro.Y[s];
+        const float4 a4 = *reinterpret_cast<const float4 *>(cs + 16 * tile + 4 * lg);
+        const float4 b4 = *reinterpret_cast<const float4 *>(cs + 80 + 16 * tile + 4 * lg);
+        op.Aa[s][0] = a4.x, op.Aa[s][1] = a4.y, op.Aa[s][2] = a4.z, op.Aa[s][3] = a4.w;
+        op.Bb[s][0] = b4.x, op.Bb[s][1] = b4.y, op.Bb[s][2] = b4.z, op.Bb[s][3] = b4.w;
+      }
+    }
+    op.gC = cs[240];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      if (s < ro.nS) {
+        const int mt = ro.S[s];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) {
+            const uint4 x = ldg16(Mr + m_off32(mt, kb, hl) + lane * 16);
+            op.Mf[s][kb][hl] = F32{{x.x, x.y, x.z, x.w}};
+          }
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) {
+          const uint2 x = ldg8(Mr + m_off16(mt, hl) + lane * 8);
+          op.Mt[s][hl] = F16{{x.x, x.y}};
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < ro.nO) {
+        const int R = ro.O[s];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) {
+            if (kb < (R + 1) / 2) {
+              const uint4 x = ldg16(Pr + p_off32(R, kb, hl) + lane * 16);
+              op.Pf[s][kb][hl] = F32{{x.x, x.y, x.z, x.w}};
+            }
+          }
+        if (!(R & 1))
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) {
+            const uint2 x = ldg8(Pr + p_off16(R, hl) + lane * 8);
+            op.Pt[s][hl] = F16{{x.x, x.y}};
+          }
+        const float4 c4 = *reinterpret_cast<const float4 *>(cs + 160 + 16 * R + 4 * lg);
+        op.Cc[s][0] = c4.x, op.Cc[s][1] = c4.y, op.Cc[s][2] = c4.z, op.Cc[s][3] = c4.w;
+      }
+    }
+  };
+
+  // one chunk: consume `cur` and staging buffer c & 1; put chunk c + 1 in flight
+  auto step = [&](int c, const ChunkOps &cur, ChunkOps &nxt) {
+    const int t0 = c * C, nv = min(C, T - t0), buf = c & 1;
+    // ---- phase 0: publish this wave's state tiles as bf16 hi/lo B operands
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      if (s < ro.nS) {
+        const int j = ro.S[s];
+        uint32_t hi[2], lo[2];
+        split4(S[s], hi, lo);
+        if (j < 6) {
+          const int kb = j >> 1, half = j & 1;
+          *reinterpret_cast<uint2 *>(Slds + kb * 1024 + lane * 16 + half * 8) = make_uint2(hi[0], hi[1]);
+          *reinterpret_cast<uint2 *>(Slds + 3584 + kb * 1024 + lane * 16 + half * 8) = make_uint2(lo[0], lo[1]);
+        } else {
+          *reinterpret_cast<uint2 *>(Slds + 3072 + lane * 8) = make_uint2(hi[0], hi[1]);
+          *reinterpret_cast<uint2 *>(Slds + 3584 + 3072 + lane * 8) = make_uint2(lo[0], lo[1]);
+        }
+      }
+    }
+    __syncthreads();
+    if (c + 1 < N) {
+      stage_issue(c + 1);
+      load_ops(nxt, c + 1);
+    }
+    // ---- phase A: S operands, Y = K S^T -> R (published), Q S^T for phase-A tiles
+    F32 Sh[3], Sl[3];
+    F16 Sth, Stl;
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) {
+      const uint4 xh = *reinterpret_cast<const uint4 *>(Slds + kb * 1024 + lane * 16);
+      const uint4 xl = *reinterpret_cast<const uint4 *>(Slds + 3584 + kb * 1024 + lane * 16);
+      Sh[kb] = F32{{xh.x, xh.y, xh.z, xh.w}};
+      Sl[kb] = F32{{xl.x, xl.y, xl.z, xl.w}};
+    }
+    {
+      const uint2 xh = *reinterpret_cast<const uint2 *>(Slds + 3072 + lane * 8);
+      const uint2 xl = *reinterpret_cast<const uint2 *>(Slds + 3584 + 3072 + lane * 8);
+      Sth = F16{{xh.x, xh.y}};
+      Stl = F16{{xl.x, xl.y}};
+    }
+    auto rows_times_S = [&](const RowFrags &rf) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) {
+        acc = mma(rf.f[kb], Sh[kb], acc);
+        acc = mma(rf.f[kb], Sl[kb], acc);
+      }
+      acc = mma(rf.t, Sth, acc);
+      acc = mma(rf.t, Stl, acc);
+      return acc;
+    };
+    const uint16_t *vt = reinterpret_cast<const uint16_t *>(lds + kLdsStage + buf * kStageBytes + kStageV);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < ro.nY) {
+        const int tile = ro.Y[s];
+        const f32x4 y = rows_times_S(rows_frag(buf, 0, tile));
+        const uint2 vv = *reinterpret_cast<const uint2 *>(vt + ln * kVtPad + 16 * tile + 4 * lg);
+        const float va[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                             __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+        float r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = cur.Aa[s][e] * va[e] - cur.Bb[s][e] * y[e];
+        uint32_t hi[2], lo[2];
+        split4(r4, hi, lo);
+        if (tile < 4) {
+          const int kb = tile >> 1, half = tile & 1;
+          *reinterpret_cast<uint2 *>(Rlds + kb * 1024 + lane * 16 + half * 8) = make_uint2(hi[0], hi[1]);
+          *reinterpret_cast<uint2 *>(Rlds + 2560 + kb * 1024 + lane * 16 + half * 8) = make_uint2(lo[0], lo[1]);
+        } else {
+          *reinterpret_cast<uint2 *>(Rlds + 2048 + lane * 8) = make_uint2(hi[0], hi[1]);
+          *reinterpret_cast<uint2 *>(Rlds + 2560 + 2048 + lane * 8) = make_uint2(lo[0], lo[1]);
+        }
+      }
+    }
+    f32x4 QS[2] = {zero4(), zero4()};
+    if (ro.nQA) QS[0] = rows_times_S(rows_frag(buf, 1, ro.QA[0]));
+    __syncthreads();
+    // ---- phase B: R operands; state update and outputs
+    F32 Rh[2], Rl[2];
+    F16 Rth, Rtl;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint4 xh = *reinterpret_cast<const uint4 *>(Rlds + kb * 1024 + lane * 16);
+      const uint4 xl = *reinterpret_cast<const uint4 *>(Rlds + 2560 + kb * 1024 + lane * 16);
+      Rh[kb] = F32{{xh.x, xh.y, xh.z, xh.w}};
+      Rl[kb] = F32{{xl.x, xl.y, xl.z, xl.w}};
+    }
+    {
+      const uint2 xh = *reinterpret_cast<const uint2 *>(Rlds + 2048 + lane * 8);
+      const uint2 xl = *reinterpret_cast<const uint2 *>(Rlds + 2560 + 2048 + lane * 8);
+      Rth = F16{{xh.x, xh.y}};
+      Rtl = F16{{xl.x, xl.y}};
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ro.nQB) QS[s] = rows_times_S(rows_frag(buf, 1, ro.QB[s]));
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      if (s < ro.nS) {
+        f32x4 acc = S[s] * cur.gC;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          acc = mma(cur.Mf[s][kb][0], Rh[kb], acc);
+          acc = mma(cur.Mf[s][kb][0], Rl[kb], acc);
+          acc = mma(cur.Mf[s][kb][1], Rh[kb], acc);
+        }
+        acc = mma(cur.Mt[s][0], Rth, acc);
+        acc = mma(cur.Mt[s][0], Rtl, acc);
+        acc = mma(cur.Mt[s][1], Rth, acc);
+        S[s] = acc;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < ro.nO) {
+        const int R = ro.O[s];
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = cur.Cc[s][e] * QS[s][e];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb < (R + 1) / 2) {
+            acc = mma(cur.Pf[s][kb][0], Rh[kb], acc);
+            acc = mma(cur.Pf[s][kb][0], Rl[kb], acc);
+            acc = mma(cur.Pf[s][kb][1], Rh[kb], acc);
+          }
+        }
+        if (!(R & 1)) {
+          // the 16-deep block covers token tile R (tile 4: the shared 16-deep R slot;
+          // tiles 0 and 2: first halves of the 32-deep R slots)
+          F16 rh, rl;
+          if (R == 4) {
+            rh = Rth;
+            rl = Rtl;
+          } else {
+            const int kb = R >> 1;
+            rh = F16{{Rh[kb].w[0], Rh[kb].w[1]}};
+            rl = F16{{Rl[kb].w[0], Rl[kb].w[1]}};
+          }
+          acc = mma(cur.Pt[s][0], rh, acc);
+          acc = mma(cur.Pt[s][0], rl, acc);
+          acc = mma(cur.Pt[s][1], rh, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * R + 4 * lg + e;
+          if (row < nv) {
+            const size_t oi = (size_t(b) * T + t0 + row) * rowstride + size_t(h) * D + 16 * nt + ln;
+            if constexpr (kOutBf16)
+              static_cast<uint16_t *>(o)[oi] = f32_to_bf16(acc[e]);
+            else
+              static_cast<float *>(o)[oi] = acc[e];
+          }
+        }
+      }
+    }
+    // staging buffer (c + 1) & 1 was last read in chunk c - 1, before this chunk's first barrier
+    if (c + 1 < N) stage_store(buf ^ 1);
+  };
+
+  ChunkOps opA, opB;
+  stage_issue(0);
+  load_ops(opA, 0);
+  stage_store(0);
+  for (int c = 0; c < N; c += 2) {
+    step(c, opA, opB);
+    if (c + 1 < N) step(c + 1, opB, opA);
+  }
+  if (state_out) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < ro.nS)
+        *reinterpret_cast<float4 *>(state_out + (u * D + 16 * nt + ln) * D + 16 * ro.S[s] + 4 * lg) =
+            make_float4(S[s][0], S[s][1], S[s][2], S[s][3]);
+  }
+}
+
+template <bool kOutBf16>
+__global__ __launch_bounds__(256) void chain_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                    const uint16_t *__restrict__ v, const char *__restrict__ Mws,
+                                                    const char *__restrict__ Pws, const float *__restrict__ CS,
+                                                    const float *state_in, float *state_out,
+                                                    void *__restrict__ o, int T, int H, int N, int units) {
+  extern __shared__ __align__(16) char lds[];
+  // Workgroup i runs on XCD i % 8: keep the 7 column tiles of a (b, h) on one
+  // XCD so that its K, Q, M and P' are fetched from HBM once into that L2.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int u = xcd + 8 * (slot / NT), nt = slot % NT;
+  if (u >= units) return;
+  const int b = u / H, h = u % H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  switch (wave) {
+    case 0: chain_role<0, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
+    case 1: chain_role<1, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
+    case 2: chain_role<2, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
+    default: chain_role<3, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
+  }
+}
+
+}  // namespace
+}  // namespace mfma
+
+size_t mfma_chunk_bytes_M() { return mfma::kMBytes; }
+size_t mfma_chunk_bytes_P() { return mfma::kPBytes; }
+size_t mfma_chunk_bytes_cs() { return mfma::kCsFloats * sizeof(float); }
+
+hipError_t launch_mfma(const Plan &p, const Args &a) {
+  char *M = a.ws + p.off_M;
+  char *P = a.ws + p.off_P;
+  float *cs = reinterpret_cast<float *>(a.ws + p.off_cs);
+  hipError_t e = mfma::launch_intra(p, a, M, P, cs);
+  if (e != hipSuccess) return e;
+  static const hipError_t lds0 = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma::chain_kernel<false>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, mfma::kLdsChain);
+  static const hipError_t lds1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma::chain_kernel<true>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, mfma::kLdsChain);
+  if (lds0 != hipSuccess) return lds0;
+  if (lds1 != hipSuccess) return lds1;
+  const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
+                 *v = static_cast<const uint16_t *>(a.v);
+  const int units = p.B * p.H;
+  const unsigned grid = 8u * mfma::NT * unsigned((units + 7) / 8);
+  stage_begin(a, kStageState);
+  if (p.o_bf16)
+    mfma::chain_kernel<true><<<dim3(grid), dim3(256), mfma::kLdsChain, a.stream>>>(
+        q, k, v, M, P, cs, a.state_in, a.state_out, a.o, p.T, p.H, p.N, units);
+  else
+    mfma::chain_kernel<false><<<dim3(grid), dim3(256), mfma::kLdsChain, a.stream>>>(
+        q, k, v, M, P, cs, a.state_in, a.state_out, a.o, p.T, p.H, p.N, units);
+  stage_end(a, kStageState);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

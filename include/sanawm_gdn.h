@@ -129,8 +129,9 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
 /* Where the intermediates live inside the workspace (byte offsets; 0 size =
  * not used by the selected kernels).  For tests and profiling. */
 typedef struct {
-    size_t beta, rq, rk, gcum;   /* fp32 [B, H, T] each: sigmoid(beta), 1/||q||, 1/||k||,
-                                    chunk-local inclusive cumsum of max(g, -80) */
+    size_t beta, rq, rk, gcum;   /* portable path: fp32 [B, H, T] each: sigmoid(beta), 1/||q||,
+                                    1/||k||, chunk-local inclusive cumsum of max(g, -80); 0 on the
+                                    MFMA path, whose intra kernel computes them in place */
     size_t mfrag, pfrag, cscal;  /* MFMA path, per (b, h, chunk) record: M = K^T diag(s) T
                                     (35,840 B) and P' = P T (15,360 B) as bf16 hi/lo operand
                                     fragments, and 256 fp32 chunk scalars; 0 on the portable path */

@@ -59,7 +59,10 @@ def test_workspace_bytes(lib):
     assert stp == L.GDN_OK and np_ > 0
     lay = L.WorkspaceLayout()
     assert lib.gdn_workspace_layout(ctypes.byref(_p()), ctypes.byref(lay)) == L.GDN_OK
-    assert lay.total == n and lay.beta < lay.rq < lay.rk < lay.gcum < lay.total
+    assert lay.total == n and lay.mfma == 1 and lay.mfrag < lay.pfrag < lay.cscal < lay.total
+    lay_p = L.WorkspaceLayout()
+    assert lib.gdn_workspace_layout(ctypes.byref(_p(flags=L.GDN_FLAG_PORTABLE_KERNELS)), ctypes.byref(lay_p)) == 0
+    assert lay_p.mfma == 0 and lay_p.beta < lay_p.rq < lay_p.rk < lay_p.gcum < lay_p.total
 
 
 @pytest.mark.parametrize("kw,status", [

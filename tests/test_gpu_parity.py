@@ -154,14 +154,15 @@ def test_closed_forms_on_gpu():
 
 
 def test_prep_scalars_match_definitions():
-    """K1 outputs (read from the workspace) against their definitions in fp64."""
+    """Standalone prep kernel outputs (portable path, read from the workspace) against their
+    definitions in fp64; the MFMA path's fused copies are checked in test_gpu_kernels."""
     w = WORKLOADS["window_2f"]
     inp = make_inputs(w, seq_len=250)
     q, k, v, g, beta, _ = to_device(inp)
-    p = gdn.problem(1, 250, 20, 112, 112, torch.bfloat16, torch.float32)
+    p = gdn.problem(1, 250, 20, 112, 112, torch.bfloat16, torch.float32, portable=True)
     lay = gdn.workspace_layout(p)
     ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
-    gdn.gdn_fwd(q, k, v, g, beta, workspace=ws)
+    gdn.gdn_fwd(q, k, v, g, beta, workspace=ws, portable=True)
     torch.cuda.synchronize()
     f = lambda off: ws[off:off + 4 * 20 * 250].view(torch.float32).view(1, 20, 250).cpu().numpy()  # noqa: E731
     bt, rq, rk, gc = f(lay.beta), f(lay.rq), f(lay.rk), f(lay.gcum)
