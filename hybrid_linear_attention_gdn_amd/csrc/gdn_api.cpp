@@ -104,6 +104,9 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
     if (P.dk != gdn::kMfmaDim || P.dv != gdn::kMfmaDim)
       return fail(GDN_ERR_UNSUPPORTED, "bf16 MFMA kernels need d_k = d_v = %d (got %d, %d)", gdn::kMfmaDim, P.dk,
                   P.dv);
+    // one chunk of rows of o (fp32) must stay addressable by a 31-bit buffer offset
+    if (size_t(gdn::kChunk) * P.H * gdn::kMfmaDim * sizeof(float) >= (size_t(1) << 31))
+      return fail(GDN_ERR_UNSUPPORTED, "too many heads for the MFMA kernels (%d)", P.H);
   } else if (P.dk > gdn::kMaxPortableDim || P.dv > gdn::kMaxPortableDim) {
     return fail(GDN_ERR_UNSUPPORTED, "portable kernels take d_k, d_v <= %d (got %d, %d)", gdn::kMaxPortableDim,
                 P.dk, P.dv);

@@ -21,6 +21,18 @@ namespace gdn {
 namespace mfma {
 namespace {
 
+// Raw buffer access (gfx9 descriptor, stride 0): an offset at or past
+// `bytes` reads zero and drops a store.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 struct Roles {
   int nY, Y[2];    // token tiles whose Y = K S^T and R this wave computes (phase A)
   int nQA, QA[1];  // token tiles whose Q S^T it computes in phase A
@@ -47,8 +59,6 @@ constexpr int kStageQ = C * kRowPad * 2;                 // 18,560
 constexpr int kStageV = 2 * C * kRowPad * 2;             // 37,120
 constexpr int kStageBytes = kStageV + 16 * kVtPad * 2;   // 39,808
 constexpr int kLdsChain = kLdsStage + 2 * kStageBytes;   // 91,904
-constexpr int kPieces = 2 * C * 14 + C * 2;              // 16-byte pieces per chunk: K, Q rows, V columns
-constexpr int kPiecesPerThread = (kPieces + 255) / 256;  // 10
 static_assert(kStageBytes % 16 == 0, "stage buffers stay 16-byte aligned");
 
 // Everything one wave reads from global memory for one chunk, besides the
@@ -93,41 +103,55 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
     }
   }
 
-  // ---- cooperative staging of K, Q rows and this tile's V columns (all 256 threads)
-  uint4 stage[kPiecesPerThread];
+  // ---- cooperative staging of K, Q rows and this tile's V columns (all 256 threads).
+  // Thread tid takes 16-byte piece (tid & 15) of rows (tid >> 4) + 16 i of K and of Q
+  // (pieces 14, 15 of a 224-byte row do not exist), and, for tid < 160, half (tid & 1)
+  // of row tid >> 1 of the V tile: every address is a fixed per-thread offset plus the chunk base.
+  // The loads are buffer loads through a descriptor that covers exactly the
+  // chunk's valid rows: rows past the end (and the non-existent pieces 14, 15)
+  // read as zero with no branch, so every wave issues the same memory
+  // instructions on every path and the in-order load counter never forces a
+  // wait on the next chunk's prefetch.
+  const int sp = tid & 15, sr = tid >> 4;
+  const bool sp_ok = sp < 14;
+  const uint32_t row_bytes = uint32_t(rowstride) * 2u;
+  const uint32_t offKQ = sp_ok ? uint32_t(sr) * row_bytes + uint32_t(h) * (D * 2) + 16u * sp : kOutOfRange;
+  const uint32_t offV = tid < 2 * C ? uint32_t(tid >> 1) * row_bytes + uint32_t(h) * (D * 2) + 32u * nt + 16u * (tid & 1)
+                                    : kOutOfRange;
+  uint4 stK[CT], stQ[CT], stV;
   auto stage_issue = [&](int c) {
     const int t0 = c * C, nv = min(C, T - t0);
-    const size_t base = (size_t(b) * T + t0) * rowstride + size_t(h) * D;
+    const size_t base = (size_t(b) * T + t0) * rowstride;
+    const uint32_t bytes = uint32_t(nv) * row_bytes;
+    const auto rk_ = make_rsrc(k + base, bytes), rq_ = make_rsrc(q + base, bytes), rv_ = make_rsrc(v + base, bytes);
 #pragma unroll
-    for (int i = 0; i < kPiecesPerThread; ++i) {
-      const int p = tid + 256 * i;
-      stage[i] = make_uint4(0, 0, 0, 0);
-      if (p < 2 * C * 14) {
-        const int m = p / (C * 14), r = (p % (C * 14)) / 14, c16 = p % 14;
-        if (r < nv) stage[i] = ldg16((m ? q : k) + base + size_t(r) * rowstride + 8 * c16);
-      } else if (p < kPieces) {
-        const int pv = p - 2 * C * 14, r = pv >> 1, half = pv & 1;
-        if (r < nv) stage[i] = ldg16(v + base + size_t(r) * rowstride + 16 * nt + 8 * half);
-      }
+    for (int i = 0; i < CT; ++i) {
+      const uint32_t off = offKQ == kOutOfRange ? kOutOfRange : offKQ + uint32_t(16 * i) * row_bytes;
+      stK[i] = buf_load16(rk_, off);
+      stQ[i] = buf_load16(rq_, off);
     }
+    stV = buf_load16(rv_, offV);
   };
   auto stage_store = [&](int buf) {
     char *sb = lds + kLdsStage + buf * kStageBytes;
+    if (sp_ok) {
 #pragma unroll
-    for (int i = 0; i < kPiecesPerThread; ++i) {
-      const int p = tid + 256 * i;
-      if (p < 2 * C * 14) {
-        const int m = p / (C * 14), r = (p % (C * 14)) / 14, c16 = p % 14;
-        uint2 *dst = reinterpret_cast<uint2 *>(sb + (m ? kStageQ : kStageK) + r * (kRowPad * 2) + 16 * c16);
-        dst[0] = make_uint2(stage[i].x, stage[i].y);
-        dst[1] = make_uint2(stage[i].z, stage[i].w);
-      } else if (p < kPieces) {
-        const int pv = p - 2 * C * 14, r = pv >> 1, half = pv & 1;
-        uint16_t *vt = reinterpret_cast<uint16_t *>(sb + kStageV);
-        const uint32_t w[4] = {stage[i].x, stage[i].y, stage[i].z, stage[i].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vt[(8 * half + j) * kVtPad + r] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
+      for (int i = 0; i < CT; ++i) {
+        const int off = (sr + 16 * i) * (kRowPad * 2) + 16 * sp;
+        uint2 *dk = reinterpret_cast<uint2 *>(sb + kStageK + off);
+        uint2 *dq = reinterpret_cast<uint2 *>(sb + kStageQ + off);
+        dk[0] = make_uint2(stK[i].x, stK[i].y);
+        dk[1] = make_uint2(stK[i].z, stK[i].w);
+        dq[0] = make_uint2(stQ[i].x, stQ[i].y);
+        dq[1] = make_uint2(stQ[i].z, stQ[i].w);
       }
+    }
+    if (tid < 2 * C) {
+      uint16_t *vt = reinterpret_cast<uint16_t *>(sb + kStageV);
+      const int vr = tid >> 1, half = tid & 1;
+      const uint32_t w[4] = {stV.x, stV.y, stV.z, stV.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vt[(8 * half + j) * kVtPad + vr] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
     }
   };
   // A-operand fragments of a 16-row tile of the staged K (m = 0) or Q (m = 1), "pair" k-order
@@ -224,10 +248,12 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       }
     }
     __syncthreads();
-    if (c + 1 < N) {
-      stage_issue(c + 1);
-      load_ops(nxt, c + 1);
-    }
+    // the last chunk re-fetches itself: the same instructions issue on every chunk
+    const int cn = min(c + 1, N - 1);
+    stage_issue(cn);
+    load_ops(nxt, cn);
+    const auto ro_ = make_rsrc(static_cast<char *>(o) + (size_t(b) * T + t0) * rowstride * (kOutBf16 ? 2 : 4),
+                               uint32_t(nv) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
     // ---- phase A: S operands, Y = K S^T -> R (published), Q S^T for phase-A tiles
     F32 Sh[3], Sl[3];
     F16 Sth, Stl;
@@ -348,21 +374,19 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
           acc = mma(cur.Pt[s][0], rl, acc);
           acc = mma(cur.Pt[s][1], rh, acc);
         }
+        // rows past the chunk's end fall outside the store descriptor and are dropped
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = 16 * R + 4 * lg + e;
-          if (row < nv) {
-            const size_t oi = (size_t(b) * T + t0 + row) * rowstride + size_t(h) * D + 16 * nt + ln;
-            if constexpr (kOutBf16)
-              static_cast<uint16_t *>(o)[oi] = f32_to_bf16(acc[e]);
-            else
-              static_cast<float *>(o)[oi] = acc[e];
-          }
+          const uint32_t oi = uint32_t(16 * R + 4 * lg + e) * uint32_t(rowstride) + uint32_t(h) * D + 16u * nt + ln;
+          if constexpr (kOutBf16)
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), ro_, int(oi * 2u), 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), ro_, int(oi * 4u), 0, 0);
         }
       }
     }
     // staging buffer (c + 1) & 1 was last read in chunk c - 1, before this chunk's first barrier
-    if (c + 1 < N) stage_store(buf ^ 1);
+    stage_store(buf ^ 1);
   };
 
   ChunkOps opA, opB;
