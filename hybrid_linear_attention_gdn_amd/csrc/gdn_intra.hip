@@ -1,25 +1,51 @@
-// Kernel "intra" of the MFMA family: per (b, h, chunk) operands of the state pass.
-// (The chunked algebra and the operand layouts are described in gdn_mfma_common.h.)
+// Kernel "intra" of the MFMA family: the per-chunk operands of the state pass,
+// one workgroup (4 waves) per (b, h, chunk), fully parallel.
+//
+// With raw bf16 rows K, Q of the chunk and fp32 scales (all derived here from
+// the raw inputs: rk = 1/||k||, rq = 1/||q||, beta = sigmoid(logit), G = the
+// chunk-local inclusive cumulative floored log-decay):
+//   A_ri = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i)   (i < r)
+//   P_ri = rq_r rk_i e^{G_r - G_i} (q_r . k_i)          (i <= r)
+//   T    = (I + A)^{-1}
+//   M    = K^T diag(s) T,  s_i = rk_i e^{G_n - G_i};     P' = P T
+// (the algebra behind these is written out in gdn_mfma_common.h).
+//
+// Steps:
+//  1. K rows -> LDS (row-major and transposed); squared norms of K and Q rows.
+//  2. K K^T and K Q^T on the matrix cores.  Wave w owns block-row I = 4 - w of
+//     T: it forms the blocks A_IK (K < I) transposed, so that each accumulator
+//     tile is directly the A-operand fragment A_IK needs below.  P goes to LDS.
+//  3. T, blocked: the diagonal blocks D_I = (I + A_II)^{-1} by forward
+//     substitution (fp32, one column per thread), then block distance L = 1..4:
+//     T_IJ = -D_I sum_{K=J}^{I-1} A_IK T_KJ on the matrix cores with bf16 hi/lo
+//     operands and fp32 accumulation, one block per wave per level.
+//  4. M^T = T^T diag(s) K and P'^T = T^T P^T on the matrix cores; the
+//     accumulators are exactly the A-operand fragments the state pass reads,
+//     split into bf16 hi/lo and stored.
+// T and P live in LDS as 16 x 16 fp32 blocks with 16-byte aligned rows, so
+// every operand fragment is one 128-bit LDS read.
 #include "gdn_mfma_common.h"
 
 namespace gdn {
 namespace mfma {
 namespace {
 
-// ============================================================================
-// Kernel "intra": one workgroup (4 waves) per (b, h, chunk).
-// ============================================================================
-constexpr int kKrStride = 120;  // bf16 per row of K (row-major), 240 B
-constexpr int kKtStride = 88;   // bf16 per row of K^T (d-major), 176 B
-constexpr int kBlk = 16 * 17;   // floats per padded 16x16 block
-constexpr int kLdsKr = 0;                                 // K rows, later the A blocks
-constexpr int kLdsKt = kLdsKr + 80 * kKrStride * 2;       // 19,200
-constexpr int kLdsP = kLdsKt + 112 * kKtStride * 2;       // +19,712
-constexpr int kLdsT = kLdsP + 15 * kBlk * 4;              // +16,320
-constexpr int kLdsX = kLdsT + 15 * kBlk * 4;              // +16,320
-constexpr int kLdsSc = kLdsX + 4 * kBlk * 4;              // +4,352
-constexpr int kLdsIntra = kLdsSc + 8 * 80 * 4;            // +2,560
-static_assert(15 * kBlk * 4 <= 80 * kKrStride * 2, "A blocks must fit in the K region");
+constexpr int kKrRow = 116;  // bf16 per K row (232 B): 8-byte reads of 16 rows hit distinct banks
+constexpr int kKtRow = 84;   // bf16 per K^T row (168 B)
+constexpr int kBs = 20;      // floats per row of a stored 16 x 16 block (80 B)
+constexpr int kBlkF = 16 * kBs;
+constexpr int kLdsT = 0;                              // 15 blocks of T^T, over the dead K rows
+constexpr int kLdsKr = 0;
+constexpr int kLdsKt = 15 * kBlkF * 4;                // 19,200
+constexpr int kLdsP = kLdsKt + 112 * kKtRow * 2;      // +18,816
+constexpr int kLdsAd = kLdsP + 15 * kBlkF * 4;        // +19,200: diagonal blocks of A
+constexpr int kLdsD = kLdsAd + 5 * kBlkF * 4;         // +6,400: diagonal blocks of T, row-major
+constexpr int kLdsSc = kLdsD + 5 * kBlkF * 4;         // +6,400
+constexpr int kLdsIntra = kLdsSc + 8 * 80 * 4;        // +2,560 = 72,576: two workgroups per CU
+static_assert(80 * kKrRow * 2 <= kLdsKt, "K rows fit under the T blocks");
+static_assert(2 * 80 * 14 * 4 <= 15 * kBlkF * 4, "norm partial sums fit in the P region");
+
+__device__ __forceinline__ F16 f16_of(const uint32_t *w) { return F16{{w[0], w[1]}}; }
 
 __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                        const float *__restrict__ g, const float *__restrict__ beta,
@@ -28,13 +54,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
                                                        uint32_t flags) {
   extern __shared__ __align__(16) char lds[];
   uint16_t *Kr = reinterpret_cast<uint16_t *>(lds + kLdsKr);
-  float *Ab = reinterpret_cast<float *>(lds + kLdsKr);  // aliases Kr after the K K^T products
   uint16_t *Kt = reinterpret_cast<uint16_t *>(lds + kLdsKt);
-  float *Pb = reinterpret_cast<float *>(lds + kLdsP);
-  float *Tb = reinterpret_cast<float *>(lds + kLdsT);  // block (I,J) holds (T_IJ)^T: [jj][ii]
-  float *Xb = reinterpret_cast<float *>(lds + kLdsX);
+  float *Tt = reinterpret_cast<float *>(lds + kLdsT);   // block (I, J), I >= J: [jj][m] = T[16I+m][16J+jj]
+  float *Pb = reinterpret_cast<float *>(lds + kLdsP);   // block (R, K), R >= K: [rr][kk] = P[16R+rr][16K+kk]
+  float *Ad = reinterpret_cast<float *>(lds + kLdsAd);  // block I: [ii][kk] = A[16I+ii][16I+kk]
+  float *Dm = reinterpret_cast<float *>(lds + kLdsD);   // block I: [ii][jj] = T[16I+ii][16I+jj]
   float *sc = reinterpret_cast<float *>(lds + kLdsSc);
   float *sbeta = sc, *srq = sc + 80, *srk = sc + 160, *sG = sc + 240, *ss = sc + 320;
+  auto blk = [](float *base, int I, int J) { return base + tri(I, J) * kBlkF; };
 
   // block -> (b, c, h) with h fastest: neighbouring workgroups read neighbouring rows
   int x = blockIdx.x;
@@ -46,38 +73,41 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
   const int n = min(C, T - t0);
   const size_t u = size_t(b) * H + h;
   const size_t rec = u * N + c;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lg = lane >> 4;
-
-  // ---- (0) per-token prep fused in: raw decays and beta inputs of this chunk
   const size_t rowstride = size_t(H) * D;  // elements between consecutive tokens
-  float *gl = Xb, *bl = Xb + 80;           // scratch until the triangular solve
+
+  // ---- (0) raw decays and beta inputs of this chunk (scratch in the D region)
+  float *gl = Dm, *bl = Dm + 80;
   if (tid < C) {
     const bool ok = tid < n;
     const size_t th = (size_t(b) * T + t0 + tid) * H + h;
     gl[tid] = ok ? fmaxf(g[th], kLogDecayFloor) : 0.f;
     bl[tid] = ok ? beta[th] : 0.f;
   }
-  // ---- (1) K rows -> LDS, row-major and transposed; per-row partial sums of
-  // squares of K and Q (14 slices of 8) for the norms, summed in a fixed order
-  float *sqk = Pb, *sqq = Pb + C * 14;  // the P blocks are written only after the norms
+  // ---- (1) K rows -> LDS, row-major and transposed; partial sums of squares of
+  // K and Q rows over 14 slices of 8, summed below in a fixed order
+  float *sqk = Pb, *sqq = Pb + C * 14;
   const uint16_t *kbase = k + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
-  const uint16_t *qrow0 = q + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
+  const uint16_t *qbase = q + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
   for (int idx = tid; idx < C * 14; idx += 256) {
     const int r = idx / 14, cc = idx % 14;
     uint4 val = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
     if (r < n) {
       val = ldg16(kbase + size_t(r) * rowstride + cc * 8);
-      qv = ldg16(qrow0 + size_t(r) * rowstride + cc * 8);
+      qv = ldg16(qbase + size_t(r) * rowstride + cc * 8);
     }
-    *reinterpret_cast<uint4 *>(Kr + r * kKrStride + cc * 8) = val;
+    uint2 *kr = reinterpret_cast<uint2 *>(Kr + r * kKrRow + cc * 8);
+    kr[0] = make_uint2(val.x, val.y);
+    kr[1] = make_uint2(val.z, val.w);
     const uint32_t w[4] = {val.x, val.y, val.z, val.w};
     const uint32_t wq[4] = {qv.x, qv.y, qv.z, qv.w};
     float pk = 0.f, pq = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint16_t e = uint16_t(w[j >> 1] >> (16 * (j & 1)));
-      Kt[(cc * 8 + j) * kKtStride + r] = e;
+      Kt[(cc * 8 + j) * kKtRow + r] = e;
       const float fk = bf16_to_f32(e), fq = bf16_to_f32(uint16_t(wq[j >> 1] >> (16 * (j & 1))));
       pk = fmaf(fk, fk, pk);
       pq = fmaf(fq, fq, pq);
@@ -86,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     sqq[r * 14 + cc] = pq;
   }
   __syncthreads();
-  // per-token scalars: beta, 1/||k||, 1/||q||, chunk-local cumulative decay G
+  // per-token scalars: beta, 1/||k||, 1/||q||, G; chunk scalars for the state pass
   if (tid < C) {
     const bool ok = tid < n;
     float nk = 0.f, nq = 0.f;
@@ -119,18 +149,17 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
   }
   __syncthreads();
 
-  // ---- (2) A (from K K^T) and P (from K Q^T), 15 lower tiles each
-  // A-operand rows of K from LDS in "pair" k-order; one tile = 3 x 32-deep + 1 x 16-deep.
+  // ---- (2) K K^T (transposed A blocks of this wave's block-row) and K Q^T
+  // K fragments over d in "pair" k-order: one tile = 3 x 32-deep + 1 x 16-deep
   auto kfrag32 = [&](int row, int kb) {
-    const uint16_t *p = Kr + row * kKrStride + 32 * kb + 4 * lg;
+    const uint16_t *p = Kr + row * kKrRow + 32 * kb + 4 * lg;
     const uint2 a = *reinterpret_cast<const uint2 *>(p), bq = *reinterpret_cast<const uint2 *>(p + 16);
     return F32{{a.x, a.y, bq.x, bq.y}};
   };
   auto kfrag16 = [&](int row) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(Kr + row * kKrStride + 96 + 4 * lg);
+    const uint2 a = *reinterpret_cast<const uint2 *>(Kr + row * kKrRow + 96 + 4 * lg);
     return F16{{a.x, a.y}};
   };
-  const uint16_t *qbase = q + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
   auto qfrag32 = [&](int row, int kb) {
     if (row >= n) return F32{{0, 0, 0, 0}};
     const uint16_t *p = qbase + size_t(row) * rowstride + 32 * kb + 4 * lg;
@@ -142,154 +171,171 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     const uint2 a = ldg8(qbase + size_t(row) * rowstride + 96 + 4 * lg);
     return F16{{a.x, a.y}};
   };
-  // A tiles: wave w takes tiles w, w+4, w+8, w+12 of the 15 (R >= I) in tri order
-  f32x4 aacc[4];
+  // tile with rows from tile Ka of K and columns from tile Kb of K: acc[e] = k_{16Ka+4lg+e} . k_{16Kb+ln}
+  auto kk_tile = [&](int Ka, int Kb) {
+    f32x4 acc = zero4();
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    aacc[s] = zero4();
-    const int tix = wave + 4 * s;
-    if (tix < 15) {
-      int R = 0;
-      while (tri(R + 1, 0) <= tix) ++R;
-      const int I = tix - tri(R, 0);
+    for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * Ka + ln, kb), kfrag32(16 * Kb + ln, kb), acc);
+    return mma(kfrag16(16 * Ka + ln), kfrag16(16 * Kb + ln), acc);
+  };
+  // A_{r i} with r = 16I + ln (lane row), i = 16K + 4lg + e
+  auto a_scale = [&](const f32x4 &acc, int I, int K, float *out) {
+    const int r = 16 * I + ln;
+    const float fr = sbeta[r] * srk[r];
 #pragma unroll
-      for (int kb = 0; kb < 3; ++kb) aacc[s] = mma(kfrag32(16 * R + ln, kb), kfrag32(16 * I + ln, kb), aacc[s]);
-      aacc[s] = mma(kfrag16(16 * R + ln), kfrag16(16 * I + ln), aacc[s]);
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * K + 4 * lg + e;
+      out[e] = (i < r) ? fr * srk[i] * expf(sG[r] - sG[i]) * acc[e] : 0.f;
+    }
+  };
+  const int I = 4 - wave;  // block-row of T owned by this wave (4, 3, 2, 1)
+  F16 Ah[4], Al[4];        // A_IK, K < I, as 16-deep A-operand fragments (hi, lo)
+#pragma unroll
+  for (int K = 0; K < 4; ++K) {
+    Ah[K] = F16{{0, 0}};
+    Al[K] = F16{{0, 0}};
+    if (K < I) {
+      float v[4];
+      a_scale(kk_tile(K, I), I, K, v);
+      uint32_t hi[2], lo[2];
+      split4(v, hi, lo);
+      Ah[K] = f16_of(hi);
+      Al[K] = f16_of(lo);
     }
   }
-  // P^T tiles (I <= R): accumulator rows = key tokens i, columns = query tokens r
+  // diagonal blocks A_II (and A_00 by the last wave) -> LDS, row-major
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int Id = d == 0 ? I : 0;
+    if (d == 0 || wave == 3) {
+      float v[4];
+      a_scale(kk_tile(Id, Id), Id, Id, v);
+      *reinterpret_cast<float4 *>(Ad + Id * kBlkF + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  // P^T tiles (kk-tile It <= query tile Rt): acc[e] = k_{16It+4lg+e} . q_{16Rt+ln}
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int tix = wave + 4 * s;
     if (tix < 15) {
-      int R = 0;
-      while (tri(R + 1, 0) <= tix) ++R;
-      const int I = tix - tri(R, 0);
+      int Rt = 0;
+      while (tri(Rt + 1, 0) <= tix) ++Rt;
+      const int It = tix - tri(Rt, 0);
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * I + ln, kb), qfrag32(16 * R + ln, kb), acc);
-      acc = mma(kfrag16(16 * I + ln), qfrag16(16 * R + ln), acc);
-      // P[r][i] for i <= r into block (R, I) row-major
-      const int r = 16 * R + ln;
-      float *blk = Pb + tri(R, I) * kBlk;
+      for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * It + ln, kb), qfrag32(16 * Rt + ln, kb), acc);
+      acc = mma(kfrag16(16 * It + ln), qfrag16(16 * Rt + ln), acc);
+      const int r = 16 * Rt + ln;
+      const float fr = srq[r];
+      float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * I + 4 * lg + e;
-        const float val = (i <= r) ? srq[r] * srk[i] * expf(sG[r] - sG[i]) * acc[e] : 0.f;
-        blk[ln * 17 + 4 * lg + e] = val;
+        const int i = 16 * It + 4 * lg + e;
+        v[e] = (i <= r) ? fr * srk[i] * expf(sG[r] - sG[i]) * acc[e] : 0.f;
       }
+      *reinterpret_cast<float4 *>(blk(Pb, Rt, It) + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
-  __syncthreads();  // every read of Kr is done: the A blocks may overwrite it
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int tix = wave + 4 * s;
-    if (tix < 15) {
-      int R = 0;
-      while (tri(R + 1, 0) <= tix) ++R;
-      const int I = tix - tri(R, 0);
-      // accumulator: column i = 16I + ln, rows r = 16R + 4lg + e
-      const int i = 16 * I + ln;
-      float *blk = Ab + tri(R, I) * kBlk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * R + 4 * lg + e;
-        const float val = (i < r) ? sbeta[r] * srk[r] * srk[i] * expf(sG[r] - sG[i]) * aacc[s][e] : 0.f;
-        blk[(4 * lg + e) * 17 + ln] = val;
-      }
-    }
-  }
-  __syncthreads();
+  __syncthreads();  // K rows are dead from here on: their LDS now holds the T blocks
 
-  // ---- (3) T = (I + A)^{-1}: diagonal blocks by forward substitution ...
+  // ---- (3a) diagonal blocks of T by forward substitution, one column per thread
   if (tid < C) {
-    const int I = tid >> 4, cc = tid & 15;
-    const float *Ad = Ab + tri(I, I) * kBlk;
+    const int Ib = tid >> 4, cc = tid & 15;
+    const float *A = Ad + Ib * kBlkF;
     float xv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float s = 0.f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) s = fmaf(Ad[r * 17 + m], xv[m], s);
+      for (int m = 0; m < r; ++m) s = fmaf(A[r * kBs + m], xv[m], s);
       xv[r] = (r < cc) ? 0.f : (r == cc ? 1.f : -s);
     }
-    float *Td = Tb + tri(I, I) * kBlk;
+    float *Dr = Dm + Ib * kBlkF;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Td[cc * 17 + r] = xv[r];
+    for (int r = 0; r < 16; ++r) Dr[r * kBs + cc] = xv[r];
+    float4 *Tr = reinterpret_cast<float4 *>(blk(Tt, Ib, Ib) + cc * kBs);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) Tr[q4] = make_float4(xv[4 * q4], xv[4 * q4 + 1], xv[4 * q4 + 2], xv[4 * q4 + 3]);
   }
   __syncthreads();
-  // ... then block rows by distance L: T_IJ = -D_I sum_{K=J}^{I-1} A_IK T_KJ
+  // ---- (3b) off-diagonal blocks, one block-distance per step
+  auto ld4 = [](const float *p) {
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    return f32x4{t.x, t.y, t.z, t.w};
+  };
+#pragma unroll
   for (int L = 1; L < CT; ++L) {
-    const int nb = CT - L;
-    for (int e = tid; e < nb * 256; e += 256) {
-      const int J = e >> 8, I = J + L, ii = (e >> 4) & 15, jj = e & 15;
-      float s = 0.f;
-      for (int K = J; K < I; ++K) {
-        const float *Aik = Ab + tri(I, K) * kBlk + ii * 17;
-        const float *Tkj = Tb + tri(K, J) * kBlk + jj * 17;  // (T_KJ)^T row jj
+    const int J = I - L;
+    if (J >= 0) {
+      f32x4 X = zero4();
 #pragma unroll
-        for (int m = 0; m < 16; ++m) s = fmaf(Aik[m], Tkj[m], s);
+      for (int K = 0; K < 4; ++K) {
+        if (K >= J && K < I) {
+          // B operand T_KJ: lane (column jj = ln, group lg) holds T[16K + 4lg + j][16J + ln]
+          uint32_t th[2], tl[2];
+          split4(ld4(blk(Tt, K, J) + ln * kBs + 4 * lg), th, tl);
+          const F16 bh = f16_of(th), bl = f16_of(tl);
+          X = mma(Ah[K], bh, X);
+          X = mma(Ah[K], bl, X);
+          X = mma(Al[K], bh, X);
+        }
       }
-      Xb[J * kBlk + ii * 17 + jj] = s;
-    }
-    __syncthreads();
-    for (int e = tid; e < nb * 256; e += 256) {
-      const int J = e >> 8, I = J + L, ii = (e >> 4) & 15, jj = e & 15;
-      const float *Dt = Tb + tri(I, I) * kBlk;  // (D_I)^T: Dt[m][ii] = D_I[ii][m]
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) s = fmaf(Dt[m * 17 + ii], Xb[J * kBlk + m * 17 + jj], s);
-      Tb[tri(I, J) * kBlk + jj * 17 + ii] = -s;
+      uint32_t xh[2], xl[2], dh[2], dl[2];
+      split4(X, xh, xl);
+      split4(ld4(Dm + I * kBlkF + ln * kBs + 4 * lg), dh, dl);
+      f32x4 Tij = zero4();
+      Tij = mma(f16_of(dh), f16_of(xh), Tij);
+      Tij = mma(f16_of(dh), f16_of(xl), Tij);
+      Tij = mma(f16_of(dl), f16_of(xh), Tij);
+      // accumulator: column jj = ln, rows ii = 4lg + e -> T[16I + 4lg + e][16J + ln]
+      *reinterpret_cast<float4 *>(blk(Tt, I, J) + ln * kBs + 4 * lg) = make_float4(-Tij[0], -Tij[1], -Tij[2], -Tij[3]);
     }
     __syncthreads();
   }
 
   // ---- (4) M^T = T^T diag(s) K  and  P'^T = T^T P^T, split and stored
-  // Tt(r, i) = T[i][r] for i >= r lives in block (tile(i), tile(r)) at [r%16][i%16]
-  auto tt = [&](int r, int i) { return Tb[tri(i >> 4, r >> 4) * kBlk + (r & 15) * 17 + (i & 15)]; };
+  // Row r of T^T over columns i = 16p + 4lg .. +3 (p >= r / 16): one 128-bit read.
+  auto tt4 = [&](int r, int p) { return ld4(blk(Tt, p, r >> 4) + (r & 15) * kBs + 4 * lg); };
   char *Mrec = Mout + rec * size_t(kMBytes);
   char *Prec = Pout + rec * size_t(kPBytes);
-  // task list: 35 M^T tiles (Rt, Dt) then 15 P'^T tiles (It <= Rt)
   for (int task = wave; task < 50; task += 4) {
     if (task < 35) {
       const int Rt = task / NT, Dt = task % NT;
-      const int r = 16 * Rt + ln;  // A-operand row (output token row of M^T)
+      const int r = 16 * Rt + ln;
       f32x4 acc = zero4();
       int p = Rt;
       while (p < CT) {
         if (p + 1 < CT) {  // 32-deep block over token tiles p, p+1
+          const f32x4 t0v = tt4(r, p), t1v = tt4(r, p + 1);
+          const f32x4 s0 = ld4(ss + 16 * p + 4 * lg), s1 = ld4(ss + 16 * p + 16 + 4 * lg);
           float v[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 16 * (p + (j >> 2)) + 4 * lg + (j & 3);
-            v[j] = (i >= r) ? tt(r, i) * ss[i] : 0.f;
+          for (int j = 0; j < 4; ++j) {
+            v[j] = t0v[j] * s0[j];
+            v[4 + j] = t1v[j] * s1[j];
           }
           F32 ah, al;
           split4(v, ah.w, al.w);
           split4(v + 4, ah.w + 2, al.w + 2);
-          const uint16_t *kt = Kt + (16 * Dt + ln) * kKtStride + 16 * p + 4 * lg;
+          const uint16_t *kt = Kt + (16 * Dt + ln) * kKtRow + 16 * p + 4 * lg;
           const uint2 k0 = *reinterpret_cast<const uint2 *>(kt), k1 = *reinterpret_cast<const uint2 *>(kt + 16);
           const F32 bk{{k0.x, k0.y, k1.x, k1.y}};
           acc = mma(ah, bk, acc);
           acc = mma(al, bk, acc);
           p += 2;
         } else {  // 16-deep block over tile p
-          float v[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 16 * p + 4 * lg + j;
-            v[j] = (i >= r) ? tt(r, i) * ss[i] : 0.f;
-          }
-          F16 ah, al;
-          split4(v, ah.w, al.w);
-          const uint2 k0 = *reinterpret_cast<const uint2 *>(Kt + (16 * Dt + ln) * kKtStride + 16 * p + 4 * lg);
+          const f32x4 t0v = tt4(r, p), s0 = ld4(ss + 16 * p + 4 * lg);
+          const float v[4] = {t0v[0] * s0[0], t0v[1] * s0[1], t0v[2] * s0[2], t0v[3] * s0[3]};
+          uint32_t hi[2], lo[2];
+          split4(v, hi, lo);
+          const uint2 k0 = *reinterpret_cast<const uint2 *>(Kt + (16 * Dt + ln) * kKtRow + 16 * p + 4 * lg);
           const F16 bk{{k0.x, k0.y}};
-          acc = mma(ah, bk, acc);
-          acc = mma(al, bk, acc);
+          acc = mma(f16_of(hi), bk, acc);
+          acc = mma(f16_of(lo), bk, acc);
           p += 1;
         }
       }
-      // accumulator: column d = 16Dt + ln, rows r = 16Rt + 4lg + e -> M[d][r], chain A-operand order
+      // accumulator: column d = 16Dt + ln, rows r = 16Rt + 4lg + e -> M[d][r], the state pass's A-operand order
       uint32_t hi[2], lo[2];
       split4(acc, hi, lo);
       if (Rt < 4) {
@@ -304,47 +350,34 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
       int tix = task - 35, Rt = 0;
       while (tri(Rt + 1, 0) <= tix) ++Rt;
       const int It = tix - tri(Rt, 0);
-      // P'^T[i][r] = sum_{k=i}^{r} T[k][i] P[r][k]; A rows i = 16It + ln, B columns r = 16Rt + ln
-      const int i = 16 * It + ln, r = 16 * Rt + ln;
-      const float *prow = Pb + ln * 17;  // row r of P inside block (Rt, kt)
+      // P'^T[i][r] = sum_{kk=i}^{r} T[kk][i] P[r][kk]; A rows i = 16It + ln, B columns r = 16Rt + ln
+      const int i = 16 * It + ln;
       f32x4 acc = zero4();
       int p = It;
       while (p <= Rt) {
         if (p + 1 <= Rt) {
-          float va[8], vb[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int kk = 16 * (p + (j >> 2)) + 4 * lg + (j & 3);
-            va[j] = (kk >= i) ? tt(i, kk) : 0.f;
-            vb[j] = (kk <= r) ? prow[tri(Rt, kk >> 4) * kBlk + (kk & 15)] : 0.f;
-          }
+          const f32x4 a0 = tt4(i, p), a1 = tt4(i, p + 1);
+          const f32x4 b0 = ld4(blk(Pb, Rt, p) + ln * kBs + 4 * lg), b1 = ld4(blk(Pb, Rt, p + 1) + ln * kBs + 4 * lg);
           F32 ah, al, bh, bl;
-          split4(va, ah.w, al.w);
-          split4(va + 4, ah.w + 2, al.w + 2);
-          split4(vb, bh.w, bl.w);
-          split4(vb + 4, bh.w + 2, bl.w + 2);
+          split4(a0, ah.w, al.w);
+          split4(a1, ah.w + 2, al.w + 2);
+          split4(b0, bh.w, bl.w);
+          split4(b1, bh.w + 2, bl.w + 2);
           acc = mma(ah, bh, acc);
           acc = mma(ah, bl, acc);
           acc = mma(al, bh, acc);
           p += 2;
         } else {
-          float va[4], vb[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int kk = 16 * p + 4 * lg + j;
-            va[j] = (kk >= i) ? tt(i, kk) : 0.f;
-            vb[j] = (kk <= r) ? prow[tri(Rt, kk >> 4) * kBlk + (kk & 15)] : 0.f;
-          }
-          F16 ah, al, bh, bl;
-          split4(va, ah.w, al.w);
-          split4(vb, bh.w, bl.w);
-          acc = mma(ah, bh, acc);
-          acc = mma(ah, bl, acc);
-          acc = mma(al, bh, acc);
+          uint32_t ah[2], al[2], bh[2], bl[2];
+          split4(tt4(i, p), ah, al);
+          split4(ld4(blk(Pb, Rt, p) + ln * kBs + 4 * lg), bh, bl);
+          acc = mma(f16_of(ah), f16_of(bh), acc);
+          acc = mma(f16_of(ah), f16_of(bl), acc);
+          acc = mma(f16_of(al), f16_of(bh), acc);
           p += 1;
         }
       }
-      // accumulator: column r = 16Rt + ln, rows i = 16It + 4lg + e -> P'[r][i], chain A-operand order
+      // accumulator: column r = 16Rt + ln, rows i = 16It + 4lg + e -> P'[r][i], the state pass's A-operand order
       uint32_t hi[2], lo[2];
       split4(acc, hi, lo);
       if (It == Rt && !(Rt & 1)) {
@@ -364,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
 hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs) {
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k);
   const unsigned chunks = unsigned(p.B) * p.H * p.N;
-  // the intra kernel needs more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU)
+  // more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU)
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsIntra);
   if (lds_ok != hipSuccess) return lds_ok;
