@@ -36,7 +36,8 @@ constexpr int kBs = 20;      // floats per row of a stored 16 x 16 block (80 B)
 constexpr int kBlkF = 16 * kBs;
 constexpr int kLdsT = 0;                              // 15 blocks of T^T, over the dead K rows
 constexpr int kLdsKr = 0;
-constexpr int kLdsKt = 15 * kBlkF * 4;                // 19,200
+constexpr int kLdsKt = 15 * kBlkF * 4;                // 19,200: Q rows until step 2 ends, then K^T
+constexpr int kLdsQr = kLdsKt;
 constexpr int kLdsP = kLdsKt + 112 * kKtRow * 2;      // +18,816
 constexpr int kLdsAd = kLdsP + 15 * kBlkF * 4;        // +19,200: diagonal blocks of A
 constexpr int kLdsD = kLdsAd + 5 * kBlkF * 4;         // +6,400: diagonal blocks of T, row-major
@@ -86,34 +87,45 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     gl[tid] = ok ? fmaxf(g[th], kLogDecayFloor) : 0.f;
     bl[tid] = ok ? beta[th] : 0.f;
   }
-  // ---- (1) K rows -> LDS, row-major and transposed; partial sums of squares of
-  // K and Q rows over 14 slices of 8, summed below in a fixed order
+  // ---- (1) K and Q rows -> LDS (row-major); partial sums of squares over 14
+  // slices of 8, summed below in a fixed order.  All row loads are issued
+  // before any is used.
   float *sqk = Pb, *sqq = Pb + C * 14;
+  uint16_t *Qr = reinterpret_cast<uint16_t *>(lds + kLdsQr);
   const uint16_t *kbase = k + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
   const uint16_t *qbase = q + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
-  for (int idx = tid; idx < C * 14; idx += 256) {
-    const int r = idx / 14, cc = idx % 14;
-    uint4 val = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-    if (r < n) {
-      val = ldg16(kbase + size_t(r) * rowstride + cc * 8);
-      qv = ldg16(qbase + size_t(r) * rowstride + cc * 8);
-    }
-    uint2 *kr = reinterpret_cast<uint2 *>(Kr + r * kKrRow + cc * 8);
-    kr[0] = make_uint2(val.x, val.y);
-    kr[1] = make_uint2(val.z, val.w);
-    const uint32_t w[4] = {val.x, val.y, val.z, val.w};
-    const uint32_t wq[4] = {qv.x, qv.y, qv.z, qv.w};
-    float pk = 0.f, pq = 0.f;
+  constexpr int kRowPieces = (C * 14 + 255) / 256;  // 5 pieces of 16 bytes per thread and matrix
+  uint4 kv[kRowPieces], qv[kRowPieces];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint16_t e = uint16_t(w[j >> 1] >> (16 * (j & 1)));
-      Kt[(cc * 8 + j) * kKtRow + r] = e;
-      const float fk = bf16_to_f32(e), fq = bf16_to_f32(uint16_t(wq[j >> 1] >> (16 * (j & 1))));
-      pk = fmaf(fk, fk, pk);
-      pq = fmaf(fq, fq, pq);
+  for (int i = 0; i < kRowPieces; ++i) {
+    const int idx = tid + 256 * i, r = idx / 14, cc = idx % 14;
+    const bool ok = idx < C * 14 && r < n;
+    kv[i] = ok ? ldg16(kbase + size_t(r) * rowstride + cc * 8) : make_uint4(0, 0, 0, 0);
+    qv[i] = ok ? ldg16(qbase + size_t(r) * rowstride + cc * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kRowPieces; ++i) {
+    const int idx = tid + 256 * i, r = idx / 14, cc = idx % 14;
+    if (idx < C * 14) {
+      uint2 *kr = reinterpret_cast<uint2 *>(Kr + r * kKrRow + cc * 8);
+      uint2 *qr = reinterpret_cast<uint2 *>(Qr + r * kKrRow + cc * 8);
+      kr[0] = make_uint2(kv[i].x, kv[i].y);
+      kr[1] = make_uint2(kv[i].z, kv[i].w);
+      qr[0] = make_uint2(qv[i].x, qv[i].y);
+      qr[1] = make_uint2(qv[i].z, qv[i].w);
+      const uint32_t w[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+      const uint32_t wq[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
+      float pk = 0.f, pq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float fk = bf16_to_f32(uint16_t(w[j >> 1] >> (16 * (j & 1))));
+        const float fq = bf16_to_f32(uint16_t(wq[j >> 1] >> (16 * (j & 1))));
+        pk = fmaf(fk, fk, pk);
+        pq = fmaf(fq, fq, pq);
+      }
+      sqk[r * 14 + cc] = pk;
+      sqq[r * 14 + cc] = pq;
     }
-    sqk[r * 14 + cc] = pk;
-    sqq[r * 14 + cc] = pq;
   }
   __syncthreads();
   // per-token scalars: beta, 1/||k||, 1/||q||, G; chunk scalars for the state pass
@@ -161,14 +173,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     return F16{{a.x, a.y}};
   };
   auto qfrag32 = [&](int row, int kb) {
-    if (row >= n) return F32{{0, 0, 0, 0}};
-    const uint16_t *p = qbase + size_t(row) * rowstride + 32 * kb + 4 * lg;
-    const uint2 a = ldg8(p), bq = ldg8(p + 16);
+    const uint16_t *p = Qr + row * kKrRow + 32 * kb + 4 * lg;
+    const uint2 a = *reinterpret_cast<const uint2 *>(p), bq = *reinterpret_cast<const uint2 *>(p + 16);
     return F32{{a.x, a.y, bq.x, bq.y}};
   };
   auto qfrag16 = [&](int row) {
-    if (row >= n) return F16{{0, 0}};
-    const uint2 a = ldg8(qbase + size_t(row) * rowstride + 96 + 4 * lg);
+    const uint2 a = *reinterpret_cast<const uint2 *>(Qr + row * kKrRow + 96 + 4 * lg);
     return F16{{a.x, a.y}};
   };
   // tile with rows from tile Ka of K and columns from tile Kb of K: acc[e] = k_{16Ka+4lg+e} . k_{16Kb+ln}
@@ -235,6 +245,16 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
       }
       *reinterpret_cast<float4 *>(blk(Pb, Rt, It) + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
     }
+  }
+  __syncthreads();
+  // Q rows are dead: K^T (d-major, for step 4) takes their place, built from the K rows
+  for (int idx = tid; idx < C * 14; idx += 256) {
+    const int r = idx / 14, cc = idx % 14;
+    const uint2 *kr = reinterpret_cast<const uint2 *>(Kr + r * kKrRow + cc * 8);
+    const uint2 lo = kr[0], hi = kr[1];
+    const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Kt[(cc * 8 + j) * kKtRow + r] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
   }
   __syncthreads();  // K rows are dead from here on: their LDS now holds the T blocks
 
