@@ -8,13 +8,14 @@
 // tiles spread over the waves.  Per chunk, two barriers exchange the bf16
 // hi/lo operands S (after phase 0) and R (after phase A) through LDS.
 //
-// Operand traffic.  K, Q and this workgroup's 16 columns of V are staged in
-// LDS one chunk ahead by all 256 threads with 16-byte row loads (a 224-byte
-// bf16 row is 14 such pieces), double-buffered; each wave then reads its
+// Operand traffic.  K, Q and this workgroup's 16 columns of V are loaded two
+// chunks ahead by all 256 threads with 16-byte row loads (a 224-byte bf16 row
+// is 14 such pieces) into a register set, and written to one of two LDS
+// staging buffers a step later; each wave then reads its
 // fragments from LDS (rows padded to 232 bytes so the 8-byte fragment reads
 // of 16 consecutive rows fall in distinct banks).  The fragment-ordered M and
-// P' records and the per-token scales are read straight into registers, one
-// chunk ahead: every such load is a contiguous 1 KB per instruction.
+// P' records and the per-token scales are read straight into registers, two
+// chunks ahead: every such load is a contiguous 1 KB per instruction.
 #include "gdn_mfma_common.h"
 
 namespace gdn {
@@ -118,8 +119,10 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
   const uint32_t offKQ = sp_ok ? uint32_t(sr) * row_bytes + uint32_t(h) * (D * 2) + 16u * sp : kOutOfRange;
   const uint32_t offV = tid < 2 * C ? uint32_t(tid >> 1) * row_bytes + uint32_t(h) * (D * 2) + 32u * nt + 16u * (tid & 1)
                                     : kOutOfRange;
-  uint4 stK[CT], stQ[CT], stV;
-  auto stage_issue = [&](int c) {
+  struct Staged {
+    uint4 k[CT], q[CT], v;
+  };
+  auto stage_issue = [&](Staged &st, int c) {
     const int t0 = c * C, nv = min(C, T - t0);
     const size_t base = (size_t(b) * T + t0) * rowstride;
     const uint32_t bytes = uint32_t(nv) * row_bytes;
@@ -127,12 +130,12 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
 #pragma unroll
     for (int i = 0; i < CT; ++i) {
       const uint32_t off = offKQ == kOutOfRange ? kOutOfRange : offKQ + uint32_t(16 * i) * row_bytes;
-      stK[i] = buf_load16(rk_, off);
-      stQ[i] = buf_load16(rq_, off);
+      st.k[i] = buf_load16(rk_, off);
+      st.q[i] = buf_load16(rq_, off);
     }
-    stV = buf_load16(rv_, offV);
+    st.v = buf_load16(rv_, offV);
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](const Staged &st, int buf) {
     char *sb = lds + kLdsStage + buf * kStageBytes;
     if (sp_ok) {
 #pragma unroll
@@ -140,16 +143,16 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
         const int off = (sr + 16 * i) * (kRowPad * 2) + 16 * sp;
         uint2 *dk = reinterpret_cast<uint2 *>(sb + kStageK + off);
         uint2 *dq = reinterpret_cast<uint2 *>(sb + kStageQ + off);
-        dk[0] = make_uint2(stK[i].x, stK[i].y);
-        dk[1] = make_uint2(stK[i].z, stK[i].w);
-        dq[0] = make_uint2(stQ[i].x, stQ[i].y);
-        dq[1] = make_uint2(stQ[i].z, stQ[i].w);
+        dk[0] = make_uint2(st.k[i].x, st.k[i].y);
+        dk[1] = make_uint2(st.k[i].z, st.k[i].w);
+        dq[0] = make_uint2(st.q[i].x, st.q[i].y);
+        dq[1] = make_uint2(st.q[i].z, st.q[i].w);
       }
     }
     if (tid < 2 * C) {
       uint16_t *vt = reinterpret_cast<uint16_t *>(sb + kStageV);
       const int vr = tid >> 1, half = tid & 1;
-      const uint32_t w[4] = {stV.x, stV.y, stV.z, stV.w};
+      const uint32_t w[4] = {st.v.x, st.v.y, st.v.z, st.v.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) vt[(8 * half + j) * kVtPad + vr] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
     }
@@ -167,6 +170,42 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
     const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 192 + 8 * lg);
     rf.t = F16{{x2.x, x2.y}};
     return rf;
+  };
+
+  // ---- L2 warm-up of chunk c + kAhead: the head's 7 column-tile workgroups
+  // (on one XCD) split its cache lines -- 280 of M, 120 of P', 8 of scales and
+  // 3 per 224-byte row of K, Q, V -- so that the staging and operand loads of
+  // that chunk hit L2 instead of all waiting on the same HBM misses.  One
+  // dword load per lane, at a fixed per-lane base plus a per-chunk stride.
+  constexpr int kAhead = 4;
+  const char *pe_base;
+  size_t pe_stride;
+  int pe_row = -1;
+  {
+    const int pe = nt + NT * (64 * (tid >> 6) + lane);  // 0 .. 1791, cache-line task
+    if (pe < 280) {
+      pe_base = Mws + u * N * size_t(kMBytes) + 128 * pe;
+      pe_stride = kMBytes;
+    } else if (pe < 400) {
+      pe_base = Pws + u * N * size_t(kPBytes) + 128 * (pe - 280);
+      pe_stride = kPBytes;
+    } else if (pe < 408) {
+      pe_base = reinterpret_cast<const char *>(CS + u * N * kCsFloats) + 128 * (pe - 400);
+      pe_stride = kCsFloats * sizeof(float);
+    } else {
+      const int r = min(pe - 408, 3 * 3 * C - 1), t = r / (3 * C), part = r % 3;
+      pe_row = (r % (3 * C)) / 3;
+      const uint16_t *src = t == 0 ? k : (t == 1 ? q : v);
+      pe_base = reinterpret_cast<const char *>(src + (size_t(b) * T * H + h) * D) + (part == 0 ? 0 : (part == 1 ? 128 : 220));
+      pe_stride = size_t(C) * row_bytes;
+    }
+  }
+  auto l2_touch = [&](int c) -> uint32_t {
+    const int cp = min(c + kAhead, N - 1);
+    // a row past the end of the last chunk touches the chunk's last row instead
+    const int rr = pe_row < 0 ? 0 : min(pe_row, T - 1 - cp * C);
+    const char *a = pe_base + size_t(cp) * pe_stride + size_t(rr) * row_bytes;
+    return *reinterpret_cast<const uint32_t *>(a);
   };
 
   auto load_ops = [&](ChunkOps &op, int c) {
@@ -228,7 +267,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
   };
 
   // one chunk: consume `cur` and staging buffer c & 1; put chunk c + 1 in flight
-  auto step = [&](int c, const ChunkOps &cur, ChunkOps &nxt) {
+  auto step = [&](int c, const ChunkOps &cur, ChunkOps &ahead, Staged &st_issue, const Staged &st_store) {
     const int t0 = c * C, nv = min(C, T - t0), buf = c & 1;
     // ---- phase 0: publish this wave's state tiles as bf16 hi/lo B operands
 #pragma unroll
@@ -248,10 +287,6 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       }
     }
     __syncthreads();
-    // the last chunk re-fetches itself: the same instructions issue on every chunk
-    const int cn = min(c + 1, N - 1);
-    stage_issue(cn);
-    load_ops(nxt, cn);
     const auto ro_ = make_rsrc(static_cast<char *>(o) + (size_t(b) * T + t0) * rowstride * (kOutBf16 ? 2 : 4),
                                uint32_t(nv) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
     // ---- phase A: S operands, Y = K S^T -> R (published), Q S^T for phase-A tiles
@@ -308,7 +343,10 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
     f32x4 QS[2] = {zero4(), zero4()};
     if (ro.nQA) QS[0] = rows_times_S(rows_frag(buf, 1, ro.QA[0]));
     __syncthreads();
-    // ---- phase B: R operands; state update and outputs
+    // ---- phase B: R operands; state update and outputs.  The operand
+    // fragments of chunk c + 2 are requested here (past the end, the last
+    // chunk is fetched again: the same instructions issue on every chunk).
+    load_ops(ahead, min(c + 2, N - 1));
     F32 Rh[2], Rl[2];
     F16 Rth, Rtl;
 #pragma unroll
@@ -385,18 +423,41 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
         }
       }
     }
-    // staging buffer (c + 1) & 1 was last read in chunk c - 1, before this chunk's first barrier
-    stage_store(buf ^ 1);
+    // K/Q/V rows two chunks ahead go into the register set freed by the last
+    // store; the set loaded one step ago (chunk c + 1) goes to staging buffer
+    // (c + 1) & 1, last read in chunk c - 1, before this chunk's first barrier.
+    stage_issue(st_issue, min(c + 2, N - 1));
+    stage_store(st_store, buf ^ 1);
   };
 
-  ChunkOps opA, opB;
-  stage_issue(0);
-  load_ops(opA, 0);
-  stage_store(0);
-  for (int c = 0; c < N; c += 2) {
-    step(c, opA, opB);
-    if (c + 1 < N) step(c + 1, opB, opA);
+  // Three operand sets and three staging register sets rotate with the chunk
+  // index mod 3 (chunk c + 1 landed, c + 2 in flight, c being consumed).
+  ChunkOps op0, op1, op2;
+  Staged st0, st1, st2;
+  stage_issue(st0, 0);
+  load_ops(op0, 0);
+  stage_store(st0, 0);
+  stage_issue(st1, min(1, N - 1));
+  load_ops(op1, min(1, N - 1));
+  uint32_t pf = 0, sink = 0;
+  auto touch = [&](int c) {
+    sink ^= pf;  // consumed a step after its load was issued
+    pf = l2_touch(c);
+  };
+  for (int c = 0; c < N; c += 3) {
+    step(c, op0, op2, st2, st1);
+    touch(c);
+    if (c + 1 < N) {
+      step(c + 1, op1, op0, st0, st2);
+      touch(c + 1);
+    }
+    if (c + 2 < N) {
+      step(c + 2, op2, op1, st1, st0);
+      touch(c + 2);
+    }
   }
+  sink ^= pf;
+  if (T < 0 && sink != 0u) static_cast<uint32_t *>(o)[0] = sink;  // never taken: keeps the touches alive
   if (state_out) {
 #pragma unroll
     for (int s = 0; s < 3; ++s)
