@@ -19,7 +19,8 @@
 //     substitution (fp32, one column per thread), then block distance L = 1..4:
 //     T_IJ = -D_I sum_{K=J}^{I-1} A_IK T_KJ on the matrix cores with bf16 hi/lo
 //     operands and fp32 accumulation, one block per wave per level.
-//  4. M^T = T^T diag(s) K and P'^T = T^T P^T on the matrix cores; the
+//  4. M^T = T^T diag(s) K and P'^T = T^T P^T on the matrix cores, each wave
+//     owning whole token-row tiles (their hi/lo fragments are built once); the
 //     accumulators are exactly the A-operand fragments the state pass reads,
 //     split into bf16 hi/lo and stored.
 // T and P live in LDS as 16 x 16 fp32 blocks with 16-byte aligned rows, so
@@ -128,36 +129,50 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     }
   }
   __syncthreads();
-  // per-token scalars: beta, 1/||k||, 1/||q||, G; chunk scalars for the state pass
-  if (tid < C) {
-    const bool ok = tid < n;
-    float nk = 0.f, nq = 0.f;
+  // per-token scalars: beta, 1/||k||, 1/||q||, G; chunk scalars for the state pass.
+  // Wave 0: lane l takes tokens l and 64 + l (l < 16); G, the inclusive prefix
+  // sum of the floored log-decays over the chunk, comes from two wave scans.
+  if (wave == 0) {
+    auto scan = [&](float x) {
 #pragma unroll
-    for (int cc = 0; cc < 14; ++cc) {
-      nk += sqk[tid * 14 + cc];
-      nq += sqq[tid * 14 + cc];
-    }
-    const float rk = (flags & kQkPrenormalized) ? 1.f : 1.f / fmaxf(sqrtf(nk), 1e-6f);
-    const float rq = (flags & kQkPrenormalized) ? 1.f : 1.f / fmaxf(sqrtf(nq), 1e-6f);
-    const float bt = (flags & kBetaIsProb) ? bl[tid] : 1.f / (1.f + expf(-bl[tid]));
-    // inclusive prefix in token order (the same additions as a sequential scan)
-    float G = 0.f, Gl = 0.f;
-    for (int j = 0; j < C; ++j) {
-      Gl += gl[j];
-      if (j == tid) G = Gl;
-    }
-    const float bo = ok ? bt : 0.f, rko = ok ? rk : 0.f, rqo = ok ? rq : 0.f;
-    const float gam = expf(G);
-    sbeta[tid] = bo;
-    srq[tid] = rqo;
-    srk[tid] = rko;
-    sG[tid] = G;
-    ss[tid] = rko * expf(Gl - G);
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      return x;
+    };
+    const float G0 = scan(gl[lane]);
+    const float G1 = scan(lane < C - 64 ? gl[64 + lane] : 0.f) + __shfl(G0, 63);
+    const float Gl = __shfl(G1, C - 65);  // G at the chunk's last token
     float *cs = CSout + rec * kCsFloats;
-    cs[tid] = bo;
-    cs[80 + tid] = bo * gam * rko;
-    cs[160 + tid] = gam * rqo;
-    if (tid == 0) cs[240] = expf(Gl);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int t = s2 == 0 ? lane : 64 + lane;
+      if (t < C) {
+        const bool ok = t < n;
+        float nk = 0.f, nq = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 14; ++cc) {
+          nk += sqk[t * 14 + cc];
+          nq += sqq[t * 14 + cc];
+        }
+        const float rk = (flags & kQkPrenormalized) ? 1.f : 1.f / fmaxf(sqrtf(nk), 1e-6f);
+        const float rq = (flags & kQkPrenormalized) ? 1.f : 1.f / fmaxf(sqrtf(nq), 1e-6f);
+        const float bt = (flags & kBetaIsProb) ? bl[t] : 1.f / (1.f + expf(-bl[t]));
+        const float G = s2 == 0 ? G0 : G1;
+        const float bo = ok ? bt : 0.f, rko = ok ? rk : 0.f, rqo = ok ? rq : 0.f;
+        const float gam = expf(G);
+        sbeta[t] = bo;
+        srq[t] = rqo;
+        srk[t] = rko;
+        sG[t] = G;
+        ss[t] = rko * expf(Gl - G);
+        cs[t] = bo;
+        cs[80 + t] = bo * gam * rko;
+        cs[160 + t] = gam * rqo;
+      }
+    }
+    if (lane == 0) cs[240] = expf(Gl);
   }
   __syncthreads();
 
@@ -181,32 +196,44 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     const uint2 a = *reinterpret_cast<const uint2 *>(Qr + row * kKrRow + 96 + 4 * lg);
     return F16{{a.x, a.y}};
   };
-  // tile with rows from tile Ka of K and columns from tile Kb of K: acc[e] = k_{16Ka+4lg+e} . k_{16Kb+ln}
-  auto kk_tile = [&](int Ka, int Kb) {
+  // decay factor e^{x}, x = G_r - G_i <= 0, on the hardware exp2
+  auto decay = [](float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); };
+  auto ld4 = [](const float *p) {
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    return f32x4{t.x, t.y, t.z, t.w};
+  };
+  const int I = 4 - wave;  // block-row of T owned by this wave (4, 3, 2, 1)
+  // K tile I: the B operand of every A_IK (K < I) and both operands of A_II
+  F32 kI[3];
+#pragma unroll
+  for (int kb = 0; kb < 3; ++kb) kI[kb] = kfrag32(16 * I + ln, kb);
+  const F16 kIt = kfrag16(16 * I + ln);
+  // tile with rows from tile Ka of K and the columns held in (b, bt): acc[e] = k_{16Ka+4lg+e} . col_{ln}
+  auto rows_times = [&](int Ka, const F32 *b, const F16 &bt) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * Ka + ln, kb), kfrag32(16 * Kb + ln, kb), acc);
-    return mma(kfrag16(16 * Ka + ln), kfrag16(16 * Kb + ln), acc);
+    for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * Ka + ln, kb), b[kb], acc);
+    return mma(kfrag16(16 * Ka + ln), bt, acc);
   };
-  // A_{r i} with r = 16I + ln (lane row), i = 16K + 4lg + e
-  auto a_scale = [&](const f32x4 &acc, int I, int K, float *out) {
-    const int r = 16 * I + ln;
-    const float fr = sbeta[r] * srk[r];
+  // A_{r i} = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i) for i < r, with r = 16Ir + ln, i = 16K + 4lg + e
+  auto a_scale = [&](const f32x4 &acc, int Ir, int K, float *out) {
+    const int r = 16 * Ir + ln;
+    const float fr = sbeta[r] * srk[r], Gr = sG[r];
+    const f32x4 rk4 = ld4(srk + 16 * K + 4 * lg), G4 = ld4(sG + 16 * K + 4 * lg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * K + 4 * lg + e;
-      out[e] = (i < r) ? fr * srk[i] * expf(sG[r] - sG[i]) * acc[e] : 0.f;
+      out[e] = (i < r) ? fr * rk4[e] * decay(Gr - G4[e]) * acc[e] : 0.f;
     }
   };
-  const int I = 4 - wave;  // block-row of T owned by this wave (4, 3, 2, 1)
-  F16 Ah[4], Al[4];        // A_IK, K < I, as 16-deep A-operand fragments (hi, lo)
+  F16 Ah[4], Al[4];  // A_IK, K < I, as 16-deep A-operand fragments (hi, lo)
 #pragma unroll
   for (int K = 0; K < 4; ++K) {
     Ah[K] = F16{{0, 0}};
     Al[K] = F16{{0, 0}};
     if (K < I) {
       float v[4];
-      a_scale(kk_tile(K, I), I, K, v);
+      a_scale(rows_times(K, kI, kIt), I, K, v);
       uint32_t hi[2], lo[2];
       split4(v, hi, lo);
       Ah[K] = f16_of(hi);
@@ -214,34 +241,38 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     }
   }
   // diagonal blocks A_II (and A_00 by the last wave) -> LDS, row-major
+  {
+    float v[4];
+    a_scale(rows_times(I, kI, kIt), I, I, v);
+    *reinterpret_cast<float4 *>(Ad + I * kBlkF + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+    if (wave == 3) {
+      F32 k0[3];
 #pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    const int Id = d == 0 ? I : 0;
-    if (d == 0 || wave == 3) {
-      float v[4];
-      a_scale(kk_tile(Id, Id), Id, Id, v);
-      *reinterpret_cast<float4 *>(Ad + Id * kBlkF + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int kb = 0; kb < 3; ++kb) k0[kb] = kfrag32(ln, kb);
+      a_scale(rows_times(0, k0, kfrag16(ln)), 0, 0, v);
+      *reinterpret_cast<float4 *>(Ad + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
   // P^T tiles (kk-tile It <= query tile Rt): acc[e] = k_{16It+4lg+e} . q_{16Rt+ln}
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int tix = wave + 4 * s;
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const int tix = wave + 4 * s2;
     if (tix < 15) {
       int Rt = 0;
       while (tri(Rt + 1, 0) <= tix) ++Rt;
       const int It = tix - tri(Rt, 0);
-      f32x4 acc = zero4();
+      F32 qR[3];
 #pragma unroll
-      for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * It + ln, kb), qfrag32(16 * Rt + ln, kb), acc);
-      acc = mma(kfrag16(16 * It + ln), qfrag16(16 * Rt + ln), acc);
+      for (int kb = 0; kb < 3; ++kb) qR[kb] = qfrag32(16 * Rt + ln, kb);
+      const f32x4 acc = rows_times(It, qR, qfrag16(16 * Rt + ln));
       const int r = 16 * Rt + ln;
-      const float fr = srq[r];
+      const float fr = srq[r], Gr = sG[r];
+      const f32x4 rk4 = ld4(srk + 16 * It + 4 * lg), G4 = ld4(sG + 16 * It + 4 * lg);
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * It + 4 * lg + e;
-        v[e] = (i <= r) ? fr * srk[i] * expf(sG[r] - sG[i]) * acc[e] : 0.f;
+        v[e] = (i <= r) ? fr * rk4[e] * decay(Gr - G4[e]) * acc[e] : 0.f;
       }
       *reinterpret_cast<float4 *>(blk(Pb, Rt, It) + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
     }
@@ -279,10 +310,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
   }
   __syncthreads();
   // ---- (3b) off-diagonal blocks, one block-distance per step
-  auto ld4 = [](const float *p) {
-    const float4 t = *reinterpret_cast<const float4 *>(p);
-    return f32x4{t.x, t.y, t.z, t.w};
-  };
 #pragma unroll
   for (int L = 1; L < CT; ++L) {
     const int J = I - L;
@@ -313,46 +340,48 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
     __syncthreads();
   }
 
-  // ---- (4) M^T = T^T diag(s) K  and  P'^T = T^T P^T, split and stored
+  // ---- (4) M^T = T^T diag(s) K  and  P'^T = T^T P^T, split and stored.
+  // Each wave owns whole token-row tiles, so it builds their bf16 hi/lo
+  // A-operand fragments once and sweeps the other dimension:
+  //   M rows Rt (over the 7 d tiles): wave 0: 0, wave 1: 1, wave 2: 2, wave 3: 3 and 4;
+  //   P' rows It (over query tiles Rt >= It): wave 0: 4, wave 1: 2 and 3, wave 2: 1, wave 3: 0.
   // Row r of T^T over columns i = 16p + 4lg .. +3 (p >= r / 16): one 128-bit read.
   auto tt4 = [&](int r, int p) { return ld4(blk(Tt, p, r >> 4) + (r & 15) * kBs + 4 * lg); };
+  auto pair = [](const F16 &a, const F16 &b) { return F32{{a.w[0], a.w[1], b.w[0], b.w[1]}}; };
   char *Mrec = Mout + rec * size_t(kMBytes);
   char *Prec = Pout + rec * size_t(kPBytes);
-  for (int task = wave; task < 50; task += 4) {
-    if (task < 35) {
-      const int Rt = task / NT, Dt = task % NT;
-      const int r = 16 * Rt + ln;
-      f32x4 acc = zero4();
-      int p = Rt;
-      while (p < CT) {
-        if (p + 1 < CT) {  // 32-deep block over token tiles p, p+1
-          const f32x4 t0v = tt4(r, p), t1v = tt4(r, p + 1);
-          const f32x4 s0 = ld4(ss + 16 * p + 4 * lg), s1 = ld4(ss + 16 * p + 16 + 4 * lg);
-          float v[8];
+  auto m_rows = [&](int Rt) {
+    const int r = 16 * Rt + ln;
+    F16 uh[CT], ul[CT];  // (T^T diag(s)) rows r over token tile p, hi/lo
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[j] = t0v[j] * s0[j];
-            v[4 + j] = t1v[j] * s1[j];
+    for (int p = 0; p < CT; ++p) {
+      if (p >= Rt) {
+        const f32x4 t = tt4(r, p), s4 = ld4(ss + 16 * p + 4 * lg);
+        const float v[4] = {t[0] * s4[0], t[1] * s4[1], t[2] * s4[2], t[3] * s4[3]};
+        uint32_t hi[2], lo[2];
+        split4(v, hi, lo);
+        uh[p] = f16_of(hi);
+        ul[p] = f16_of(lo);
+      }
+    }
+#pragma unroll
+    for (int Dt = 0; Dt < NT; ++Dt) {
+      const uint16_t *kt = Kt + (16 * Dt + ln) * kKtRow + 4 * lg;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int p = 0; p < CT; ++p) {
+        if (p >= Rt && !((p - Rt) & 1)) {
+          if (p + 1 < CT) {  // 32-deep block over token tiles p, p + 1
+            const uint2 k0 = *reinterpret_cast<const uint2 *>(kt + 16 * p), k1 = *reinterpret_cast<const uint2 *>(kt + 16 * p + 16);
+            const F32 bk{{k0.x, k0.y, k1.x, k1.y}};
+            acc = mma(pair(uh[p], uh[p + 1]), bk, acc);
+            acc = mma(pair(ul[p], ul[p + 1]), bk, acc);
+          } else {  // 16-deep block over tile p
+            const uint2 k0 = *reinterpret_cast<const uint2 *>(kt + 16 * p);
+            const F16 bk{{k0.x, k0.y}};
+            acc = mma(uh[p], bk, acc);
+            acc = mma(ul[p], bk, acc);
           }
-          F32 ah, al;
-          split4(v, ah.w, al.w);
-          split4(v + 4, ah.w + 2, al.w + 2);
-          const uint16_t *kt = Kt + (16 * Dt + ln) * kKtRow + 16 * p + 4 * lg;
-          const uint2 k0 = *reinterpret_cast<const uint2 *>(kt), k1 = *reinterpret_cast<const uint2 *>(kt + 16);
-          const F32 bk{{k0.x, k0.y, k1.x, k1.y}};
-          acc = mma(ah, bk, acc);
-          acc = mma(al, bk, acc);
-          p += 2;
-        } else {  // 16-deep block over tile p
-          const f32x4 t0v = tt4(r, p), s0 = ld4(ss + 16 * p + 4 * lg);
-          const float v[4] = {t0v[0] * s0[0], t0v[1] * s0[1], t0v[2] * s0[2], t0v[3] * s0[3]};
-          uint32_t hi[2], lo[2];
-          split4(v, hi, lo);
-          const uint2 k0 = *reinterpret_cast<const uint2 *>(Kt + (16 * Dt + ln) * kKtRow + 16 * p + 4 * lg);
-          const F16 bk{{k0.x, k0.y}};
-          acc = mma(f16_of(hi), bk, acc);
-          acc = mma(f16_of(lo), bk, acc);
-          p += 1;
         }
       }
       // accumulator: column d = 16Dt + ln, rows r = 16Rt + 4lg + e -> M[d][r], the state pass's A-operand order
@@ -366,35 +395,43 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
         *reinterpret_cast<uint2 *>(Mrec + m_off16(Dt, 0) + lane * 8) = make_uint2(hi[0], hi[1]);
         *reinterpret_cast<uint2 *>(Mrec + m_off16(Dt, 1) + lane * 8) = make_uint2(lo[0], lo[1]);
       }
-    } else {
-      int tix = task - 35, Rt = 0;
-      while (tri(Rt + 1, 0) <= tix) ++Rt;
-      const int It = tix - tri(Rt, 0);
-      // P'^T[i][r] = sum_{kk=i}^{r} T[kk][i] P[r][kk]; A rows i = 16It + ln, B columns r = 16Rt + ln
-      const int i = 16 * It + ln;
+    }
+  };
+  // P'^T[i][r] = sum_{kk=i}^{r} T^T[i][kk] P^T[kk][r]: A rows i = 16It + ln, B columns r = 16Rt + ln
+  auto p_rows = [&](int It) {
+    const int i = 16 * It + ln;
+    F16 th[CT], tl[CT];
+#pragma unroll
+    for (int p = 0; p < CT; ++p) {
+      if (p >= It) {
+        uint32_t hi[2], lo[2];
+        split4(tt4(i, p), hi, lo);
+        th[p] = f16_of(hi);
+        tl[p] = f16_of(lo);
+      }
+    }
+#pragma unroll
+    for (int Rt = 0; Rt < CT; ++Rt) {
+      if (Rt < It) continue;
       f32x4 acc = zero4();
-      int p = It;
-      while (p <= Rt) {
-        if (p + 1 <= Rt) {
-          const f32x4 a0 = tt4(i, p), a1 = tt4(i, p + 1);
-          const f32x4 b0 = ld4(blk(Pb, Rt, p) + ln * kBs + 4 * lg), b1 = ld4(blk(Pb, Rt, p + 1) + ln * kBs + 4 * lg);
-          F32 ah, al, bh, bl;
-          split4(a0, ah.w, al.w);
-          split4(a1, ah.w + 2, al.w + 2);
-          split4(b0, bh.w, bl.w);
-          split4(b1, bh.w + 2, bl.w + 2);
-          acc = mma(ah, bh, acc);
-          acc = mma(ah, bl, acc);
-          acc = mma(al, bh, acc);
-          p += 2;
-        } else {
-          uint32_t ah[2], al[2], bh[2], bl[2];
-          split4(tt4(i, p), ah, al);
-          split4(ld4(blk(Pb, Rt, p) + ln * kBs + 4 * lg), bh, bl);
-          acc = mma(f16_of(ah), f16_of(bh), acc);
-          acc = mma(f16_of(ah), f16_of(bl), acc);
-          acc = mma(f16_of(al), f16_of(bh), acc);
-          p += 1;
+#pragma unroll
+      for (int p = 0; p < CT; ++p) {
+        if (p >= It && p <= Rt && !((p - It) & 1)) {
+          if (p + 1 <= Rt) {
+            F32 bh, bl;
+            split4(ld4(blk(Pb, Rt, p) + ln * kBs + 4 * lg), bh.w, bl.w);
+            split4(ld4(blk(Pb, Rt, p + 1) + ln * kBs + 4 * lg), bh.w + 2, bl.w + 2);
+            const F32 ah = pair(th[p], th[p + 1]), al = pair(tl[p], tl[p + 1]);
+            acc = mma(ah, bh, acc);
+            acc = mma(ah, bl, acc);
+            acc = mma(al, bh, acc);
+          } else {
+            uint32_t bh[2], bl[2];
+            split4(ld4(blk(Pb, Rt, p) + ln * kBs + 4 * lg), bh, bl);
+            acc = mma(th[p], f16_of(bh), acc);
+            acc = mma(th[p], f16_of(bl), acc);
+            acc = mma(tl[p], f16_of(bh), acc);
+          }
         }
       }
       // accumulator: column r = 16Rt + ln, rows i = 16It + 4lg + e -> P'[r][i], the state pass's A-operand order
@@ -409,6 +446,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
         *reinterpret_cast<uint2 *>(Prec + p_off32(Rt, kb, 1) + lane * 16 + half * 8) = make_uint2(lo[0], lo[1]);
       }
     }
+  };
+  switch (wave) {
+    case 0: m_rows(0); p_rows(4); break;
+    case 1: m_rows(1); p_rows(2); p_rows(3); break;
+    case 2: m_rows(2); p_rows(1); break;
+    default: m_rows(3); m_rows(4); p_rows(0); break;
   }
 }
 
