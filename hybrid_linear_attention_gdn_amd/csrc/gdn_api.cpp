@@ -33,24 +33,24 @@ Profiler &profiler() {
 
 namespace gdn {
 
-void stage_begin(const Args &a, Stage s) {
+void stage_begin(const Args &a, Stage s, hipStream_t stream) {
   if (!a.profile) return;
   hipEvent_t e;
   if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, a.stream);
+  hipEventRecord(e, stream ? stream : a.stream);
   Profiler &P = profiler();
   std::lock_guard<std::mutex> lk(P.mu);
   P.open[s].push_back(e);
 }
 
-void stage_end(const Args &a, Stage s) {
+void stage_end(const Args &a, Stage s, hipStream_t stream) {
   if (!a.profile) return;
   Profiler &P = profiler();
   std::lock_guard<std::mutex> lk(P.mu);
   if (P.open[s].empty()) return;
   hipEvent_t e;
   if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, a.stream);
+  hipEventRecord(e, stream ? stream : a.stream);
   P.done[s].emplace_back(P.open[s].back(), e);
   P.open[s].pop_back();
 }
@@ -130,6 +130,7 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
     P.off_M = take(chunks * gdn::mfma_chunk_bytes_M());
     P.off_P = take(chunks * gdn::mfma_chunk_bytes_P());
     P.off_cs = take(chunks * gdn::mfma_chunk_bytes_cs());
+    P.off_Sseg = take(units * size_t(P.dv) * P.dk * sizeof(float));
   } else {
     P.off_beta = take(sz);
     P.off_rq = take(sz);

@@ -18,6 +18,10 @@
 // chunks ahead: every such load is a contiguous 1 KB per instruction.
 #include "gdn_mfma_common.h"
 
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
 namespace gdn {
 namespace mfma {
 namespace {
@@ -85,7 +89,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
                                            const uint16_t *__restrict__ v, const char *__restrict__ Mws,
                                            const char *__restrict__ Pws, const float *__restrict__ CS,
                                            const float *state_in, float *state_out, void *__restrict__ o, int T,
-                                           int H, int N, int b, int h, int nt, char *lds) {
+                                           int H, int N, int cb, int ce, int b, int h, int nt, char *lds) {
   constexpr Roles ro = kRoles[W];
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
   const size_t u = size_t(b) * H + h;
@@ -201,7 +205,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
     }
   }
   auto l2_touch = [&](int c) -> uint32_t {
-    const int cp = min(c + kAhead, N - 1);
+    const int cp = min(c + kAhead, ce - 1);
     // a row past the end of the last chunk touches the chunk's last row instead
     const int rr = pe_row < 0 ? 0 : min(pe_row, T - 1 - cp * C);
     const char *a = pe_base + size_t(cp) * pe_stride + size_t(rr) * row_bytes;
@@ -346,7 +350,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
     // ---- phase B: R operands; state update and outputs.  The operand
     // fragments of chunk c + 2 are requested here (past the end, the last
     // chunk is fetched again: the same instructions issue on every chunk).
-    load_ops(ahead, min(c + 2, N - 1));
+    load_ops(ahead, min(c + 2, ce - 1));
     F32 Rh[2], Rl[2];
     F16 Rth, Rtl;
 #pragma unroll
@@ -426,7 +430,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
     // K/Q/V rows two chunks ahead go into the register set freed by the last
     // store; the set loaded one step ago (chunk c + 1) goes to staging buffer
     // (c + 1) & 1, last read in chunk c - 1, before this chunk's first barrier.
-    stage_issue(st_issue, min(c + 2, N - 1));
+    stage_issue(st_issue, min(c + 2, ce - 1));
     stage_store(st_store, buf ^ 1);
   };
 
@@ -434,24 +438,24 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
   // index mod 3 (chunk c + 1 landed, c + 2 in flight, c being consumed).
   ChunkOps op0, op1, op2;
   Staged st0, st1, st2;
-  stage_issue(st0, 0);
-  load_ops(op0, 0);
-  stage_store(st0, 0);
-  stage_issue(st1, min(1, N - 1));
-  load_ops(op1, min(1, N - 1));
+  stage_issue(st0, cb);
+  load_ops(op0, cb);
+  stage_store(st0, cb & 1);
+  stage_issue(st1, min(cb + 1, ce - 1));
+  load_ops(op1, min(cb + 1, ce - 1));
   uint32_t pf = 0, sink = 0;
   auto touch = [&](int c) {
     sink ^= pf;  // consumed a step after its load was issued
     pf = l2_touch(c);
   };
-  for (int c = 0; c < N; c += 3) {
+  for (int c = cb; c < ce; c += 3) {
     step(c, op0, op2, st2, st1);
     touch(c);
-    if (c + 1 < N) {
+    if (c + 1 < ce) {
       step(c + 1, op1, op0, st0, st2);
       touch(c + 1);
     }
-    if (c + 2 < N) {
+    if (c + 2 < ce) {
       step(c + 2, op2, op1, st1, st0);
       touch(c + 2);
     }
@@ -472,7 +476,8 @@ __global__ __launch_bounds__(256) void chain_kernel(const uint16_t *__restrict__
                                                     const uint16_t *__restrict__ v, const char *__restrict__ Mws,
                                                     const char *__restrict__ Pws, const float *__restrict__ CS,
                                                     const float *state_in, float *state_out,
-                                                    void *__restrict__ o, int T, int H, int N, int units) {
+                                                    void *__restrict__ o, int T, int H, int N, int cb, int ce,
+                                                    int units) {
   extern __shared__ __align__(16) char lds[];
   // Workgroup i runs on XCD i % 8: keep the 7 column tiles of a (b, h) on one
   // XCD so that its K, Q, M and P' are fetched from HBM once into that L2.
@@ -482,10 +487,10 @@ __global__ __launch_bounds__(256) void chain_kernel(const uint16_t *__restrict__
   const int b = u / H, h = u % H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wave) {
-    case 0: chain_role<0, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
-    case 1: chain_role<1, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
-    case 2: chain_role<2, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
-    default: chain_role<3, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, b, h, nt, lds); break;
+    case 0: chain_role<0, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 1: chain_role<1, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 2: chain_role<2, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
+    default: chain_role<3, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
   }
 }
 
@@ -496,31 +501,124 @@ size_t mfma_chunk_bytes_M() { return mfma::kMBytes; }
 size_t mfma_chunk_bytes_P() { return mfma::kPBytes; }
 size_t mfma_chunk_bytes_cs() { return mfma::kCsFloats * sizeof(float); }
 
+namespace {
+
+// A second stream per device on which the intra kernel of later chunk ranges
+// runs while the state pass works through earlier ones, plus the events that
+// order them.  Used when the state pass has more workgroups (7 per (b, h))
+// than the device has CUs: it then runs in more than one round of workgroups,
+// and the intra kernel fills the CUs its last round leaves free.  (With one
+// round, intra workgroups that start first take CUs the state pass is waiting
+// for, and the two kernels only slow each other down.)
+struct SideResources {
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ev;
+  int cus = -1;
+};
+std::mutex g_side_mu;
+SideResources g_side[64];
+
+// Chunk ranges: a short first range (the intra kernel runs alone on it), then
+// ranges growing by 30% each, so that the intra kernel of range s + 1 (on the
+// CUs the state pass leaves free) finishes while the state pass works on range s.
+void segment_bounds(int N, std::vector<int> &bounds) {
+  bounds.assign(1, 0);
+  int len = 16;
+  while (bounds.back() < N) {
+    bounds.push_back(std::min(N, bounds.back() + len));
+    len = len + (len * 3 + 9) / 10;
+  }
+}
+constexpr int kSegmentMinChunks = 64;
+
+hipError_t launch_chain(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb, int ce,
+                        const float *sin, float *sout, hipStream_t st) {
+  const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
+                 *v = static_cast<const uint16_t *>(a.v);
+  const int units = p.B * p.H;
+  const unsigned grid = 8u * mfma::NT * unsigned((units + 7) / 8);
+  if (p.o_bf16)
+    mfma::chain_kernel<true><<<dim3(grid), dim3(256), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
+                                                                           p.H, p.N, cb, ce, units);
+  else
+    mfma::chain_kernel<false><<<dim3(grid), dim3(256), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
+                                                                            p.H, p.N, cb, ce, units);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_mfma(const Plan &p, const Args &a) {
   char *M = a.ws + p.off_M;
   char *P = a.ws + p.off_P;
   float *cs = reinterpret_cast<float *>(a.ws + p.off_cs);
-  hipError_t e = mfma::launch_intra(p, a, M, P, cs);
-  if (e != hipSuccess) return e;
+  float *seg_state = reinterpret_cast<float *>(a.ws + p.off_Sseg);
   static const hipError_t lds0 = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma::chain_kernel<false>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, mfma::kLdsChain);
   static const hipError_t lds1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma::chain_kernel<true>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, mfma::kLdsChain);
   if (lds0 != hipSuccess) return lds0;
   if (lds1 != hipSuccess) return lds1;
-  const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
-                 *v = static_cast<const uint16_t *>(a.v);
-  const int units = p.B * p.H;
-  const unsigned grid = 8u * mfma::NT * unsigned((units + 7) / 8);
+  hipError_t e;
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    if (g_side[dev].cus < 0 &&
+        hipDeviceGetAttribute(&g_side[dev].cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      g_side[dev].cus = 0;
+    cus = g_side[dev].cus;
+  }
+  const long chain_blocks = long(p.B) * p.H * mfma::NT;
+  if (p.N < kSegmentMinChunks || chain_blocks <= cus) {
+    stage_begin(a, kStageIntra);
+    e = mfma::launch_intra(p, a, M, P, cs, 0, p.N, a.stream);
+    stage_end(a, kStageIntra);
+    if (e != hipSuccess) return e;
+    stage_begin(a, kStageState);
+    e = launch_chain(p, a, M, P, cs, 0, p.N, a.state_in, a.state_out, a.stream);
+    stage_end(a, kStageState);
+    return e;
+  }
+  std::vector<int> bounds;
+  segment_bounds(p.N, bounds);
+  const int segs = int(bounds.size()) - 1;
+  // one caller at a time per device enqueues on the shared side stream and events
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideResources &R = g_side[dev];
+  if (!R.side && (e = hipStreamCreateWithFlags(&R.side, hipStreamNonBlocking)) != hipSuccess) {
+    R.side = nullptr;
+    return e;
+  }
+  while (int(R.ev.size()) < segs + 1) {
+    hipEvent_t ev;
+    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
+    R.ev.push_back(ev);
+  }
+  // fork: the side stream starts after the caller's earlier work (the inputs)
+  if ((e = hipEventRecord(R.ev[segs], a.stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(R.side, R.ev[segs], 0)) != hipSuccess) return e;
+  stage_begin(a, kStageIntra, R.side);
+  for (int s = 0; s < segs; ++s) {
+    if ((e = mfma::launch_intra(p, a, M, P, cs, bounds[s], bounds[s + 1], R.side)) != hipSuccess) return e;
+    if ((e = hipEventRecord(R.ev[s], R.side)) != hipSuccess) return e;
+  }
+  stage_end(a, kStageIntra, R.side);
+  // the state pass: range s after the intra kernel of range s; the state is
+  // carried between ranges in the workspace (each workgroup reads and writes
+  // only its own slice, so in place is safe).  The last wait joins the side
+  // stream back into the caller's stream.
   stage_begin(a, kStageState);
-  if (p.o_bf16)
-    mfma::chain_kernel<true><<<dim3(grid), dim3(256), mfma::kLdsChain, a.stream>>>(
-        q, k, v, M, P, cs, a.state_in, a.state_out, a.o, p.T, p.H, p.N, units);
-  else
-    mfma::chain_kernel<false><<<dim3(grid), dim3(256), mfma::kLdsChain, a.stream>>>(
-        q, k, v, M, P, cs, a.state_in, a.state_out, a.o, p.T, p.H, p.N, units);
+  for (int s = 0; s < segs; ++s) {
+    if ((e = hipStreamWaitEvent(a.stream, R.ev[s], 0)) != hipSuccess) return e;
+    const float *sin = s == 0 ? a.state_in : seg_state;
+    float *sout = s == segs - 1 ? a.state_out : seg_state;
+    if ((e = launch_chain(p, a, M, P, cs, bounds[s], bounds[s + 1], sin, sout, a.stream)) != hipSuccess) return e;
+  }
   stage_end(a, kStageState);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace gdn

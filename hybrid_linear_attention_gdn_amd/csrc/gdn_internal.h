@@ -28,6 +28,7 @@ struct Plan {
   size_t off_beta = 0, off_rq = 0, off_rk = 0, off_gcum = 0;       // fp32 [B,H,T]
   size_t off_W = 0, off_Ut = 0, off_U = 0, off_S0 = 0;              // portable path
   size_t off_M = 0, off_P = 0, off_cs = 0;                           // MFMA path
+  size_t off_Sseg = 0;  // MFMA path: fp32 [B, H, d_v, d_k] state carried between chunk ranges
   size_t total = 0;
 };
 
@@ -43,8 +44,9 @@ struct Args {
 
 // Timing stages (see gdn_profile_begin in include/sanawm_gdn.h).
 enum Stage : int { kStagePrep = 0, kStageIntra = 1, kStageState = 2, kStageOutput = 3, kNumStages = 4 };
-void stage_begin(const Args &a, Stage s);
-void stage_end(const Args &a, Stage s);
+// timing events around a stage, on `stream` (default: the call's stream)
+void stage_begin(const Args &a, Stage s, hipStream_t stream = nullptr);
+void stage_end(const Args &a, Stage s, hipStream_t stream = nullptr);
 
 // Kernel launch sequences (each returns the first launch error, if any).
 hipError_t launch_prep(const Plan &p, const Args &a);

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
                                                        const float *__restrict__ g, const float *__restrict__ beta,
                                                        char *__restrict__ Mout, char *__restrict__ Pout,
                                                        float *__restrict__ CSout, int T, int H, int N,
-                                                       uint32_t flags) {
+                                                       int c_first, int n_chunks, uint32_t flags) {
   extern __shared__ __align__(16) char lds[];
   uint16_t *Kr = reinterpret_cast<uint16_t *>(lds + kLdsKr);
   uint16_t *Kt = reinterpret_cast<uint16_t *>(lds + kLdsKt);
@@ -65,12 +65,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
   float *sbeta = sc, *srq = sc + 80, *srk = sc + 160, *sG = sc + 240, *ss = sc + 320;
   auto blk = [](float *base, int I, int J) { return base + tri(I, J) * kBlkF; };
 
-  // block -> (b, c, h) with h fastest: neighbouring workgroups read neighbouring rows
+  // block -> (b, c, h) over chunks c_first .. c_first + n_chunks - 1, h fastest:
+  // neighbouring workgroups read neighbouring rows
   int x = blockIdx.x;
   const int h = x % H;
   x /= H;
-  const int c = x % N;
-  const int b = x / N;
+  const int c = c_first + x % n_chunks;
+  const int b = x / n_chunks;
   const int t0 = c * C;
   const int n = min(C, T - t0);
   const size_t u = size_t(b) * H + h;
@@ -457,17 +458,18 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
 
 }  // namespace
 
-hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs) {
+hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs, int c_first, int c_end,
+                        hipStream_t stream) {
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k);
-  const unsigned chunks = unsigned(p.B) * p.H * p.N;
+  const int n_chunks = c_end - c_first;
+  const unsigned blocks = unsigned(p.B) * p.H * unsigned(n_chunks);
   // more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU)
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsIntra);
   if (lds_ok != hipSuccess) return lds_ok;
-  stage_begin(a, kStageIntra);
-  intra_kernel<<<dim3(chunks), dim3(256), kLdsIntra, a.stream>>>(q, k, a.g, a.beta, M, P, cs, p.T, p.H, p.N,
-                                                                 p.flags);
-  stage_end(a, kStageIntra);
+  if (n_chunks <= 0) return hipSuccess;
+  intra_kernel<<<dim3(blocks), dim3(256), kLdsIntra, stream>>>(q, k, a.g, a.beta, M, P, cs, p.T, p.H, p.N, c_first,
+                                                              n_chunks, p.flags);
   return hipGetLastError();
 }
 

@@ -113,8 +113,10 @@ __device__ __forceinline__ int p_off16(int R, int hl) { return p_base(R) + (R / 
 // lower-triangular 16x16 block index (I >= J)
 __device__ __forceinline__ constexpr int tri(int I, int J) { return I * (I + 1) / 2 + J; }
 
-// Launches the intra kernel writing M, P' and the chunk scales (gdn_intra.hip).
-hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs);
+// Launches the intra kernel writing M, P' and the chunk scales of chunks
+// c_first .. c_end - 1 of every (b, h) on `stream` (gdn_intra.hip).
+hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs, int c_first, int c_end,
+                        hipStream_t stream);
 
 }  // namespace mfma
 }  // namespace gdn
