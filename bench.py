@@ -8,6 +8,10 @@ roofline (HIP events recorded by the library around each kernel, inside the
 timed region), and the fp64 CPU oracle timed on this host as a baseline.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload clip_241f]
+
+`roofline.traffic` is the dominant kernel's measured HBM bytes per launch from
+profiles/traffic_<kernel>_<workload>.json, reported only while the hash of the
+kernel's sources stored there matches the sources of this tree.
 """
 from __future__ import annotations
 
@@ -51,19 +55,24 @@ def flops_per_token_head(C: int = 80, d: int = 112) -> float:
     return 6 * d * d + 5 * C * d + C * C / 3
 
 
-def cpu_baseline(w, max_tokens: int):
-    """fp64 oracle on a bounded sample of the same workload: all heads, the first tokens."""
+def cpu_baseline(w, max_tokens: int, min_seconds: float):
+    """fp64 oracle on a bounded sample of the same workload: all heads, the first
+    `max_tokens` tokens, repeated until `min_seconds` of wall time have passed."""
     from hybrid_linear_attention_gdn_amd.inputs import make_inputs
     from oracle.recurrence import default_threads, gdn_recurrence
     T = min(w.seq_len, max_tokens)
     inp = make_inputs(w, seq_len=T, frame_tokens=w.frame_tokens)
     threads = min(default_threads(w.batch * w.heads), 16)
-    t0 = time.perf_counter()
-    gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, nthreads=threads, want_state=True)
-    dt = time.perf_counter() - t0
-    return {"value": w.batch * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: all {w.batch}x{w.heads} (batch, head) units, first {T} of {w.seq_len} tokens "
-                      f"({w.batch * T * w.heads} token-heads, {dt:.2f} s wall, fp64 C recurrence)",
+    runs, dt = 0, 0.0
+    while runs == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, nthreads=threads, want_state=True)
+        dt += time.perf_counter() - t0
+        runs += 1
+    return {"value": runs * w.batch * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: all {w.batch}x{w.heads} (batch, head) units, first {T} of {w.seq_len} tokens, "
+                      f"{runs} passes ({runs * w.batch * T * w.heads} token-heads, {dt:.1f} s wall, "
+                      f"fp64 C recurrence)",
             "seconds": round(dt, 3)}
 
 
@@ -75,8 +84,12 @@ def main():
     ap.add_argument("--workload", default="clip_241f")
     ap.add_argument("--o-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--portable", action="store_true", help="time the fp32 vector-ALU kernels instead")
-    ap.add_argument("--cpu-tokens", type=int, default=13200, help="tokens of the oracle's CPU sample")
+    ap.add_argument("--cpu-tokens", type=int, default=1 << 30, help="tokens of the oracle's CPU sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, one plain device-to-device copy of this many MiB (a kernel of "
+                         "known traffic, to calibrate memory counters under a profiler)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -90,6 +103,7 @@ def main():
 
     from hybrid_linear_attention_gdn_amd import gdn
     from hybrid_linear_attention_gdn_amd.inputs import WORKLOADS, make_inputs
+    from hybrid_linear_attention_gdn_amd.rocprof_summary import kernel_source_hash
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -158,13 +172,27 @@ def main():
     path_gbs = path_bytes / (ms * 1e-3) / 1e9
     tflops = flops_per_token_head() * token_heads / (ms * 1e-3) / 1e12
 
+    # measured HBM bytes per launch of the dominant kernel (rocprofv3 FETCH_SIZE and
+    # WRITE_SIZE, calibrated on a plain copy), valid only for the sources they were taken on
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
     if os.path.exists(tpath):
         try:
-            traffic = json.load(open(tpath)).get("bytes_per_launch")
+            rec = json.load(open(tpath))
+            if rec.get("source_hash") == kernel_source_hash(dom, mfma) and rec.get("o_dtype") == args.o_dtype:
+                traffic = rec.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
+
+    if args.copy_mib > 0:
+        # an elementwise kernel (not a DMA copy, which the counters would not see):
+        # reads and writes exactly copy_mib MiB
+        src = torch.ones((args.copy_mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": "GDN fwd tokens/s per layer (20h×112d, bf16) + % MFMA peak on 1 MI355X",
@@ -191,7 +219,7 @@ def main():
         "gdn_per_dit_forward_ms": {"x20_layers": round(20 * ms, 3), "x15_gdn_layers": round(15 * ms, 3)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

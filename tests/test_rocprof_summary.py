@@ -1,0 +1,54 @@
+"""Host logic of the profiling summaries: kernel-name shortening, counter
+calibration against the copy of known size, and the source hash that gates the
+stored traffic figure in bench.py."""
+import csv
+import json
+import os
+
+from hybrid_linear_attention_gdn_amd import rocprof_summary as rs
+
+HDR = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size", "Kernel_Id",
+       "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count",
+       "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+CHAIN = "void gdn::mfma::(anonymous namespace)::chain_kernel<false>(unsigned short const*, float const*, int)"
+NEG = ("void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)"
+       "::{lambda()#2}, std::array<char*, 2ul> >(int, at::native::neg_kernel_cuda)")
+
+
+def test_short_name():
+    assert rs.short_name(CHAIN) == "chain_kernel<false>"
+    assert rs.short_name("gdn::mfma::(anonymous namespace)::intra_kernel(unsigned short const*)") == "intra_kernel"
+    assert rs.short_name(NEG).startswith("vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda")
+
+
+def _counters(path, counter, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(HDR)
+        for i, (name, value) in enumerate(rows):
+            w.writerow([i, i + 1, "Agent 1", 1, 1, 1, 64, 1, name, 256, 0, 0, 8, 0, 8, counter, value, 0, 1])
+
+
+def test_traffic_calibration(tmp_path):
+    # the copy of 4 MiB reads as half its size on FETCH_SIZE (2x factor) and exactly on WRITE_SIZE
+    _counters(str(tmp_path / "f"), "FETCH_SIZE", [(CHAIN, 100.0), (CHAIN, 300.0), (NEG, 2048.0)])
+    _counters(str(tmp_path / "w"), "WRITE_SIZE", [(CHAIN, 50.0), (CHAIN, 50.0), (NEG, 4096.0)])
+    out_json, out_md = str(tmp_path / "t.json"), str(tmp_path / "t.md")
+    rs.main(["traffic", "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"), "--copy-mib", "4",
+             "--kernel", "chain_kernel", "--stage", "state", "--workload", "w", "--fetch-command", "cf",
+             "--write-command", "cw", "--json", out_json, "--md", out_md])
+    rec = json.load(open(out_json))
+    assert rec["calibration"]["fetch_factor"] == 2.0 and rec["calibration"]["write_factor"] == 1.0
+    assert rec["fetch_bytes_per_launch"] == 200 * 1024 * 2       # mean 200 KiB, doubled
+    assert rec["write_bytes_per_launch"] == 50 * 1024
+    assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    assert rec["source_hash"] == rs.kernel_source_hash("state", True)
+    assert "cf" in open(out_md).read()
+
+
+def test_source_hash_tracks_the_kernel_files():
+    a = rs.kernel_source_hash("state", True)
+    b = rs.kernel_source_hash("intra", True)
+    assert a != b and len(a) == 16
+    assert rs.kernel_source_hash("state", True) == a
