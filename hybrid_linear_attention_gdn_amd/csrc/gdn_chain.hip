@@ -13,8 +13,9 @@
 // is 14 such pieces) into a register set, and written to one of two LDS
 // staging buffers a step later; each wave then reads its
 // fragments from LDS (rows padded to 232 bytes so the 8-byte fragment reads
-// of 16 consecutive rows fall in distinct banks).  The fragment-ordered M and
-// P' records and the per-token scales are read straight into registers, two
+// of 16 consecutive rows fall in distinct banks).  The chunk's 1 KB record of
+// per-token scales is staged with the rows (one load by wave 0).  The
+// fragment-ordered M and P' records are read straight into registers, two
 // chunks ahead: every such load is a contiguous 1 KB per instruction.
 #include "gdn_mfma_common.h"
 
@@ -62,21 +63,19 @@ constexpr int kLdsStage = kLdsR + 2 * (2 * 1024 + 512);  // two K/Q/V^T buffers
 constexpr int kStageK = 0;
 constexpr int kStageQ = C * kRowPad * 2;                 // 18,560
 constexpr int kStageV = 2 * C * kRowPad * 2;             // 37,120
-constexpr int kStageBytes = kStageV + 16 * kVtPad * 2;   // 39,808
-constexpr int kLdsChain = kLdsStage + 2 * kStageBytes;   // 91,904
+constexpr int kStageCs = kStageV + 16 * kVtPad * 2;     // 39,808: the chunk's 256 scale floats
+constexpr int kStageBytes = kStageCs + kCsFloats * 4;    // 40,832
+constexpr int kLdsChain = kLdsStage + 2 * kStageBytes;   // 93,952
 static_assert(kStageBytes % 16 == 0, "stage buffers stay 16-byte aligned");
 
 // Everything one wave reads from global memory for one chunk, besides the
 // staged rows: independent of the state, so the next chunk's set is in flight
 // while the current one is consumed.
 struct ChunkOps {
-  float Aa[2][4], Bb[2][4];  // beta, beta*gamma*rk for the rows of the Y tiles
-  float Cc[2][4];            // gamma*rq for the rows of the output tiles
   F32 Mf[3][2][2];           // M fragments of the owned state tiles [tile][block][hi/lo]
   F16 Mt[3][2];
   F32 Pf[2][2][2];           // P' fragments of the output tiles
   F16 Pt[2][2];
-  float gC;                  // gamma at the chunk's last token
 };
 
 struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k = d_k)
@@ -124,7 +123,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
   const uint32_t offV = tid < 2 * C ? uint32_t(tid >> 1) * row_bytes + uint32_t(h) * (D * 2) + 32u * nt + 16u * (tid & 1)
                                     : kOutOfRange;
   struct Staged {
-    uint4 k[CT], q[CT], v;
+    uint4 k[CT], q[CT], v, cs;  // cs: wave 0 only
   };
   auto stage_issue = [&](Staged &st, int c) {
     const int t0 = c * C, nv = min(C, T - t0);
@@ -138,6 +137,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       st.q[i] = buf_load16(rq_, off);
     }
     st.v = buf_load16(rv_, offV);
+    if (W == 0) st.cs = ldg16(CS + (u * N + c) * kCsFloats + 4 * lane);  // the chunk's scales: one 1 KB load
   };
   auto stage_store = [&](const Staged &st, int buf) {
     char *sb = lds + kLdsStage + buf * kStageBytes;
@@ -160,6 +160,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
 #pragma unroll
       for (int j = 0; j < 8; ++j) vt[(8 * half + j) * kVtPad + vr] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
     }
+    if (W == 0) *reinterpret_cast<uint4 *>(sb + kStageCs + 16 * lane) = st.cs;
   };
   // A-operand fragments of a 16-row tile of the staged K (m = 0) or Q (m = 1), "pair" k-order
   auto rows_frag = [&](int buf, int m, int tile) {
@@ -213,20 +214,8 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
   };
 
   auto load_ops = [&](ChunkOps &op, int c) {
-    const float *cs = CS + (u * N + c) * kCsFloats;
     const char *Mr = Mws + (u * N + c) * size_t(kMBytes);
     const char *Pr = Pws + (u * N + c) * size_t(kPBytes);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < ro.nY) {
-        const int tile = ro.Y[s];
-        const float4 a4 = *reinterpret_cast<const float4 *>(cs + 16 * tile + 4 * lg);
-        const float4 b4 = *reinterpret_cast<const float4 *>(cs + 80 + 16 * tile + 4 * lg);
-        op.Aa[s][0] = a4.x, op.Aa[s][1] = a4.y, op.Aa[s][2] = a4.z, op.Aa[s][3] = a4.w;
-        op.Bb[s][0] = b4.x, op.Bb[s][1] = b4.y, op.Bb[s][2] = b4.z, op.Bb[s][3] = b4.w;
-      }
-    }
-    op.gC = cs[240];
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       if (s < ro.nS) {
@@ -264,8 +253,6 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
             const uint2 x = ldg8(Pr + p_off16(R, hl) + lane * 8);
             op.Pt[s][hl] = F16{{x.x, x.y}};
           }
-        const float4 c4 = *reinterpret_cast<const float4 *>(cs + 160 + 16 * R + 4 * lg);
-        op.Cc[s][0] = c4.x, op.Cc[s][1] = c4.y, op.Cc[s][2] = c4.z, op.Cc[s][3] = c4.w;
       }
     }
   };
@@ -321,6 +308,11 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       return acc;
     };
     const uint16_t *vt = reinterpret_cast<const uint16_t *>(lds + kLdsStage + buf * kStageBytes + kStageV);
+    const float *csl = reinterpret_cast<const float *>(lds + kLdsStage + buf * kStageBytes + kStageCs);
+    auto ldf4 = [](const float *p) {
+      const float4 t = *reinterpret_cast<const float4 *>(p);
+      return f32x4{t.x, t.y, t.z, t.w};
+    };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < ro.nY) {
@@ -330,8 +322,9 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
         const float va[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
                              __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
         float r4[4];
+        const f32x4 aa = ldf4(csl + 16 * tile + 4 * lg), bb = ldf4(csl + 80 + 16 * tile + 4 * lg);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] = cur.Aa[s][e] * va[e] - cur.Bb[s][e] * y[e];
+        for (int e = 0; e < 4; ++e) r4[e] = aa[e] * va[e] - bb[e] * y[e];
         uint32_t hi[2], lo[2];
         split4(r4, hi, lo);
         if (tile < 4) {
@@ -372,7 +365,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       if (s < ro.nS) {
-        f32x4 acc = S[s] * cur.gC;
+        f32x4 acc = S[s] * csl[240];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           acc = mma(cur.Mf[s][kb][0], Rh[kb], acc);
@@ -390,8 +383,9 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       if (s < ro.nO) {
         const int R = ro.O[s];
         f32x4 acc;
+        const f32x4 cc = ldf4(csl + 160 + 16 * R + 4 * lg);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = cur.Cc[s][e] * QS[s][e];
+        for (int e = 0; e < 4; ++e) acc[e] = cc[e] * QS[s][e];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb < (R + 1) / 2) {

@@ -126,6 +126,28 @@ def test_minute_cfg_sampled_heads():
     assert np.isfinite(o).all()
 
 
+def test_chunk_ranges_on_two_streams_equal_one_launch():
+    """B = 2 x 20 heads needs 280 state-pass workgroups, more than the 256 CUs:
+    the library then runs the state pass in chunk ranges, overlapped with the
+    intra kernel on a second stream, carrying the state through the workspace.
+    With batch 1 a copy of batch 0, batch 0 must equal the single-launch B = 1
+    result bit for bit (a ragged 5,063-token sequence with an initial state)."""
+    w = WORKLOADS["clip_241f"]
+    inp = make_inputs(w, seq_len=5063)
+    inp.state0 = (0.02 * np.random.default_rng(7).standard_normal((1, 20, 112, 112))).astype(np.float32)
+    q, k, v, g, beta, s0 = to_device(inp)
+    _say("case two streams: B=2 (chunk ranges) vs B=1, T=5063")
+    o1, st1 = gdn.gdn_fwd(q, k, v, g, beta, s0)
+    cat = lambda t: torch.cat([t, t], 0).contiguous()  # noqa: E731
+    o2, st2 = gdn.gdn_fwd(cat(q), cat(k), cat(v), cat(g), cat(beta), cat(s0))
+    torch.cuda.synchronize()
+    assert torch.equal(o2[:1], o1) and torch.equal(o2[1:], o1)
+    assert torch.equal(st2[:1], st1) and torch.equal(st2[1:], st1)
+    o_ref, s_ref = oracle_for(inp, heads=[0, 19], batches=[0])
+    _check(inp, o1.cpu().numpy()[:, :, [0, 19]], st1.cpu().numpy()[:, [0, 19]], o_ref, s_ref, TOL_BF16,
+           "two streams, heads 0 and 19")
+
+
 def test_closed_forms_on_gpu():
     from hybrid_linear_attention_gdn_amd.inputs import Workload
     w = Workload("closed", 1, 2, 2, 100, "bf16", 77)
