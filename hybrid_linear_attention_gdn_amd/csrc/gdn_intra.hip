@@ -49,6 +49,27 @@ static_assert(2 * 80 * 14 * 4 <= 15 * kBlkF * 4, "norm partial sums fit in the P
 
 __device__ __forceinline__ F16 f16_of(const uint32_t *w) { return F16{{w[0], w[1]}}; }
 
+// inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within rows
+// of 16 lanes, then row broadcasts across them)
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, true));
+}
+__device__ __forceinline__ float wave_scan(float x) {
+  x += dpp<0x111>(x);       // row_shr:1
+  x += dpp<0x112>(x);       // row_shr:2
+  x += dpp<0x114>(x);       // row_shr:4
+  x += dpp<0x118>(x);       // row_shr:8
+  x += dpp<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+// e^x on the hardware exp2 (relative error a few ulp for |x| up to ~100)
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
 __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                        const float *__restrict__ g, const float *__restrict__ beta,
                                                        char *__restrict__ Mout, char *__restrict__ Pout,
@@ -131,49 +152,41 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
   }
   __syncthreads();
   // per-token scalars: beta, 1/||k||, 1/||q||, G; chunk scalars for the state pass.
-  // Wave 0: lane l takes tokens l and 64 + l (l < 16); G, the inclusive prefix
-  // sum of the floored log-decays over the chunk, comes from two wave scans.
-  if (wave == 0) {
-    auto scan = [&](float x) {
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
-      return x;
-    };
-    const float G0 = scan(gl[lane]);
-    const float G1 = scan(lane < C - 64 ? gl[64 + lane] : 0.f) + __shfl(G0, 63);
-    const float Gl = __shfl(G1, C - 65);  // G at the chunk's last token
+  // Waves 0 and 1 take tokens 64 w + lane; G, the inclusive prefix sum of the
+  // floored log-decays over the chunk, comes from wave scans of its two parts.
+  // The hardware reciprocal square root, reciprocal and exp2 are within a few
+  // ulp (the bf16 path's error budget is 1e-2 of rms(o)).
+  if (wave < 2) {
+    const float G0 = wave_scan(gl[lane]);                               // tokens 0 .. 63
+    const float G1 = wave_scan(lane < C - 64 ? gl[64 + lane] : 0.f);   // tokens 64 .. 79, local
+    const float G0_last = lane_value(G0, 63);
+    const float Gl = G0_last + lane_value(G1, C - 65);  // G at the chunk's last token
+    const int t = 64 * wave + lane;
     float *cs = CSout + rec * kCsFloats;
+    if (t < C) {
+      const bool ok = t < n;
+      float nk = 0.f, nq = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int t = s2 == 0 ? lane : 64 + lane;
-      if (t < C) {
-        const bool ok = t < n;
-        float nk = 0.f, nq = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < 14; ++cc) {
-          nk += sqk[t * 14 + cc];
-          nq += sqq[t * 14 + cc];
-        }
-        const float rk = (flags & kQkPrenormalized) ? 1.f : 1.f / fmaxf(sqrtf(nk), 1e-6f);
-        const float rq = (flags & kQkPrenormalized) ? 1.f : 1.f / fmaxf(sqrtf(nq), 1e-6f);
-        const float bt = (flags & kBetaIsProb) ? bl[t] : 1.f / (1.f + expf(-bl[t]));
-        const float G = s2 == 0 ? G0 : G1;
-        const float bo = ok ? bt : 0.f, rko = ok ? rk : 0.f, rqo = ok ? rq : 0.f;
-        const float gam = expf(G);
-        sbeta[t] = bo;
-        srq[t] = rqo;
-        srk[t] = rko;
-        sG[t] = G;
-        ss[t] = rko * expf(Gl - G);
-        cs[t] = bo;
-        cs[80 + t] = bo * gam * rko;
-        cs[160 + t] = gam * rqo;
+      for (int cc = 0; cc < 14; ++cc) {
+        nk += sqk[t * 14 + cc];
+        nq += sqq[t * 14 + cc];
       }
+      const float rk = (flags & kQkPrenormalized) ? 1.f : __builtin_amdgcn_rsqf(fmaxf(nk, 1e-12f));
+      const float rq = (flags & kQkPrenormalized) ? 1.f : __builtin_amdgcn_rsqf(fmaxf(nq, 1e-12f));
+      const float bt = (flags & kBetaIsProb) ? bl[t] : __builtin_amdgcn_rcpf(1.f + fexp(-bl[t]));
+      const float G = wave == 0 ? G0 : G0_last + G1;
+      const float bo = ok ? bt : 0.f, rko = ok ? rk : 0.f, rqo = ok ? rq : 0.f;
+      const float gam = fexp(G);
+      sbeta[t] = bo;
+      srq[t] = rqo;
+      srk[t] = rko;
+      sG[t] = G;
+      ss[t] = rko * fexp(Gl - G);
+      cs[t] = bo;
+      cs[80 + t] = bo * gam * rko;
+      cs[160 + t] = gam * rqo;
     }
-    if (lane == 0) cs[240] = expf(Gl);
+    if (wave == 0 && lane == 0) cs[240] = fexp(Gl);
   }
   __syncthreads();
 
