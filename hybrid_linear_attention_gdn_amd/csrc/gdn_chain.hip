@@ -1,22 +1,39 @@
 // Kernel "chain" of the MFMA family: the sequential state pass fused with the
-// output, one workgroup (4 waves) per (b, h, 16 columns of d_v).
+// output, one workgroup per (b, h, 16 columns of d_v).
 //
 // Per chunk (the algebra is in gdn_mfma_common.h):
 //   Y = K S^T,  R = diag(beta) V - diag(beta gamma rk) Y,
 //   O = diag(gamma rq) Q S^T + P' R,   S^T <- gamma_n S^T + M R.
 // The 16 x 112 fp32 state slice S^T lives in accumulator registers as 7 row
-// tiles spread over the waves.  Per chunk, two barriers exchange the bf16
-// hi/lo operands S (after phase 0) and R (after phase A) through LDS.
+// tiles spread over four compute waves.  Two barriers per chunk: X opens
+// chunk c (S published as bf16 hi/lo B operands, the chunk's rows and record
+// landed in LDS), Y follows phase A (R published; every other LDS operand
+// of the chunk already read into registers).
 //
-// Operand traffic.  K, Q and this workgroup's 16 columns of V are loaded two
-// chunks ahead by all 256 threads with 16-byte row loads (a 224-byte bf16 row
-// is 14 such pieces) into a register set, and written to one of two LDS
-// staging buffers a step later; each wave then reads its
-// fragments from LDS (rows padded to 232 bytes so the 8-byte fragment reads
-// of 16 consecutive rows fall in distinct banks).  The chunk's 1 KB record of
-// per-token scales is staged with the rows (one load by wave 0).  The
-// fragment-ordered M and P' records are read straight into registers, two
-// chunks ahead: every such load is a contiguous 1 KB per instruction.
+// Wave roles (eight waves, two per SIMD):
+//   0-3  compute: every operand comes from LDS; they issue no global load,
+//        only the output stores.
+//   4-6  copy: buffer-to-LDS loads (16 bytes per lane, no register round
+//        trip) of the chunk's M and P' record, scales, K and Q rows and this
+//        workgroup's 16 columns of V.  Each copy wave waits on exact counts of
+//        its own loads, so later copies stay in flight across the barriers.
+//   7    L2 warm-up of a chunk two steps ahead.
+// With one wave per SIMD doing everything, a load that cannot issue blocks
+// the matrix instructions queued behind it in that wave; split this way, the
+// compute waves keep issuing while the copy waves wait on the memory system.
+//
+// Buffers.  Rows (K, Q, V, scales) are double-buffered and the M / P' record
+// single-buffered.  Phase A reads all of them, so at barrier Y both the
+// record buffer and row buffer c & 1 are free: the copy waves then issue
+// chunk c + 1's record (due at X of c + 1) and chunk c + 2's rows.
+//
+// K and Q rows sit at a 256-byte stride with their 16-byte pieces permuted
+// by row (slot = piece ^ (row & 15)), so the 16-byte fragment reads of 16
+// consecutive rows hit 16 distinct bank groups.  The products K S^T and
+// Q S^T use the instruction's natural k-order (lane group g holds k = 8g ..
+// 8g + 7), which makes each K/Q fragment one contiguous 16-byte read; the
+// state tiles are written to LDS in that order.  The products with R keep
+// the "pair" k-order of the M and P' records.
 #include "gdn_mfma_common.h"
 
 #include <algorithm>
@@ -29,14 +46,35 @@ namespace {
 
 // Raw buffer access (gfx9 descriptor, stride 0): an offset at or past
 // `bytes` reads zero and drops a store.
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), 0x00020000);
 }
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
-  return make_uint4(x.x, x.y, x.z, x.w);
+// 16 bytes per lane from buffer offset `off` into LDS at dst + 16 * lane
+// (dst is wave-uniform); an out-of-range lane writes zeros.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, int(off), 0, 0, 0);
+}
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier for the compute waves that also keeps the scheduler from
+// moving register-only work (the matrix products) across it: each phase's
+// products must stay on their side of the barrier that hands buffers back.
+__device__ __forceinline__ void compute_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Barrier for the waves that touch LDS only through the copy engine (or not
+// at all): no fence, so no wait on the copies still in flight is implied.
+__device__ __forceinline__ void bare_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct Roles {
@@ -54,29 +92,34 @@ __device__ constexpr Roles kRoles[4] = {
     {1, {2, 0}, 1, {2}, 0, {0, 0}, 1, {2, 0}, 2, {5, 6, 0}},
     {2, {3, 4}, 0, {0}, 2, {3, 4}, 2, {3, 4}, 0, {0, 0, 0}},
 };
+constexpr int kComputeWaves = 4;
+constexpr int kThreads = 8 * 64;
 
-constexpr int kRowPad = 116;  // bf16 per staged K/Q row (232 B)
-constexpr int kVtPad = 84;    // bf16 per staged V^T row (168 B)
-constexpr int kLdsS = 0;                                 // S operand: hi/lo x (3 x 1 KB + 512 B)
-constexpr int kLdsR = 2 * (3 * 1024 + 512);              // R operand: hi/lo x (2 x 1 KB + 512 B)
-constexpr int kLdsStage = kLdsR + 2 * (2 * 1024 + 512);  // two K/Q/V^T buffers
-constexpr int kStageK = 0;
-constexpr int kStageQ = C * kRowPad * 2;                 // 18,560
-constexpr int kStageV = 2 * C * kRowPad * 2;             // 37,120
-constexpr int kStageCs = kStageV + 16 * kVtPad * 2;     // 39,808: the chunk's 256 scale floats
-constexpr int kStageBytes = kStageCs + kCsFloats * 4;    // 40,832
-constexpr int kLdsChain = kLdsStage + 2 * kStageBytes;   // 93,952
-static_assert(kStageBytes % 16 == 0, "stage buffers stay 16-byte aligned");
+// LDS map (bytes)
+constexpr int kLdsS = 0;                         // S operand: hi/lo x (3 x 1 KB + 512 B)
+constexpr int kLdsR = 2 * (3 * 1024 + 512);      // R operand: hi/lo x (2 x 1 KB + 512 B)
+constexpr int kLdsMP = kLdsR + 2 * (2 * 1024 + 512);  // M then P' record of the current chunk
+constexpr int kLdsRows = kLdsMP + kMBytes + kPBytes;  // two row buffers
+constexpr int kRowStride = 256;                  // bytes per staged K/Q row (224 used)
+constexpr int kRowK = 0;
+constexpr int kRowQ = C * kRowStride;            // 20,480
+constexpr int kRowV = 2 * C * kRowStride;        // 40,960: V tile, 80 rows x 32 B (+ 512 B of tail zeros)
+constexpr int kRowCs = kRowV + 3 * 1024;         // 44,032: the chunk's 256 scale floats
+constexpr int kRowsBytes = kRowCs + kCsFloats * 4;  // 45,056
+constexpr int kLdsChain = kLdsRows + 2 * kRowsBytes;  // 153,600
+static_assert(kMBytes % 1024 == 0 && kPBytes % 1024 == 0 && kCsFloats * 4 == 1024, "whole 1 KB copies");
+static_assert(kLdsMP % 1024 == 0 && kLdsRows % 1024 == 0 && kRowsBytes % 1024 == 0, "copy targets 1 KB aligned");
+static_assert(kLdsChain <= 160 * 1024, "fits one CU's LDS");
 
-// Everything one wave reads from global memory for one chunk, besides the
-// staged rows: independent of the state, so the next chunk's set is in flight
-// while the current one is consumed.
-struct ChunkOps {
-  F32 Mf[3][2][2];           // M fragments of the owned state tiles [tile][block][hi/lo]
-  F16 Mt[3][2];
-  F32 Pf[2][2][2];           // P' fragments of the output tiles
-  F16 Pt[2][2];
-};
+// Copy split between the three copy waves: per chunk, a share of the M / P'
+// record and a share of the rows.
+constexpr int kMInstr = kMBytes / 1024;             // 35
+constexpr int kPInstr = kPBytes / 1024;             // 15
+constexpr int kMShare = 17;                         // waves 0, 1: M 0..16, 17..33; wave 2: M 34 and P'
+constexpr int kRowInstrKQ = C * kRowStride / 1024;  // 20 per matrix
+__device__ constexpr int kRecShare[3] = {kMShare, kMShare, kMInstr - 2 * kMShare + kPInstr};
+__device__ constexpr int kRowShare[3] = {kRowInstrKQ, kRowInstrKQ, 3 + 1};
+static_assert(kMShare + 2 * kRowInstrKQ < 64 && kMInstr - 2 * kMShare + kPInstr + 8 < 64, "vmcnt holds 63");
 
 struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k = d_k)
   F32 f[3];
@@ -84,17 +127,17 @@ struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k 
 };
 
 template <int W, bool kOutBf16>
-__device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                           const uint16_t *__restrict__ v, const char *__restrict__ Mws,
-                                           const char *__restrict__ Pws, const float *__restrict__ CS,
-                                           const float *state_in, float *state_out, void *__restrict__ o, int T,
-                                           int H, int N, int cb, int ce, int b, int h, int nt, char *lds) {
+__device__ __forceinline__ void compute_role(const float *__restrict__ state_in, float *state_out,
+                                             void *__restrict__ o, int T, int H, int cb, int ce, int b, int h,
+                                             int nt, char *lds) {
   constexpr Roles ro = kRoles[W];
-  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+  constexpr int nA = ro.nY + ro.nQA;  // 16-row tiles of K or Q multiplied by S^T in phase A
+  const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const size_t u = size_t(b) * H + h;
   const size_t rowstride = size_t(H) * D;
   char *Slds = lds + kLdsS;
   char *Rlds = lds + kLdsR;
+  const char *MPlds = lds + kLdsMP;
 
   // ---- state slice: S^T tile j, accumulator rows d_k = 16j + 4lg + e, column d_v = 16nt + ln
   f32x4 S[3];
@@ -106,181 +149,81 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       S[s] = f32x4{t.x, t.y, t.z, t.w};
     }
   }
+  // Where this lane's hi half of tile j goes in the B-operand image of S in
+  // the natural k-order: the 16 bytes read by lane (ln, g) of 32-deep block kb
+  // are rows 8(g & 1) .. + 7 of tile 2kb + (g >> 1), i.e. the 8-byte halves
+  // written by lane groups 2(g & 1) and 2(g & 1) + 1 of that tile.
+  auto s_slot = [&](int j) { return (j >> 1) * 1024 + (ln + 16 * (2 * (j & 1) + (lg >> 1))) * 16 + (lg & 1) * 8; };
 
-  // ---- cooperative staging of K, Q rows and this tile's V columns (all 256 threads).
-  // Thread tid takes 16-byte piece (tid & 15) of rows (tid >> 4) + 16 i of K and of Q
-  // (pieces 14, 15 of a 224-byte row do not exist), and, for tid < 160, half (tid & 1)
-  // of row tid >> 1 of the V tile: every address is a fixed per-thread offset plus the chunk base.
-  // The loads are buffer loads through a descriptor that covers exactly the
-  // chunk's valid rows: rows past the end (and the non-existent pieces 14, 15)
-  // read as zero with no branch, so every wave issues the same memory
-  // instructions on every path and the in-order load counter never forces a
-  // wait on the next chunk's prefetch.
-  const int sp = tid & 15, sr = tid >> 4;
-  const bool sp_ok = sp < 14;
-  const uint32_t row_bytes = uint32_t(rowstride) * 2u;
-  const uint32_t offKQ = sp_ok ? uint32_t(sr) * row_bytes + uint32_t(h) * (D * 2) + 16u * sp : kOutOfRange;
-  const uint32_t offV = tid < 2 * C ? uint32_t(tid >> 1) * row_bytes + uint32_t(h) * (D * 2) + 32u * nt + 16u * (tid & 1)
-                                    : kOutOfRange;
-  struct Staged {
-    uint4 k[CT], q[CT], v, cs;  // cs: wave 0 only
-  };
-  auto stage_issue = [&](Staged &st, int c) {
-    const int t0 = c * C, nv = min(C, T - t0);
-    const size_t base = (size_t(b) * T + t0) * rowstride;
-    const uint32_t bytes = uint32_t(nv) * row_bytes;
-    const auto rk_ = make_rsrc(k + base, bytes), rq_ = make_rsrc(q + base, bytes), rv_ = make_rsrc(v + base, bytes);
-#pragma unroll
-    for (int i = 0; i < CT; ++i) {
-      const uint32_t off = offKQ == kOutOfRange ? kOutOfRange : offKQ + uint32_t(16 * i) * row_bytes;
-      st.k[i] = buf_load16(rk_, off);
-      st.q[i] = buf_load16(rq_, off);
-    }
-    st.v = buf_load16(rv_, offV);
-    if (W == 0) st.cs = ldg16(CS + (u * N + c) * kCsFloats + 4 * lane);  // the chunk's scales: one 1 KB load
-  };
-  auto stage_store = [&](const Staged &st, int buf) {
-    char *sb = lds + kLdsStage + buf * kStageBytes;
-    if (sp_ok) {
-#pragma unroll
-      for (int i = 0; i < CT; ++i) {
-        const int off = (sr + 16 * i) * (kRowPad * 2) + 16 * sp;
-        uint2 *dk = reinterpret_cast<uint2 *>(sb + kStageK + off);
-        uint2 *dq = reinterpret_cast<uint2 *>(sb + kStageQ + off);
-        dk[0] = make_uint2(st.k[i].x, st.k[i].y);
-        dk[1] = make_uint2(st.k[i].z, st.k[i].w);
-        dq[0] = make_uint2(st.q[i].x, st.q[i].y);
-        dq[1] = make_uint2(st.q[i].z, st.q[i].w);
-      }
-    }
-    if (tid < 2 * C) {
-      uint16_t *vt = reinterpret_cast<uint16_t *>(sb + kStageV);
-      const int vr = tid >> 1, half = tid & 1;
-      const uint32_t w[4] = {st.v.x, st.v.y, st.v.z, st.v.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vt[(8 * half + j) * kVtPad + vr] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
-    }
-    if (W == 0) *reinterpret_cast<uint4 *>(sb + kStageCs + 16 * lane) = st.cs;
-  };
-  // A-operand fragments of a 16-row tile of the staged K (m = 0) or Q (m = 1), "pair" k-order
-  auto rows_frag = [&](int buf, int m, int tile) {
-    const char *rowp = lds + kLdsStage + buf * kStageBytes + (m ? kStageQ : kStageK) + (16 * tile + ln) * (kRowPad * 2);
+  // A-operand fragments of a 16-row tile of the staged K (m = 0) or Q (m = 1)
+  auto rows_frag = [&](const char *rb, int m, int tile) {
+    const char *rowp = rb + (m ? kRowQ : kRowK) + (16 * tile + ln) * kRowStride;
     RowFrags rf;
 #pragma unroll
     for (int kb = 0; kb < 3; ++kb) {
-      const uint2 x0 = *reinterpret_cast<const uint2 *>(rowp + 64 * kb + 8 * lg);
-      const uint2 x1 = *reinterpret_cast<const uint2 *>(rowp + 64 * kb + 32 + 8 * lg);
-      rf.f[kb] = F32{{x0.x, x0.y, x1.x, x1.y}};
+      const uint4 x = *reinterpret_cast<const uint4 *>(rowp + 16 * ((4 * kb + lg) ^ ln));
+      rf.f[kb] = F32{{x.x, x.y, x.z, x.w}};
     }
-    const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 192 + 8 * lg);
+    const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 16 * ((12 + (lg >> 1)) ^ ln) + 8 * (lg & 1));
     rf.t = F16{{x2.x, x2.y}};
     return rf;
   };
-
-  // ---- L2 warm-up of chunk c + kAhead: the head's 7 column-tile workgroups
-  // (on one XCD) split its cache lines -- 280 of M, 120 of P', 8 of scales and
-  // 3 per 224-byte row of K, Q, V -- so that the staging and operand loads of
-  // that chunk hit L2 instead of all waiting on the same HBM misses.  One
-  // dword load per lane, at a fixed per-lane base plus a per-chunk stride.
-  constexpr int kAhead = 4;
-  const char *pe_base;
-  size_t pe_stride;
-  int pe_row = -1;
-  {
-    const int pe = nt + NT * (64 * (tid >> 6) + lane);  // 0 .. 1791, cache-line task
-    if (pe < 280) {
-      pe_base = Mws + u * N * size_t(kMBytes) + 128 * pe;
-      pe_stride = kMBytes;
-    } else if (pe < 400) {
-      pe_base = Pws + u * N * size_t(kPBytes) + 128 * (pe - 280);
-      pe_stride = kPBytes;
-    } else if (pe < 408) {
-      pe_base = reinterpret_cast<const char *>(CS + u * N * kCsFloats) + 128 * (pe - 400);
-      pe_stride = kCsFloats * sizeof(float);
-    } else {
-      const int r = min(pe - 408, 3 * 3 * C - 1), t = r / (3 * C), part = r % 3;
-      pe_row = (r % (3 * C)) / 3;
-      const uint16_t *src = t == 0 ? k : (t == 1 ? q : v);
-      pe_base = reinterpret_cast<const char *>(src + (size_t(b) * T * H + h) * D) + (part == 0 ? 0 : (part == 1 ? 128 : 220));
-      pe_stride = size_t(C) * row_bytes;
-    }
-  }
-  auto l2_touch = [&](int c) -> uint32_t {
-    const int cp = min(c + kAhead, ce - 1);
-    // a row past the end of the last chunk touches the chunk's last row instead
-    const int rr = pe_row < 0 ? 0 : min(pe_row, T - 1 - cp * C);
-    const char *a = pe_base + size_t(cp) * pe_stride + size_t(rr) * row_bytes;
-    return *reinterpret_cast<const uint32_t *>(a);
+  auto ldf4 = [](const float *p) {
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    return f32x4{t.x, t.y, t.z, t.w};
   };
-
-  auto load_ops = [&](ChunkOps &op, int c) {
-    const char *Mr = Mws + (u * N + c) * size_t(kMBytes);
-    const char *Pr = Pws + (u * N + c) * size_t(kPBytes);
+  auto ld32 = [&](int off) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(MPlds + off + lane * 16);
+    return F32{{x.x, x.y, x.z, x.w}};
+  };
+  auto ld16 = [&](int off) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(MPlds + off + lane * 8);
+    return F16{{x.x, x.y}};
+  };
+  // tiles x (hi, lo) independent accumulation chains over the four k-blocks of d_k
+  auto rows_times_S = [](const RowFrags *rf, int n, const F32 *Sh, const F32 *Sl, const F16 &Sth, const F16 &Stl,
+                         f32x4 *out) {
+    f32x4 ah[2] = {zero4(), zero4()}, al[2] = {zero4(), zero4()};
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      if (s < ro.nS) {
-        const int mt = ro.S[s];
+    for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl) {
-            const uint4 x = ldg16(Mr + m_off32(mt, kb, hl) + lane * 16);
-            op.Mf[s][kb][hl] = F32{{x.x, x.y, x.z, x.w}};
-          }
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-          const uint2 x = ldg8(Mr + m_off16(mt, hl) + lane * 8);
-          op.Mt[s][hl] = F16{{x.x, x.y}};
+      for (int a = 0; a < 2; ++a)
+        if (a < n) {
+          ah[a] = mma(rf[a].f[kb], Sh[kb], ah[a]);
+          al[a] = mma(rf[a].f[kb], Sl[kb], al[a]);
         }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+      if (a < n) {
+        ah[a] = mma(rf[a].t, Sth, ah[a]);
+        al[a] = mma(rf[a].t, Stl, al[a]);
+        out[a] = ah[a] + al[a];
       }
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < ro.nO) {
-        const int R = ro.O[s];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl) {
-            if (kb < (R + 1) / 2) {
-              const uint4 x = ldg16(Pr + p_off32(R, kb, hl) + lane * 16);
-              op.Pf[s][kb][hl] = F32{{x.x, x.y, x.z, x.w}};
-            }
-          }
-        if (!(R & 1))
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl) {
-            const uint2 x = ldg8(Pr + p_off16(R, hl) + lane * 8);
-            op.Pt[s][hl] = F16{{x.x, x.y}};
-          }
-      }
-    }
   };
 
-  // one chunk: consume `cur` and staging buffer c & 1; put chunk c + 1 in flight
-  auto step = [&](int c, const ChunkOps &cur, ChunkOps &ahead, Staged &st_issue, const Staged &st_store) {
-    const int t0 = c * C, nv = min(C, T - t0), buf = c & 1;
-    // ---- phase 0: publish this wave's state tiles as bf16 hi/lo B operands
+  // phase 0 of the first chunk: publish the entry state
+  auto publish_S = [&]() {
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       if (s < ro.nS) {
         const int j = ro.S[s];
         uint32_t hi[2], lo[2];
         split4(S[s], hi, lo);
-        if (j < 6) {
-          const int kb = j >> 1, half = j & 1;
-          *reinterpret_cast<uint2 *>(Slds + kb * 1024 + lane * 16 + half * 8) = make_uint2(hi[0], hi[1]);
-          *reinterpret_cast<uint2 *>(Slds + 3584 + kb * 1024 + lane * 16 + half * 8) = make_uint2(lo[0], lo[1]);
-        } else {
-          *reinterpret_cast<uint2 *>(Slds + 3072 + lane * 8) = make_uint2(hi[0], hi[1]);
-          *reinterpret_cast<uint2 *>(Slds + 3584 + 3072 + lane * 8) = make_uint2(lo[0], lo[1]);
-        }
+        const int off = j < 6 ? s_slot(j) : 3072 + lane * 8;
+        *reinterpret_cast<uint2 *>(Slds + off) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2 *>(Slds + 3584 + off) = make_uint2(lo[0], lo[1]);
       }
     }
-    __syncthreads();
-    const auto ro_ = make_rsrc(static_cast<char *>(o) + (size_t(b) * T + t0) * rowstride * (kOutBf16 ? 2 : 4),
-                               uint32_t(nv) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
-    // ---- phase A: S operands, Y = K S^T -> R (published), Q S^T for phase-A tiles
+  };
+  publish_S();
+  for (int c = cb; c < ce; ++c) {
+    const int t0 = c * C, nv = min(C, T - t0);
+    const char *rb = lds + kLdsRows + (c & 1) * kRowsBytes;
+    const float *csl = reinterpret_cast<const float *>(rb + kRowCs);
+    const uint16_t *vl = reinterpret_cast<const uint16_t *>(rb + kRowV);
+    compute_barrier();  // X: chunk c opens (S published; its rows and record landed)
+    // ---- phase A: every LDS operand of the chunk except R is read here, so
+    // that both buffers are free once R is published
     F32 Sh[3], Sl[3];
     F16 Sth, Stl;
 #pragma unroll
@@ -296,35 +239,66 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       Sth = F16{{xh.x, xh.y}};
       Stl = F16{{xl.x, xl.y}};
     }
-    auto rows_times_S = [&](const RowFrags &rf) {
-      f32x4 acc = zero4();
+    RowFrags fa[2];
 #pragma unroll
-      for (int kb = 0; kb < 3; ++kb) {
-        acc = mma(rf.f[kb], Sh[kb], acc);
-        acc = mma(rf.f[kb], Sl[kb], acc);
+    for (int a = 0; a < 2; ++a)
+      if (a < nA) fa[a] = rows_frag(rb, a < ro.nY ? 0 : 1, a < ro.nY ? ro.Y[a] : ro.QA[0]);
+    f32x4 aa[2], bb[2];
+    float va[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ro.nY) {
+        const int tile = ro.Y[s];
+        aa[s] = ldf4(csl + 16 * tile + 4 * lg);
+        bb[s] = ldf4(csl + 80 + 16 * tile + 4 * lg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) va[s][e] = bf16_to_f32(vl[(16 * tile + 4 * lg + e) * 16 + ln]);
       }
-      acc = mma(rf.t, Sth, acc);
-      acc = mma(rf.t, Stl, acc);
-      return acc;
-    };
-    const uint16_t *vt = reinterpret_cast<const uint16_t *>(lds + kLdsStage + buf * kStageBytes + kStageV);
-    const float *csl = reinterpret_cast<const float *>(lds + kLdsStage + buf * kStageBytes + kStageCs);
-    auto ldf4 = [](const float *p) {
-      const float4 t = *reinterpret_cast<const float4 *>(p);
-      return f32x4{t.x, t.y, t.z, t.w};
-    };
+    __builtin_amdgcn_sched_barrier(0);  // the operands of Y and R first: they are on the critical path
+    RowFrags fb[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ro.nQB) fb[s] = rows_frag(rb, 1, ro.QB[s]);
+    F32 Mf[3][2][2];
+    F16 Mt[3][2];
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < ro.nS) {
+        const int mt = ro.S[s];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) Mf[s][kb][hl] = ld32(m_off32(mt, kb, hl));
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) Mt[s][hl] = ld16(m_off16(mt, hl));
+      }
+    F32 Pf[2][2][2];
+    F16 Pt[2][2];
+    f32x4 cc[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ro.nO) {
+        const int R = ro.O[s];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+            if (kb < (R + 1) / 2) Pf[s][kb][hl] = ld32(kMBytes + p_off32(R, kb, hl));
+        if (!(R & 1))
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) Pt[s][hl] = ld16(kMBytes + p_off16(R, hl));
+        cc[s] = ldf4(csl + 160 + 16 * R + 4 * lg);
+      }
+    const float gamma_n = csl[240];
+    f32x4 ya[2];
+    rows_times_S(fa, nA, Sh, Sl, Sth, Stl, ya);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < ro.nY) {
         const int tile = ro.Y[s];
-        const f32x4 y = rows_times_S(rows_frag(buf, 0, tile));
-        const uint2 vv = *reinterpret_cast<const uint2 *>(vt + ln * kVtPad + 16 * tile + 4 * lg);
-        const float va[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
-                             __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
         float r4[4];
-        const f32x4 aa = ldf4(csl + 16 * tile + 4 * lg), bb = ldf4(csl + 80 + 16 * tile + 4 * lg);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] = aa[e] * va[e] - bb[e] * y[e];
+        for (int e = 0; e < 4; ++e) r4[e] = aa[s][e] * va[s][e] - bb[s][e] * ya[s][e];
         uint32_t hi[2], lo[2];
         split4(r4, hi, lo);
         if (tile < 4) {
@@ -338,12 +312,10 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       }
     }
     f32x4 QS[2] = {zero4(), zero4()};
-    if (ro.nQA) QS[0] = rows_times_S(rows_frag(buf, 1, ro.QA[0]));
-    __syncthreads();
-    // ---- phase B: R operands; state update and outputs.  The operand
-    // fragments of chunk c + 2 are requested here (past the end, the last
-    // chunk is fetched again: the same instructions issue on every chunk).
-    load_ops(ahead, min(c + 2, ce - 1));
+    if (ro.nQA) QS[0] = ya[ro.nY];
+    compute_barrier();  // Y: R published; the record and row buffer c & 1 may be refilled
+    // ---- phase B: R operands, the state update, S published for chunk c + 1,
+    // then the outputs
     F32 Rh[2], Rl[2];
     F16 Rth, Rtl;
 #pragma unroll
@@ -359,57 +331,84 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
       Rth = F16{{xh.x, xh.y}};
       Rtl = F16{{xl.x, xl.y}};
     }
+    // S^T tile update: gamma_n S + Mhi Rhi + Mhi Rlo + Mlo Rhi as three chains
+    f32x4 a0[3], a1[3], a2[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < ro.nS) {
+        a0[s] = S[s] * gamma_n;
+        a1[s] = zero4();
+        a2[s] = zero4();
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+        if (s < ro.nS) {
+          a0[s] = mma(Mf[s][kb][0], Rh[kb], a0[s]);
+          a1[s] = mma(Mf[s][kb][0], Rl[kb], a1[s]);
+          a2[s] = mma(Mf[s][kb][1], Rh[kb], a2[s]);
+        }
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < ro.nS) {
+        a0[s] = mma(Mt[s][0], Rth, a0[s]);
+        a1[s] = mma(Mt[s][0], Rtl, a1[s]);
+        a2[s] = mma(Mt[s][1], Rth, a2[s]);
+        S[s] = a0[s] + a1[s] + a2[s];
+      }
+    // S written for chunk c + 1: every wave read S of chunk c before Y
+    publish_S();
+    if (ro.nQB) {
+      f32x4 qb[2];
+      rows_times_S(fb, ro.nQB, Sh, Sl, Sth, Stl, qb);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s < ro.nQB) QS[s] = qb[s];
+    }
+    // outputs: diag(gamma rq) Q S^T + P'hi Rhi + P'hi Rlo + P'lo Rhi
+    f32x4 o0[2], o1[2], o2[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      if (s < ro.nQB) QS[s] = rows_times_S(rows_frag(buf, 1, ro.QB[s]));
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      if (s < ro.nS) {
-        f32x4 acc = S[s] * csl[240];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          acc = mma(cur.Mf[s][kb][0], Rh[kb], acc);
-          acc = mma(cur.Mf[s][kb][0], Rl[kb], acc);
-          acc = mma(cur.Mf[s][kb][1], Rh[kb], acc);
-        }
-        acc = mma(cur.Mt[s][0], Rth, acc);
-        acc = mma(cur.Mt[s][0], Rtl, acc);
-        acc = mma(cur.Mt[s][1], Rth, acc);
-        S[s] = acc;
+      if (s < ro.nO) {
+        o0[s] = cc[s] * QS[s];
+        o1[s] = zero4();
+        o2[s] = zero4();
       }
-    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s < ro.nO && kb < (ro.O[s] + 1) / 2) {
+          o0[s] = mma(Pf[s][kb][0], Rh[kb], o0[s]);
+          o1[s] = mma(Pf[s][kb][0], Rl[kb], o1[s]);
+          o2[s] = mma(Pf[s][kb][1], Rh[kb], o2[s]);
+        }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ro.nO && !(ro.O[s] & 1)) {
+        // the 16-deep block covers token tile R (tile 4: the shared 16-deep R slot;
+        // tiles 0 and 2: first halves of the 32-deep R slots)
+        const int R = ro.O[s];
+        F16 rh, rl;
+        if (R == 4) {
+          rh = Rth;
+          rl = Rtl;
+        } else {
+          rh = F16{{Rh[R >> 1].w[0], Rh[R >> 1].w[1]}};
+          rl = F16{{Rl[R >> 1].w[0], Rl[R >> 1].w[1]}};
+        }
+        o0[s] = mma(Pt[s][0], rh, o0[s]);
+        o1[s] = mma(Pt[s][0], rl, o1[s]);
+        o2[s] = mma(Pt[s][1], rh, o2[s]);
+      }
+    const auto ro_ = make_rsrc(static_cast<char *>(o) + (size_t(b) * T + t0) * rowstride * (kOutBf16 ? 2 : 4),
+                               uint32_t(nv) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < ro.nO) {
         const int R = ro.O[s];
-        f32x4 acc;
-        const f32x4 cc = ldf4(csl + 160 + 16 * R + 4 * lg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = cc[e] * QS[s][e];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (kb < (R + 1) / 2) {
-            acc = mma(cur.Pf[s][kb][0], Rh[kb], acc);
-            acc = mma(cur.Pf[s][kb][0], Rl[kb], acc);
-            acc = mma(cur.Pf[s][kb][1], Rh[kb], acc);
-          }
-        }
-        if (!(R & 1)) {
-          // the 16-deep block covers token tile R (tile 4: the shared 16-deep R slot;
-          // tiles 0 and 2: first halves of the 32-deep R slots)
-          F16 rh, rl;
-          if (R == 4) {
-            rh = Rth;
-            rl = Rtl;
-          } else {
-            const int kb = R >> 1;
-            rh = F16{{Rh[kb].w[0], Rh[kb].w[1]}};
-            rl = F16{{Rl[kb].w[0], Rl[kb].w[1]}};
-          }
-          acc = mma(cur.Pt[s][0], rh, acc);
-          acc = mma(cur.Pt[s][0], rl, acc);
-          acc = mma(cur.Pt[s][1], rh, acc);
-        }
+        const f32x4 acc = o0[s] + o1[s] + o2[s];
         // rows past the chunk's end fall outside the store descriptor and are dropped
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -421,41 +420,7 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
         }
       }
     }
-    // K/Q/V rows two chunks ahead go into the register set freed by the last
-    // store; the set loaded one step ago (chunk c + 1) goes to staging buffer
-    // (c + 1) & 1, last read in chunk c - 1, before this chunk's first barrier.
-    stage_issue(st_issue, min(c + 2, ce - 1));
-    stage_store(st_store, buf ^ 1);
-  };
-
-  // Three operand sets and three staging register sets rotate with the chunk
-  // index mod 3 (chunk c + 1 landed, c + 2 in flight, c being consumed).
-  ChunkOps op0, op1, op2;
-  Staged st0, st1, st2;
-  stage_issue(st0, cb);
-  load_ops(op0, cb);
-  stage_store(st0, cb & 1);
-  stage_issue(st1, min(cb + 1, ce - 1));
-  load_ops(op1, min(cb + 1, ce - 1));
-  uint32_t pf = 0, sink = 0;
-  auto touch = [&](int c) {
-    sink ^= pf;  // consumed a step after its load was issued
-    pf = l2_touch(c);
-  };
-  for (int c = cb; c < ce; c += 3) {
-    step(c, op0, op2, st2, st1);
-    touch(c);
-    if (c + 1 < ce) {
-      step(c + 1, op1, op0, st0, st2);
-      touch(c + 1);
-    }
-    if (c + 2 < ce) {
-      step(c + 2, op2, op1, st1, st0);
-      touch(c + 2);
-    }
   }
-  sink ^= pf;
-  if (T < 0 && sink != 0u) static_cast<uint32_t *>(o)[0] = sink;  // never taken: keeps the touches alive
   if (state_out) {
 #pragma unroll
     for (int s = 0; s < 3; ++s)
@@ -465,13 +430,148 @@ __device__ __forceinline__ void chain_role(const uint16_t *__restrict__ q, const
   }
 }
 
+// Copy wave L (0, 1 or 2).  Before barrier X of chunk c its rows and record
+// must have landed; after barrier Y (phase A has read both buffers) the wave
+// issues its share of chunk c + 1's record and of chunk c + 2's rows.  Loads
+// complete in issue order, so each wait names the number of younger copies
+// that may still be in flight (at most a record share and two row shares:
+// 57 of the 63 the counter holds).
+template <int L>
+__device__ __forceinline__ void copy_role(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                          const uint16_t *__restrict__ v, const char *__restrict__ Mws,
+                                          const char *__restrict__ Pws, const float *__restrict__ CS, int T,
+                                          int H, int N, int cb, int ce, int b, int h, int nt, char *lds) {
+  constexpr int kRec = kRecShare[L], kRow = kRowShare[L];
+  const int lane = threadIdx.x & 63;
+  const size_t u = size_t(b) * H + h;
+  const uint32_t row_bytes = uint32_t(H) * D * 2u;
+  // K / Q: copy i fills LDS rows 4i .. 4i + 3, lane -> (row 4i + lane / 16,
+  // slot lane % 16) holding piece slot ^ (row & 15); pieces 14 and 15 of a
+  // 224-byte row do not exist and read as zero
+  auto kq_off = [&](int i) {
+    const int r = 4 * i + (lane >> 4), p = (lane & 15) ^ (r & 15);
+    return p < 14 ? uint32_t(r) * row_bytes + uint32_t(h) * (D * 2) + 16u * p : kOutOfRange;
+  };
+  // V: copy i fills rows 32i .. 32i + 31 (32 bytes each: this tile's 16 columns)
+  auto v_off = [&](int i) {
+    const int r = 32 * i + (lane >> 1);
+    return r < C ? uint32_t(r) * row_bytes + uint32_t(h) * (D * 2) + 32u * nt + 16u * (lane & 1) : kOutOfRange;
+  };
+  // wave 0: K rows; wave 1: Q rows; wave 2: the V tile and the scales
+  auto copy_rows = [&](int c) {
+    const int t0 = c * C, nv = min(C, T - t0);
+    const size_t base = (size_t(b) * T + t0) * size_t(H) * D;
+    const uint32_t bytes = uint32_t(nv) * row_bytes;  // rows past the end read as zero
+    char *rb = lds + kLdsRows + (c & 1) * kRowsBytes;
+    if constexpr (L < 2) {
+      const auto rs = make_rsrc((L == 0 ? k : q) + base, bytes);
+#pragma unroll
+      for (int i = 0; i < kRowInstrKQ; ++i) copy16(rs, rb + (L == 0 ? kRowK : kRowQ) + 1024 * i, kq_off(i));
+    } else {
+      const auto rv = make_rsrc(v + base, bytes);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) copy16(rv, rb + kRowV + 1024 * i, v_off(i));
+      copy16(make_rsrc(CS + (u * N + c) * kCsFloats, kCsFloats * 4), rb + kRowCs, 16u * lane);
+    }
+  };
+  // waves 0, 1: 17 KB of M each; wave 2: the last KB of M and P'
+  auto copy_record = [&](int c) {
+    const auto rm = make_rsrc(Mws + (u * N + c) * size_t(kMBytes), kMBytes);
+    constexpr int m0 = L == 0 ? 0 : (L == 1 ? kMShare : 2 * kMShare), m1 = L == 2 ? kMInstr : m0 + kMShare;
+#pragma unroll
+    for (int i = m0; i < m1; ++i) copy16(rm, lds + kLdsMP + 1024 * i, 1024u * i + 16u * lane);
+    if constexpr (L == 2) {
+      const auto rp = make_rsrc(Pws + (u * N + c) * size_t(kPBytes), kPBytes);
+#pragma unroll
+      for (int i = 0; i < kPInstr; ++i) copy16(rp, lds + kLdsMP + kMBytes + 1024 * i, 1024u * i + 16u * lane);
+    }
+  };
+  if (cb < ce) {
+    copy_rows(cb);
+    copy_record(cb);
+    if (cb + 1 < ce) copy_rows(cb + 1);
+  }
+  for (int c = cb; c < ce; ++c) {
+    // in flight, oldest first: rows(c), record(c), rows(c + 1) if c + 1 < ce
+    if (c + 1 < ce)
+      wait_vm<kRow>();
+    else
+      wait_vm<0>();
+    bare_barrier();  // X: chunk c opens
+    bare_barrier();  // Y: chunk c's record and rows have been read
+    if (c + 1 < ce) copy_record(c + 1);
+    if (c + 2 < ce) copy_rows(c + 2);
+  }
+  wait_vm<0>();
+}
+
+// L2 warm-up of chunk c + kAhead: the head's 7 column-tile workgroups (on
+// one XCD) split its cache lines -- 280 of M, 120 of P', 8 of scales and
+// 3 per 224-byte row of K, Q, V -- so that the copies of that chunk hit L2
+// instead of all waiting on the same HBM misses.  Four dword loads per lane
+// per chunk, each at a fixed per-lane base plus a per-chunk stride, consumed a
+// chunk later.
+constexpr int kAhead = 2;
+__device__ __forceinline__ void warm_role(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                          const uint16_t *__restrict__ v, const char *__restrict__ Mws,
+                                          const char *__restrict__ Pws, const float *__restrict__ CS,
+                                          void *__restrict__ o, int T, int H, int N, int cb, int ce, int b, int h,
+                                          int nt) {
+  const int lane = threadIdx.x & 63;
+  const size_t u = size_t(b) * H + h;
+  const size_t row_bytes = size_t(H) * D * 2;
+  const char *base[4];
+  size_t stride[4];
+  int prow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pe = nt + NT * (64 * j + lane);  // 0 .. 1791, cache-line task
+    prow[j] = -1;
+    if (pe < 280) {
+      base[j] = Mws + u * N * size_t(kMBytes) + 128 * pe;
+      stride[j] = kMBytes;
+    } else if (pe < 400) {
+      base[j] = Pws + u * N * size_t(kPBytes) + 128 * (pe - 280);
+      stride[j] = kPBytes;
+    } else if (pe < 408) {
+      base[j] = reinterpret_cast<const char *>(CS + u * N * kCsFloats) + 128 * (pe - 400);
+      stride[j] = kCsFloats * sizeof(float);
+    } else {
+      const int r = min(pe - 408, 3 * 3 * C - 1), t = r / (3 * C), part = r % 3;
+      prow[j] = (r % (3 * C)) / 3;
+      const uint16_t *src = t == 0 ? k : (t == 1 ? q : v);
+      base[j] = reinterpret_cast<const char *>(src + (size_t(b) * T * H + h) * D) +
+                (part == 0 ? 0 : (part == 1 ? 128 : 220));
+      stride[j] = size_t(C) * row_bytes;
+    }
+  }
+  uint32_t pf[4] = {0u, 0u, 0u, 0u}, sink = 0;
+  for (int c = cb; c < ce; ++c) {
+    const int cp = min(c + kAhead, ce - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sink ^= pf[j];  // consumed a chunk after its load was issued
+      // a row past the end of the last chunk touches the chunk's last row instead
+      const int rr = prow[j] < 0 ? 0 : min(prow[j], T - 1 - cp * C);
+      pf[j] = *reinterpret_cast<const uint32_t *>(base[j] + size_t(cp) * stride[j] + size_t(rr) * row_bytes);
+    }
+    bare_barrier();
+    bare_barrier();
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sink ^= pf[j];
+  if (T < 0 && sink != 0u) static_cast<uint32_t *>(o)[0] = sink;  // never taken: keeps the touches alive
+}
+
 template <bool kOutBf16>
-__global__ __launch_bounds__(256) void chain_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                    const uint16_t *__restrict__ v, const char *__restrict__ Mws,
-                                                    const char *__restrict__ Pws, const float *__restrict__ CS,
-                                                    const float *state_in, float *state_out,
-                                                    void *__restrict__ o, int T, int H, int N, int cb, int ce,
-                                                    int units) {
+__global__ __launch_bounds__(kThreads) void chain_kernel(const uint16_t *__restrict__ q,
+                                                         const uint16_t *__restrict__ k,
+                                                         const uint16_t *__restrict__ v,
+                                                         const char *__restrict__ Mws,
+                                                         const char *__restrict__ Pws,
+                                                         const float *__restrict__ CS, const float *state_in,
+                                                         float *state_out, void *__restrict__ o, int T, int H,
+                                                         int N, int cb, int ce, int units) {
   extern __shared__ __align__(16) char lds[];
   // Workgroup i runs on XCD i % 8: keep the 7 column tiles of a (b, h) on one
   // XCD so that its K, Q, M and P' are fetched from HBM once into that L2.
@@ -481,10 +581,14 @@ __global__ __launch_bounds__(256) void chain_kernel(const uint16_t *__restrict__
   const int b = u / H, h = u % H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wave) {
-    case 0: chain_role<0, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 1: chain_role<1, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 2: chain_role<2, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
-    default: chain_role<3, kOutBf16>(q, k, v, Mws, Pws, CS, state_in, state_out, o, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 0: compute_role<0, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 1: compute_role<1, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 2: compute_role<2, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 3: compute_role<3, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 4: copy_role<0>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 5: copy_role<1>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 6: copy_role<2>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    default: warm_role(q, k, v, Mws, Pws, CS, o, T, H, N, cb, ce, b, h, nt); break;
   }
 }
 
@@ -532,10 +636,10 @@ hipError_t launch_chain(const Plan &p, const Args &a, const char *M, const char 
   const int units = p.B * p.H;
   const unsigned grid = 8u * mfma::NT * unsigned((units + 7) / 8);
   if (p.o_bf16)
-    mfma::chain_kernel<true><<<dim3(grid), dim3(256), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
+    mfma::chain_kernel<true><<<dim3(grid), dim3(mfma::kThreads), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
                                                                            p.H, p.N, cb, ce, units);
   else
-    mfma::chain_kernel<false><<<dim3(grid), dim3(256), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
+    mfma::chain_kernel<false><<<dim3(grid), dim3(mfma::kThreads), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
                                                                             p.H, p.N, cb, ce, units);
   return hipGetLastError();
 }

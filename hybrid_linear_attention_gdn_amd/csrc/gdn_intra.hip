@@ -87,11 +87,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
   auto blk = [](float *base, int I, int J) { return base + tri(I, J) * kBlkF; };
 
   // block -> (b, c, h) over chunks c_first .. c_first + n_chunks - 1, h fastest:
-  // neighbouring workgroups read neighbouring rows
+  // neighbouring workgroups read neighbouring rows.  Chunks run last to
+  // first, so that the records and rows of the first chunks, which the state
+  // pass reads first, are the most recently touched when it starts (and are
+  // still in the last-level cache).
   int x = blockIdx.x;
   const int h = x % H;
   x /= H;
-  const int c = c_first + x % n_chunks;
+  const int c = c_first + (n_chunks - 1 - x % n_chunks);
   const int b = x / n_chunks;
   const int t0 = c * C;
   const int n = min(C, T - t0);

@@ -25,6 +25,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -39,13 +40,21 @@ _COMMON = {True: ["gdn_mfma_common.h", "gdn_internal.h"], False: ["gdn_prep.hip"
                                                                     "gdn_internal.h"]}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed, so that
+    editing a comment does not count as changing the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(stage: str, mfma: bool) -> str:
-    """Short hash of the sources of the kernel that `stage` runs."""
+    """Short hash of the code (comments excluded) of the kernel that `stage` runs."""
     files = _STAGE_SOURCES.get((mfma, stage), []) + _COMMON[mfma]
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(PKG, "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -52,3 +52,9 @@ def test_source_hash_tracks_the_kernel_files():
     b = rs.kernel_source_hash("intra", True)
     assert a != b and len(a) == 16
     assert rs.kernel_source_hash("state", True) == a
+
+
+def test_source_hash_ignores_comments_and_layout():
+    a = rs._code_only("int x = 1; // note\n/* block\n comment */  int  y = 2;\n")
+    assert a == "int x = 1; int y = 2;"
+    assert rs._code_only("a //c\nb") != rs._code_only("a b c")
