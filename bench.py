@@ -184,6 +184,22 @@ def main():
         except (OSError, ValueError):
             traffic = None
 
+    # cold steps: a 512 MiB buffer is written before each step (outside the timed
+    # events) so that the 256 MB last-level cache holds none of the step's data
+    cold_steps = min(args.steps, 10)
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(cold_steps):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cold_ms = float(np.median(cold))
+
     if args.copy_mib > 0:
         # an elementwise kernel (not a DMA copy, which the counters would not see):
         # reads and writes exactly copy_mib MiB
@@ -216,6 +232,8 @@ def main():
         "path_roofline": {"algorithmic_GBps": round(path_gbs, 1), "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
                           "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         "stages_ms": {s: round(v[0], 5) for s, v in stages.items()},
+        "cold": {"ms_per_step": round(cold_ms, 5), "tokens_per_s": round(B * T / (cold_ms * 1e-3), 1),
+                 "steps": cold_steps, "note": "median over steps each preceded by a 512 MiB write"},
         "gdn_per_dit_forward_ms": {"x20_layers": round(20 * ms, 3), "x15_gdn_layers": round(15 * ms, 3)},
     }
     if not args.no_cpu_baseline:

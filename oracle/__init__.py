@@ -1,4 +1,5 @@
-"""CPU oracle for the frame-wise Gated DeltaNet forward -- TEST INFRASTRUCTURE.
+"""CPU oracles for the frame-wise Gated DeltaNet forward and the streaming
+attention block -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import anything from this package.  The HIP library and its
@@ -14,6 +15,8 @@ Contents
                 from it; pins the algebra the GPU path uses and exposes its
                 per-chunk intermediates.
 ``exact``       exact-rational brute force of the product form on tiny inputs.
+``attention``   fp64 softmax attention of the streaming chunk-causal attention
+                block (sink frames + rolling cache of past blocks).
 
 Every function pins to something other than itself in ``tests/test_oracle_*``:
 hand-derived values, closed forms, exact rationals, limits and invariants.
