@@ -1,4 +1,5 @@
-"""ctypes declarations of the C ABI in include/sanawm_gdn.h (argument marshalling only)."""
+"""ctypes declarations of the C ABI in include/sanawm_gdn.h and include/sanawm_attn.h
+(argument marshalling only)."""
 from __future__ import annotations
 
 import ctypes
@@ -15,12 +16,20 @@ EXPORTED = ("gdn_chunk_len", "gdn_workspace_bytes", "gdn_fwd", "gdn_chunk_step",
             "gdn_profile_begin", "gdn_profile_end", "gdn_profile_stage_name",
             "gdn_status_string", "gdn_last_error", "gdn_version")
 NUM_STAGES = 4
+# every symbol include/sanawm_attn.h declares
+EXPORTED_ATTN = ("attn_cache_bytes", "attn_block_fwd")
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class AttnProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("frame_tokens", ctypes.c_int32), ("frames_per_block", ctypes.c_int32),
+                ("cached_blocks", ctypes.c_int32), ("sink_frames", ctypes.c_int32), ("o_dtype", ctypes.c_int32)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -64,5 +73,10 @@ def load():
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
+    A = ctypes.POINTER(AttnProblem)
+    lib.attn_cache_bytes.restype = ctypes.c_int
+    lib.attn_cache_bytes.argtypes = [A, ctypes.POINTER(sz)]
+    lib.attn_block_fwd.restype = ctypes.c_int
+    lib.attn_block_fwd.argtypes = [A, ctypes.c_int32, vp, vp, vp, vp, sz, vp, vp]
     _lib = lib
     return lib

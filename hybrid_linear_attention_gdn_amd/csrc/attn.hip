@@ -1,0 +1,393 @@
+// Streaming chunk-causal softmax attention block (see include/sanawm_attn.h).
+//
+// Two kernels per call:
+//   stage: writes the block's k and v into its ring slot of the cache (and
+//          its sink frames, if any, into the sink slot): K as rows of 112 bf16,
+//          V transposed (per slot, 112 rows of the slot's keys), so that the
+//          attention kernel's V operand is a run of consecutive keys.
+//   attn:  flash attention over the context segments (sink slot, the ring
+//          slots of the cached blocks, the current block's slot), one
+//          workgroup per (b, h, 128 queries): four compute waves (32 queries
+//          each) and two copy waves that bring 64-key tiles of K and V^T into
+//          LDS with buffer-to-LDS loads, double-buffered, one barrier per tile.
+//
+// The compute waves work in transposed form.  S^T = K Q^T puts one query per
+// lane (the accumulator column), so the running max and sum of a query stay
+// in its lanes; its four 16-key row groups sit in lane groups g = 0..3 and
+// are combined with two lane exchanges per tile.  O^T = V^T P^T then takes P^T
+// straight from the S^T accumulators: two 16-key accumulator tiles are one
+// 32-deep B operand in the "pair" k-order (slots 0-3: keys 4g..4g+3 of the
+// first tile, slots 4-7: the same of the second), and V^T fragments are read
+// in that order.  Each O^T accumulator lane again holds one query, so the
+// per-tile rescale by e^(m_old - m_new) is lane-local.
+//
+// Precision: q, k, v enter the matrix cores as the exact bf16 inputs; scores
+// and the softmax are fp32; P is rounded to bf16 (relative 2^-9 per weight)
+// for the P V product, accumulated in fp32.
+#include "gdn_mfma_common.h"
+
+#include <algorithm>
+
+namespace gdn {
+namespace attn {
+namespace {
+
+using mfma::F16;
+using mfma::F32;
+using mfma::f32x4;
+using mfma::mma;
+using mfma::zero4;
+
+constexpr int D = 112;
+constexpr int KT = 64;                      // keys per tile
+constexpr int kComputeWaves = 4;
+constexpr int QW = 32;                      // queries per compute wave (two 16-query tiles)
+constexpr int QB = QW * kComputeWaves;      // 128 queries per workgroup
+constexpr int kThreads = (kComputeWaves + 2) * 64;
+constexpr int kKRow = 256;                  // bytes per staged K row (224 used)
+constexpr int kKTile = KT * kKRow;          // 16 KB
+constexpr int kVTile = D * KT * 2;          // 14 KB: V^T rows of 64 keys (128 B)
+constexpr int kBuf = kKTile + kVTile;       // 30 KB
+constexpr int kLds = 2 * kBuf;              // 60 KB: two workgroups per CU
+constexpr int kKInstr = kKTile / 1024;      // 16 copies of 1 KB per K tile
+constexpr int kVInstr = kVTile / 1024;      // 14 per V^T tile
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), 0x00020000);
+}
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, int(off), 0, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void bare_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void compute_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
+// stage: one workgroup (256 threads) per (b, h, 64 tokens of the block)
+__global__ __launch_bounds__(256) void stage_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                                    char *__restrict__ cache, int Lb, int H, int units,
+                                                    size_t bh_bytes, int total_keys, int ring_koff, int sink_koff,
+                                                    int sink_keys, int sink_len, int block_tok0) {
+  __shared__ uint16_t vs[KT][D + 2];  // the tile's V rows (row pitch 228 B)
+  const int tiles = (Lb + KT - 1) / KT;
+  const int u = blockIdx.x / tiles, t0 = (blockIdx.x % tiles) * KT;
+  if (u >= units) return;
+  const int b = u / H, h = u % H;
+  const int n = min(KT, Lb - t0);
+  const int tid = threadIdx.x;
+  char *base = cache + size_t(u) * bh_bytes;
+  const size_t rowstride = size_t(H) * D;
+  const uint16_t *ksrc = k + (size_t(b) * Lb + t0) * rowstride + size_t(h) * D;
+  const uint16_t *vsrc = v + (size_t(b) * Lb + t0) * rowstride + size_t(h) * D;
+  // tokens of this block that are also sink tokens: block-local t < sink_len
+  for (int idx = tid; idx < n * 14; idx += 256) {
+    const int t = idx / 14, p = idx % 14;
+    const uint4 kx = *reinterpret_cast<const uint4 *>(ksrc + size_t(t) * rowstride + 8 * p);
+    *reinterpret_cast<uint4 *>(base + size_t(ring_koff + t0 + t) * (D * 2) + 16 * p) = kx;
+    if (t0 + t < sink_len)
+      *reinterpret_cast<uint4 *>(base + size_t(sink_koff + block_tok0 + t0 + t) * (D * 2) + 16 * p) = kx;
+    const uint4 vx = *reinterpret_cast<const uint4 *>(vsrc + size_t(t) * rowstride + 8 * p);
+    const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vs[t][8 * p + j] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
+  }
+  __syncthreads();
+  // V^T of a slot: row d holds the slot's keys; this tile fills keys t0 .. t0 + n - 1
+  auto put_vt = [&](int slot_koff, int slot_len, int key0, int limit) {
+    uint16_t *vt = reinterpret_cast<uint16_t *>(base + size_t(total_keys) * (D * 2) + size_t(slot_koff) * (D * 2));
+    for (int idx = tid; idx < D * n; idx += 256) {
+      const int d = idx / n, t = idx % n;
+      if (t < limit) vt[size_t(d) * slot_len + key0 + t] = vs[t][d];
+    }
+  };
+  put_vt(ring_koff, Lb, t0, n);
+  if (t0 < sink_len) put_vt(sink_koff, sink_keys, block_tok0 + t0, min(n, sink_len - t0));
+}
+
+// ---------------------------------------------------------------------------
+// attention: context segments, each a run of keys in one cache slot
+struct Segs {
+  int n;              // segments (1 .. 4)
+  int koff[4];        // first key of the segment's slot in the per-(b, h) key space
+  int len[4];         // keys of the segment (a prefix of the slot)
+  int slot_len[4];    // keys of the slot (row length of its V^T)
+  int tiles0[5];      // tiles before segment s; tiles0[n] = all tiles
+};
+
+__device__ __forceinline__ void tile_of(const Segs &sg, int j, int &s, int &key0, int &nvalid) {
+  s = 0;
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (i < sg.n && j >= sg.tiles0[i]) s = i;
+  key0 = KT * (j - sg.tiles0[s]);
+  nvalid = min(KT, sg.len[s] - key0);
+}
+
+// Copy wave L (0: K tile, 1: V^T tile): tile j into buffer j & 1.
+template <int L>
+__device__ __forceinline__ void copy_role(const char *__restrict__ bh, int total_keys, const Segs &sg, char *lds) {
+  const int lane = threadIdx.x & 63;
+  const int ntiles = sg.tiles0[sg.n];
+  auto issue = [&](int j) {
+    int s, key0, nvalid;
+    tile_of(sg, j, s, key0, nvalid);
+    char *buf = lds + (j & 1) * kBuf;
+    if constexpr (L == 0) {
+      // key r = 4i + lane / 16 of the tile, LDS slot lane % 16 holds piece slot ^ (r & 15)
+      const auto rs = make_rsrc(bh + size_t(sg.koff[s] + key0) * (D * 2), uint32_t(nvalid) * (D * 2));
+#pragma unroll
+      for (int i = 0; i < kKInstr; ++i) {
+        const int r = 4 * i + (lane >> 4), p = (lane & 15) ^ (r & 15);
+        copy16(rs, buf + 1024 * i, p < 14 ? uint32_t(r) * (D * 2) + 16u * p : kOutOfRange);
+      }
+    } else {
+      // V^T row d = 8i + lane / 8, LDS slot lane % 8 holds keys 8 (slot ^ (d & 7)) .. + 7;
+      // keys past the slot read as zero, keys past the segment are masked
+      const char *vt = bh + size_t(total_keys) * (D * 2) + size_t(sg.koff[s]) * (D * 2);
+      const auto rs = make_rsrc(vt, uint32_t(sg.slot_len[s]) * (D * 2));
+#pragma unroll
+      for (int i = 0; i < kVInstr; ++i) {
+        const int d = 8 * i + (lane >> 3), p = (lane & 7) ^ (d & 7);
+        copy16(rs, buf + kKTile + 1024 * i, (uint32_t(d) * sg.slot_len[s] + key0 + 8 * p) * 2u);
+      }
+    }
+  };
+  if (ntiles > 0) issue(0);
+  for (int j = 0; j < ntiles; ++j) {
+    wait_vm<0>();    // tile j landed
+    bare_barrier();  // compute waves are done with buffer (j + 1) & 1
+    if (j + 1 < ntiles) issue(j + 1);
+  }
+}
+
+template <int W, bool kOutBf16>
+__device__ __forceinline__ void compute_role(const uint16_t *__restrict__ q, void *__restrict__ o, int Lb, int H,
+                                             int b, int h, int qt, const Segs &sg, char *lds) {
+  const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+  const size_t rowstride = size_t(H) * D;
+  const int q0 = qt * QB + W * QW;  // first query of this wave
+  // Q^T fragments (B operand of S^T = K Q^T, natural k-order): lane (ln, g) of
+  // query tile qq holds q[q0 + 16 qq + ln][32 kb + 8 g .. + 7], tail [96 + 4 g .. + 3]
+  F32 qf[2][3];
+  F16 qtl[2];
+  {
+    const auto rq = make_rsrc(q + size_t(b) * Lb * rowstride, uint32_t(Lb) * uint32_t(rowstride) * 2u);
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const uint32_t row = (uint32_t(q0 + 16 * qq + ln) * uint32_t(rowstride) + uint32_t(h) * D) * 2u;
+      const uint32_t rowo = q0 + 16 * qq + ln < Lb ? row : kOutOfRange;
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+            rq, int(rowo == kOutOfRange ? kOutOfRange : rowo + 64u * kb + 16u * lg), 0, 0);
+        qf[qq][kb] = F32{{x.x, x.y, x.z, x.w}};
+      }
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(
+          rq, int(rowo == kOutOfRange ? kOutOfRange : rowo + 192u + 8u * lg), 0, 0);
+      qtl[qq] = F16{{x.x, x.y}};
+    }
+  }
+  // scores in the log2 domain: q . k / sqrt(d) * log2(e)
+  const float scale2 = 1.44269504088896341f / __builtin_sqrtf(float(D));
+  f32x4 oacc[7][2];
+#pragma unroll
+  for (int dt = 0; dt < 7; ++dt) oacc[dt][0] = oacc[dt][1] = zero4();
+  float m[2] = {-__builtin_inff(), -__builtin_inff()}, l[2] = {0.f, 0.f};
+  const int ntiles = sg.tiles0[sg.n];
+  for (int j = 0; j < ntiles; ++j) {
+    int s, key0, nvalid;
+    tile_of(sg, j, s, key0, nvalid);
+    compute_barrier();  // tile j is in buffer j & 1
+    const char *kb_ = lds + (j & 1) * kBuf;
+    const char *vb_ = kb_ + kKTile;
+    // ---- S^T = K Q^T: key tile t (16 keys), query tile qq
+    f32x4 sacc[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const char *rowp = kb_ + (16 * t + ln) * kKRow;
+      F32 kf[3];
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(rowp + 16 * ((4 * kb + lg) ^ ln));
+        kf[kb] = F32{{x.x, x.y, x.z, x.w}};
+      }
+      const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 16 * ((12 + (lg >> 1)) ^ ln) + 8 * (lg & 1));
+      const F16 kt{{x2.x, x2.y}};
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 3; ++kb) acc = mma(kf[kb], qf[qq][kb], acc);
+        sacc[t][qq] = mma(kt, qtl[qq], acc);
+      }
+    }
+    // ---- online softmax per query (one query per lane column)
+    F32 pf[2][2];  // P^T B operands [qq][key pair]
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      float sv[4][4];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = 16 * t + 4 * lg + e < nvalid;
+          sv[t][e] = ok ? sacc[t][qq][e] * scale2 : -__builtin_inff();
+          mx = fmaxf(mx, sv[t][e]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[qq], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[qq] - mnew);
+      m[qq] = mnew;
+      float ps = 0.f;
+      float pv[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[t][e] = __builtin_amdgcn_exp2f(sv[t][e] - mnew);
+          ps += pv[t][e];
+        }
+      l[qq] = l[qq] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < 7; ++dt) oacc[dt][qq] = oacc[dt][qq] * alpha;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        pf[qq][pp] = F32{{pack_bf16x2(pv[2 * pp][0], pv[2 * pp][1]), pack_bf16x2(pv[2 * pp][2], pv[2 * pp][3]),
+                          pack_bf16x2(pv[2 * pp + 1][0], pv[2 * pp + 1][1]),
+                          pack_bf16x2(pv[2 * pp + 1][2], pv[2 * pp + 1][3])}};
+    }
+    // ---- O^T += V^T P^T: d tile dt, key pair pp (keys 32 pp .. 32 pp + 31)
+#pragma unroll
+    for (int dt = 0; dt < 7; ++dt) {
+      const int d = 16 * dt + ln;
+      const char *vrow = vb_ + d * (KT * 2);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int p0 = 4 * pp + (lg >> 1), p1 = p0 + 2;
+        const uint2 a0 = *reinterpret_cast<const uint2 *>(vrow + 16 * (p0 ^ (d & 7)) + 8 * (lg & 1));
+        const uint2 a1 = *reinterpret_cast<const uint2 *>(vrow + 16 * (p1 ^ (d & 7)) + 8 * (lg & 1));
+        const F32 vf{{a0.x, a0.y, a1.x, a1.y}};
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) oacc[dt][qq] = mma(vf, pf[qq][pp], oacc[dt][qq]);
+      }
+    }
+  }
+  // ---- normalise and store: lane (ln, g) of query tile qq holds d = 16 dt + 4 g .. + 3
+  const auto ro = make_rsrc(static_cast<char *>(o) + size_t(b) * Lb * rowstride * (kOutBf16 ? 2 : 4),
+                            uint32_t(Lb) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    float lt = l[qq] + __shfl_xor(l[qq], 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.f / lt;
+    const int qi = q0 + 16 * qq + ln;
+    const uint32_t row = qi < Lb ? uint32_t(qi) * uint32_t(rowstride) + uint32_t(h) * D : kOutOfRange;
+#pragma unroll
+    for (int dt = 0; dt < 7; ++dt) {
+      const f32x4 w = oacc[dt][qq] * inv;
+      const uint32_t el = row == kOutOfRange ? kOutOfRange : row + 16u * dt + 4u * lg;
+      if constexpr (kOutBf16) {
+        const u32x2_t pk = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(pk, ro, int(el == kOutOfRange ? kOutOfRange : el * 2u), 0, 0);
+      } else {
+        const u32x4_t pk = {__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]),
+                            __float_as_uint(w[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(pk, ro, int(el == kOutOfRange ? kOutOfRange : el * 4u), 0, 0);
+      }
+    }
+  }
+}
+
+template <bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void attn_kernel(const uint16_t *__restrict__ q,
+                                                        const char *__restrict__ cache, void *__restrict__ o,
+                                                        int Lb, int H, int units, int nqt, size_t bh_bytes,
+                                                        int total_keys, Segs sg) {
+  extern __shared__ __align__(16) char lds[];
+  // the query tiles of one (b, h) run on one XCD (workgroup i on XCD i % 8), so
+  // its K and V^T are fetched into that L2 once
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int u = xcd + 8 * (slot / nqt), qt = slot % nqt;
+  if (u >= units) return;
+  const int b = u / H, h = u % H;
+  const char *bh = cache + size_t(u) * bh_bytes;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  switch (wave) {
+    case 0: compute_role<0, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
+    case 1: compute_role<1, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
+    case 2: compute_role<2, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
+    case 3: compute_role<3, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
+    case 4: copy_role<0>(bh, total_keys, sg, lds); break;
+    default: copy_role<1>(bh, total_keys, sg, lds); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnPlan &p, int block, const void *q, const void *k, const void *v, void *cache,
+                       void *o, hipStream_t stream) {
+  const int units = p.B * p.H;
+  const int ring = block % (p.C + 1);
+  const int ring_koff = p.Ls + ring * p.Lb;
+  const int block_tok0 = block * p.Lb;                           // first token of the block in the stream
+  const int sink_len = std::max(0, std::min(p.Lb, p.Ls - block_tok0));  // block tokens that are sink tokens
+  char *c = static_cast<char *>(cache);
+  {
+    const unsigned grid = unsigned(units) * unsigned((p.Lb + KT - 1) / KT);
+    stage_kernel<<<dim3(grid), dim3(256), 0, stream>>>(static_cast<const uint16_t *>(k),
+                                                       static_cast<const uint16_t *>(v), c, p.Lb, p.H, units,
+                                                       p.bh_bytes, p.total_keys, ring_koff, 0, p.Ls, sink_len,
+                                                       block_tok0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // context segments: uncovered sink frames, the cached blocks (oldest first), the current block
+  Segs sg{};
+  const int first_block = std::max(0, block - p.C);
+  const int sink_uncovered = std::min(p.Ls, first_block * p.Lb);  // sink keys below the window
+  auto add = [&](int koff, int len, int slot_len) {
+    sg.koff[sg.n] = koff;
+    sg.len[sg.n] = len;
+    sg.slot_len[sg.n] = slot_len;
+    sg.tiles0[sg.n + 1] = sg.tiles0[sg.n] + (len + KT - 1) / KT;
+    ++sg.n;
+  };
+  if (sink_uncovered > 0) add(0, sink_uncovered, p.Ls);
+  for (int nb = first_block; nb <= block; ++nb) add(p.Ls + (nb % (p.C + 1)) * p.Lb, p.Lb, p.Lb);
+  static const hipError_t lds0 = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<false>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  static const hipError_t lds1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<true>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (lds0 != hipSuccess) return lds0;
+  if (lds1 != hipSuccess) return lds1;
+  const int nqt = (p.Lb + QB - 1) / QB;
+  const unsigned grid = 8u * unsigned(nqt) * unsigned((units + 7) / 8);
+  if (p.o_bf16)
+    attn_kernel<true><<<dim3(grid), dim3(kThreads), kLds, stream>>>(static_cast<const uint16_t *>(q), c, o, p.Lb,
+                                                                   p.H, units, nqt, p.bh_bytes, p.total_keys, sg);
+  else
+    attn_kernel<false><<<dim3(grid), dim3(kThreads), kLds, stream>>>(static_cast<const uint16_t *>(q), c, o, p.Lb,
+                                                                    p.H, units, nqt, p.bh_bytes, p.total_keys, sg);
+  return hipGetLastError();
+}
+
+}  // namespace attn
+}  // namespace gdn

@@ -4,6 +4,7 @@
 // enqueue work on the caller's stream and never synchronise, allocate or free
 // device memory.
 #include "sanawm_gdn.h"
+#include "sanawm_attn.h"
 
 #include <atomic>
 #include <cstdarg>
@@ -305,6 +306,78 @@ gdn_status_t gdn_profile_end(float *ms, int32_t *calls, int32_t n) {
     if (calls) calls[s] = 0;
   }
   return st;
+}
+
+// ---- streaming attention block (include/sanawm_attn.h) ----
+static gdn_status_t attn_plan(const attn_problem_t *p, gdn::AttnPlan &P) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem descriptor is NULL");
+  if (p->batch < 1 || p->num_heads < 1 || p->frame_tokens < 1 || p->frames_per_block < 1 || p->cached_blocks < 0 ||
+      p->sink_frames < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "bad stream geometry: batch=%d heads=%d frame_tokens=%d "
+                "frames_per_block=%d cached_blocks=%d sink_frames=%d", p->batch, p->num_heads, p->frame_tokens,
+                p->frames_per_block, p->cached_blocks, p->sink_frames);
+  if (p->o_dtype != GDN_F32 && p->o_dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown output dtype %d", p->o_dtype);
+  if (p->head_dim != gdn::kMfmaDim)
+    return fail(GDN_ERR_UNSUPPORTED, "the attention block takes head_dim %d (got %d)", gdn::kMfmaDim, p->head_dim);
+  const long long lb = (long long)p->frame_tokens * p->frames_per_block;
+  const long long ls = (long long)p->frame_tokens * p->sink_frames;
+  const long long keys = ls + (long long)(p->cached_blocks + 1) * lb;
+  const long long rowbytes = (long long)p->num_heads * p->head_dim * 4;
+  // buffer offsets inside the kernels are 32-bit: per (b, h) cache slice, per-batch q and o
+  if (keys * 448 >= (1LL << 31) || lb * rowbytes >= (1LL << 31) || (long long)p->batch * p->num_heads > (1 << 24))
+    return fail(GDN_ERR_UNSUPPORTED, "attention block too large (block tokens %lld, cached keys %lld)", lb, keys);
+  P.B = p->batch;
+  P.H = p->num_heads;
+  P.ft = p->frame_tokens;
+  P.fpb = p->frames_per_block;
+  P.C = p->cached_blocks;
+  P.S = p->sink_frames;
+  P.Lb = int(lb);
+  P.Ls = int(ls);
+  P.total_keys = int(keys);
+  P.bh_bytes = align_up(size_t(keys) * 448);
+  P.o_bf16 = p->o_dtype == GDN_BF16;
+  return GDN_OK;
+}
+
+gdn_status_t attn_cache_bytes(const attn_problem_t *p, size_t *bytes) {
+  if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = 0;
+  gdn::AttnPlan P;
+  const gdn_status_t st = attn_plan(p, P);
+  if (st != GDN_OK) return st;
+  size_t total;
+  if (!mul_ok(size_t(P.B) * size_t(P.H), P.bh_bytes, &total)) return fail(GDN_ERR_UNSUPPORTED, "cache too large");
+  *bytes = total;
+  return GDN_OK;
+}
+
+gdn_status_t attn_block_fwd(const attn_problem_t *p, int32_t block, const void *q, const void *k, const void *v,
+                            void *cache, size_t cache_bytes, void *o, void *hip_stream) {
+  gdn::AttnPlan P;
+  gdn_status_t st = attn_plan(p, P);
+  if (st != GDN_OK) return st;
+  if (block < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "block index %d is negative", block);
+  if ((long long)block * P.Lb >= (1LL << 31))
+    return fail(GDN_ERR_UNSUPPORTED, "block index %d too large", block);
+  const struct {
+    const void *ptr;
+    const char *name;
+  } need[] = {{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {cache, "cache"}};
+  for (const auto &n : need) {
+    if (!n.ptr) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is NULL", n.name);
+    if (reinterpret_cast<uintptr_t>(n.ptr) % 16) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n.name);
+  }
+  if (reinterpret_cast<uintptr_t>(cache) % kAlign)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "cache is not %zu-byte aligned", kAlign);
+  size_t need_bytes = 0;
+  if ((st = attn_cache_bytes(p, &need_bytes)) != GDN_OK) return st;
+  if (cache_bytes < need_bytes)
+    return fail(GDN_ERR_WORKSPACE, "cache too small: %zu < %zu bytes", cache_bytes, need_bytes);
+  const hipError_t e = gdn::attn::launch_attn(P, block, q, k, v, cache, o, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
 }
 
 const char *gdn_profile_stage_name(int32_t stage) {

@@ -54,6 +54,20 @@ hipError_t launch_portable(const Plan &p, const Args &a);
 hipError_t launch_mfma(const Plan &p, const Args &a);
 hipError_t launch_state_passthrough(const Plan &p, const Args &a);
 
+// Streaming attention block (attn.hip): the validated geometry of one call.
+struct AttnPlan {
+  int B = 0, H = 0;
+  int ft = 0, fpb = 0, C = 0, S = 0;  // frame tokens, frames per block, cached blocks, sink frames
+  int Lb = 0, Ls = 0;                 // tokens per block, sink tokens
+  int total_keys = 0;                 // keys per (b, h) in the cache: sink slot + C + 1 ring slots
+  size_t bh_bytes = 0;                // cache bytes per (b, h)
+  bool o_bf16 = false;
+};
+namespace attn {
+hipError_t launch_attn(const AttnPlan &p, int block, const void *q, const void *k, const void *v, void *cache,
+                       void *o, hipStream_t stream);
+}
+
 // bytes needed by the MFMA path's own intermediates (beyond the prep scalars)
 size_t mfma_chunk_bytes_M();
 size_t mfma_chunk_bytes_P();

@@ -156,3 +156,31 @@ def make_inputs(w: Workload, *, seed: int | None = None, seq_len: int | None = N
         inp.q_bits, inp.k_bits, inp.v_bits = (round_bf16_bits(a) for a in (q, k, v))
         inp.q, inp.k, inp.v = (bf16_bits_to_f32(bb) for bb in (inp.q_bits, inp.k_bits, inp.v_bits))
     return inp
+
+
+@dataclass
+class AttnStream:
+    """q, k, v of a whole stream of attention blocks: [B, blocks * L_b, H, d]
+    bf16 patterns (``*_bits``) and their fp32 values."""
+    q_bits: np.ndarray
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    block_tokens: int
+
+
+def make_attn_stream(B: int, H: int, frame_tokens: int, frames_per_block: int, blocks: int, seed: int,
+                     d: int = HEAD_DIM) -> AttnStream:
+    """Seeded inputs of the streaming attention block: q, k, v ~ N(0, 1), drawn
+    per batch row in the order q, k, v ([T, H, d] each), rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    T = blocks * frames_per_block * frame_tokens
+    arrs = [np.empty((B, T, H, d), np.float32) for _ in range(3)]
+    for b in range(B):
+        for a in arrs:
+            a[b] = rng.standard_normal((T, H, d), dtype=np.float32)
+    bits = [round_bf16_bits(a) for a in arrs]
+    vals = [bf16_bits_to_f32(x) for x in bits]
+    return AttnStream(*bits, *vals, block_tokens=frames_per_block * frame_tokens)

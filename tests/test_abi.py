@@ -135,3 +135,32 @@ def test_unsupported_head_dim_on_mfma_path(lib):
         assert st == L.GDN_ERR_UNSUPPORTED
     else:
         assert st == L.GDN_OK
+
+
+ATTN_HEADER = os.path.join(ROOT, "include", "sanawm_attn.h")
+
+
+def test_attention_exports_and_host_checks(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(ATTN_HEADER).read(), flags=re.S)
+    decl = sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    assert set(decl) == set(L.EXPORTED_ATTN), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+    # the page geometry: 880-token frames, 3 per block, 2 cached blocks, 1 sink frame
+    p = L.AttnProblem(1, 20, 112, 880, 3, 2, 1, L.GDN_F32)
+    n = ctypes.c_size_t(0)
+    assert lib.attn_cache_bytes(ctypes.byref(p), ctypes.byref(n)) == L.GDN_OK
+    keys = 880 + 3 * 2640
+    assert n.value == 20 * ((keys * 448 + 255) // 256 * 256)
+    bad = L.AttnProblem(1, 20, 128, 880, 3, 2, 1, L.GDN_F32)
+    assert lib.attn_cache_bytes(ctypes.byref(bad), ctypes.byref(n)) == L.GDN_ERR_UNSUPPORTED and n.value == 0
+    bad = L.AttnProblem(1, 20, 112, 880, 0, 2, 1, L.GDN_F32)
+    assert lib.attn_cache_bytes(ctypes.byref(bad), ctypes.byref(n)) == L.GDN_ERR_INVALID_ARGUMENT
+    # argument errors come back before any device call
+    fake = ctypes.c_void_p(256)
+    assert lib.attn_block_fwd(ctypes.byref(p), -1, fake, fake, fake, fake, 1 << 40, fake, None) == \
+        L.GDN_ERR_INVALID_ARGUMENT
+    assert lib.attn_block_fwd(ctypes.byref(p), 0, None, fake, fake, fake, 1 << 40, fake, None) == \
+        L.GDN_ERR_INVALID_ARGUMENT
+    assert b"q is NULL" in lib.gdn_last_error()
+    assert lib.attn_block_fwd(ctypes.byref(p), 0, fake, fake, fake, fake, 16, fake, None) == L.GDN_ERR_WORKSPACE
