@@ -76,6 +76,77 @@ def cpu_baseline(w, max_tokens: int, min_seconds: float):
             "seconds": round(dt, 3)}
 
 
+def attn_bench(args):
+    """The streaming attention block (include/sanawm_attn.h) at the page geometry:
+    880-token frames, 3 frames per block, 2 cached blocks, 1 sink frame, 20
+    heads x 112.  Blocks 0..3 fill the cache; the timed step re-runs block 3
+    (stage + attention: 2,640 queries over 8,800 keys), the steady state of a
+    stream.  Prints one JSON line of its own."""
+    import numpy as np
+    import torch
+
+    from hybrid_linear_attention_gdn_amd import attn
+    from hybrid_linear_attention_gdn_amd.inputs import make_attn_stream
+
+    B, H, ft, fpb, C, S = 1, 20, 880, 3, 2, 1
+    blocks = 4
+    dev = torch.device("cuda:0")
+    s = make_attn_stream(B, H, ft, fpb, blocks, 400)
+    up = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    Lb = s.block_tokens
+    q, k, v = (up(x) for x in (s.q_bits, s.k_bits, s.v_bits))
+    o_dtype = torch.float32 if args.o_dtype == "fp32" else torch.bfloat16
+    p = attn.problem(B, H, ft, fpb, C, S, o_dtype)
+    cache = attn.new_cache(p)
+    parts = [tuple(t[:, n * Lb:(n + 1) * Lb].contiguous() for t in (q, k, v)) for n in range(blocks)]
+    o = torch.empty((B, Lb, H, 112), dtype=o_dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for n in range(blocks):
+        attn.block_fwd(p, n, *parts[n], cache, o, stream)
+    step = lambda: attn.block_fwd(p, blocks - 1, *parts[-1], cache, o, stream)  # noqa: E731
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    keys = 10 * ft
+    flops = 4.0 * B * H * Lb * keys * 112  # Q K^T and P V, 2 flops per multiply-add
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "streaming attention block TFLOP/s (2,640 queries x 8,800 keys, 20h x 112d, bf16) on 1 MI355X",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) q/k/v)",
+        "config": {"workload": "attn_block: block 3 of a stream (sink frame + 2 cached blocks + current block)",
+                   "batch": B, "heads": H, "head_dim": 112, "queries": Lb, "keys": keys, "o_dtype": args.o_dtype},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "tokens_per_s": round(B * Lb / (ms * 1e-3), 1),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import attention as A
+        rows = np.concatenate([np.arange(f * ft, (f + 1) * ft) for f in A.context_frames(blocks - 1, fpb, C, S)])
+        runs, dt, heads = 0, 0.0, 0
+        while runs == 0 or dt < args.cpu_seconds:
+            h = runs % H
+            t0 = time.perf_counter()
+            A.attention(s.q[0, (blocks - 1) * Lb:blocks * Lb, h].astype(np.float64), s.k[0, rows, h], s.v[0, rows, h])
+            dt += time.perf_counter() - t0
+            runs += 1
+            heads += 1
+        cpu_flops = 4.0 * heads * Lb * keys * 112
+        out["cpu_baseline"] = {"value": round(cpu_flops / dt / 1e12, 5), "unit": "TFLOP/s",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+                               "kind": "oracle", "sample": f"{heads} (head, block) attentions of 2,640 x 8,800 in "
+                                                           f"fp64 numpy, {dt:.1f} s wall"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +158,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30, help="tokens of the oracle's CPU sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn", action="store_true", help="time the streaming attention block instead of the GDN layer")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, to calibrate memory counters under a profiler)")
@@ -97,6 +169,9 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only: the GDN forward's (batch, head) units "
                                    "are independent and would shard without communication; run --gpus 1"}))
         sys.exit(2)
+    if args.attn:
+        attn_bench(args)
+        return
 
     import numpy as np
     import torch

@@ -7,9 +7,13 @@
 //          attention kernel's V operand is a run of consecutive keys.
 //   attn:  flash attention over the context segments (sink slot, the ring
 //          slots of the cached blocks, the current block's slot), one
-//          workgroup per (b, h, 128 queries): four compute waves (32 queries
-//          each) and two copy waves that bring 64-key tiles of K and V^T into
-//          LDS with buffer-to-LDS loads, double-buffered, one barrier per tile.
+//          workgroup per (b, h, 224 queries): seven compute waves (32 queries
+//          each, two per SIMD) and a copy wave that brings 64-key tiles of K
+//          and V^T into LDS with buffer-to-LDS loads, one barrier per tile.  The compute
+//          waves are software-pipelined: step j forms S^T of tile j while it
+//          accumulates P V of tile j - 1 (independent products), then takes
+//          the softmax of tile j.  K tiles therefore run one tile ahead of V^T
+//          tiles; each kind is double-buffered.
 //
 // The compute waves work in transposed form.  S^T = K Q^T puts one query per
 // lane (the accumulator column), so the running max and sum of a query stay
@@ -20,6 +24,18 @@
 // first tile, slots 4-7: the same of the second), and V^T fragments are read
 // in that order.  Each O^T accumulator lane again holds one query, so the
 // per-tile rescale by e^(m_old - m_new) is lane-local.
+//
+// V^T layout: within every 32-key group of a slot, position 8g + s holds key
+// 4g + s (s < 4) or 16 + 4g + (s - 4) (s >= 4), so that the eight keys a lane
+// needs in the pair order are one 16-byte read.  Slot rows are padded to a
+// multiple of 64 keys, the padding zero-filled by the stage kernel.
+//
+// Running maximum: each tile's maximum of a query is reduced over its four
+// lane groups with two lane swaps (v_permlane16_swap / v_permlane32_swap,
+// register-only), so P is taken against the exact running maximum and the
+// query's largest weight is exactly 1 (a stale maximum would leave that
+// dominant weight to bf16 rounding).  The accumulators are rescaled only when
+// some query of the wave has a new maximum (a wave-uniform branch).
 //
 // Precision: q, k, v enter the matrix cores as the exact bf16 inputs; scores
 // and the softmax are fp32; P is rounded to bf16 (relative 2^-9 per weight)
@@ -40,15 +56,15 @@ using mfma::zero4;
 
 constexpr int D = 112;
 constexpr int KT = 64;                      // keys per tile
-constexpr int kComputeWaves = 4;
+constexpr int kComputeWaves = 7;            // two per SIMD (one SIMD shares with the copy wave)
 constexpr int QW = 32;                      // queries per compute wave (two 16-query tiles)
-constexpr int QB = QW * kComputeWaves;      // 128 queries per workgroup
-constexpr int kThreads = (kComputeWaves + 2) * 64;
+constexpr int QB = QW * kComputeWaves;      // 224 queries per workgroup
+constexpr int kThreads = (kComputeWaves + 1) * 64;
 constexpr int kKRow = 256;                  // bytes per staged K row (224 used)
 constexpr int kKTile = KT * kKRow;          // 16 KB
 constexpr int kVTile = D * KT * 2;          // 14 KB: V^T rows of 64 keys (128 B)
-constexpr int kBuf = kKTile + kVTile;       // 30 KB
-constexpr int kLds = 2 * kBuf;              // 60 KB: two workgroups per CU
+constexpr int kLdsV = 2 * kKTile;           // two K tile buffers, then two V^T tile buffers
+constexpr int kLds = kLdsV + 2 * kVTile;    // 60 KB
 constexpr int kKInstr = kKTile / 1024;      // 16 copies of 1 KB per K tile
 constexpr int kVInstr = kVTile / 1024;      // 14 per V^T tile
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;
@@ -67,6 +83,20 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of a column)
+__device__ __forceinline__ float lanes4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lanes4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ void bare_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
@@ -80,10 +110,17 @@ __device__ __forceinline__ void compute_barrier() {
 
 // ---------------------------------------------------------------------------
 // stage: one workgroup (256 threads) per (b, h, 64 tokens of the block)
+// position of key kk of a slot in its V^T rows (a permutation inside each 32-key group)
+__device__ __forceinline__ int vt_pos(int kk) {
+  const int g = kk & 31, hi = g >> 4, r = g & 15;
+  return (kk & ~31) + 8 * (r >> 2) + 4 * hi + (r & 3);
+}
+
 __global__ __launch_bounds__(256) void stage_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
                                                     char *__restrict__ cache, int Lb, int H, int units,
-                                                    size_t bh_bytes, int total_keys, int ring_koff, int sink_koff,
-                                                    int sink_keys, int sink_len, int block_tok0) {
+                                                    size_t bh_bytes, int ring_koff, size_t ring_vt, int ring_pad,
+                                                    int sink_koff, size_t sink_vt, int sink_keys, int sink_pad,
+                                                    int sink_len, int block_tok0) {
   __shared__ uint16_t vs[KT][D + 2];  // the tile's V rows (row pitch 228 B)
   const int tiles = (Lb + KT - 1) / KT;
   const int u = blockIdx.x / tiles, t0 = (blockIdx.x % tiles) * KT;
@@ -108,16 +145,25 @@ __global__ __launch_bounds__(256) void stage_kernel(const uint16_t *__restrict__
     for (int j = 0; j < 8; ++j) vs[t][8 * p + j] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
   }
   __syncthreads();
-  // V^T of a slot: row d holds the slot's keys; this tile fills keys t0 .. t0 + n - 1
-  auto put_vt = [&](int slot_koff, int slot_len, int key0, int limit) {
-    uint16_t *vt = reinterpret_cast<uint16_t *>(base + size_t(total_keys) * (D * 2) + size_t(slot_koff) * (D * 2));
-    for (int idx = tid; idx < D * n; idx += 256) {
-      const int d = idx / n, t = idx % n;
-      if (t < limit) vt[size_t(d) * slot_len + key0 + t] = vs[t][d];
+  // V^T of a slot (row d: the slot's keys, permuted, rows of `pad` keys); this
+  // tile fills keys key0 .. key0 + limit - 1, and the workgroup holding the
+  // slot's last key also zero-fills the padding keys len .. pad - 1
+  auto put_vt = [&](size_t vt_off, int pad, int len, int key0, int limit) {
+    uint16_t *vt = reinterpret_cast<uint16_t *>(base + vt_off);
+    for (int idx = tid; idx < D * limit; idx += 256) {
+      const int d = idx / limit, t = idx % limit;
+      vt[size_t(d) * pad + vt_pos(key0 + t)] = vs[t][d];
+    }
+    if (key0 + limit == len) {
+      const int np = pad - len;
+      for (int idx = tid; idx < D * np; idx += 256) {
+        const int d = idx / np, t = idx % np;
+        vt[size_t(d) * pad + vt_pos(len + t)] = 0;
+      }
     }
   };
-  put_vt(ring_koff, Lb, t0, n);
-  if (t0 < sink_len) put_vt(sink_koff, sink_keys, block_tok0 + t0, min(n, sink_len - t0));
+  put_vt(ring_vt, ring_pad, Lb, t0, n);
+  if (t0 < sink_len) put_vt(sink_vt, sink_pad, sink_keys, block_tok0 + t0, min(n, sink_len - t0));
 }
 
 // ---------------------------------------------------------------------------
@@ -126,7 +172,8 @@ struct Segs {
   int n;              // segments (1 .. 4)
   int koff[4];        // first key of the segment's slot in the per-(b, h) key space
   int len[4];         // keys of the segment (a prefix of the slot)
-  int slot_len[4];    // keys of the slot (row length of its V^T)
+  int pad[4];         // keys per V^T row of the slot (a multiple of 64)
+  int vt_off[4];      // byte offset of the slot's V^T in the per-(b, h) cache slice
   int tiles0[5];      // tiles before segment s; tiles0[n] = all tiles
 };
 
@@ -140,45 +187,54 @@ __device__ __forceinline__ void tile_of(const Segs &sg, int j, int &s, int &key0
 }
 
 // Copy wave L (0: K tile, 1: V^T tile): tile j into buffer j & 1.
-template <int L>
-__device__ __forceinline__ void copy_role(const char *__restrict__ bh, int total_keys, const Segs &sg, char *lds) {
+__device__ __forceinline__ void copy_role(const char *__restrict__ bh, const Segs &sg, char *lds) {
   const int lane = threadIdx.x & 63;
   const int ntiles = sg.tiles0[sg.n];
-  auto issue = [&](int j) {
+  auto issue_k = [&](int j) {
     int s, key0, nvalid;
     tile_of(sg, j, s, key0, nvalid);
-    char *buf = lds + (j & 1) * kBuf;
-    if constexpr (L == 0) {
+    {
       // key r = 4i + lane / 16 of the tile, LDS slot lane % 16 holds piece slot ^ (r & 15)
+      char *buf = lds + (j & 1) * kKTile;
       const auto rs = make_rsrc(bh + size_t(sg.koff[s] + key0) * (D * 2), uint32_t(nvalid) * (D * 2));
 #pragma unroll
       for (int i = 0; i < kKInstr; ++i) {
         const int r = 4 * i + (lane >> 4), p = (lane & 15) ^ (r & 15);
         copy16(rs, buf + 1024 * i, p < 14 ? uint32_t(r) * (D * 2) + 16u * p : kOutOfRange);
       }
-    } else {
-      // V^T row d = 8i + lane / 8, LDS slot lane % 8 holds keys 8 (slot ^ (d & 7)) .. + 7;
-      // keys past the slot read as zero, keys past the segment are masked
-      const char *vt = bh + size_t(total_keys) * (D * 2) + size_t(sg.koff[s]) * (D * 2);
-      const auto rs = make_rsrc(vt, uint32_t(sg.slot_len[s]) * (D * 2));
+    }
+  };
+  auto issue_v = [&](int j) {
+    int s, key0, nvalid;
+    tile_of(sg, j, s, key0, nvalid);
+    {
+      // V^T row d = 8i + lane / 8, LDS slot lane % 8 holds positions 8 (slot ^ ((d >> 1) & 7)) .. + 7:
+      // the sixteen 16-byte reads of rows d = 0..15 at one position hit distinct bank groups.
+      // Positions past the segment hold other keys of the slot or the zero padding (masked)
+      char *buf = lds + kLdsV + (j & 1) * kVTile;
+      const auto rs = make_rsrc(bh + sg.vt_off[s], uint32_t(sg.pad[s]) * (D * 2));
 #pragma unroll
       for (int i = 0; i < kVInstr; ++i) {
-        const int d = 8 * i + (lane >> 3), p = (lane & 7) ^ (d & 7);
-        copy16(rs, buf + kKTile + 1024 * i, (uint32_t(d) * sg.slot_len[s] + key0 + 8 * p) * 2u);
+        const int d = 8 * i + (lane >> 3), p = (lane & 7) ^ ((d >> 1) & 7);
+        copy16(rs, buf + 1024 * i, (uint32_t(d) * sg.pad[s] + key0 + 8 * p) * 2u);
       }
     }
   };
-  if (ntiles > 0) issue(0);
-  for (int j = 0; j < ntiles; ++j) {
-    wait_vm<0>();    // tile j landed
-    bare_barrier();  // compute waves are done with buffer (j + 1) & 1
-    if (j + 1 < ntiles) issue(j + 1);
+  // barrier j (j = 0 .. ntiles) opens step j, which reads K tile j and V^T
+  // tile j - 1; after it, K tile j + 1 and V^T tile j are issued (their
+  // buffers were last read in step j - 1)
+  issue_k(0);
+  for (int j = 0; j <= ntiles; ++j) {
+    wait_vm<0>();
+    bare_barrier();
+    if (j + 1 < ntiles) issue_k(j + 1);
+    if (j < ntiles) issue_v(j);
   }
 }
 
-template <int W, bool kOutBf16>
-__device__ __forceinline__ void compute_role(const uint16_t *__restrict__ q, void *__restrict__ o, int Lb, int H,
-                                             int b, int h, int qt, const Segs &sg, char *lds) {
+template <bool kOutBf16>
+__device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__ q, void *__restrict__ o, int Lb,
+                                             int H, int b, int h, int qt, const Segs &sg, char *lds) {
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const size_t rowstride = size_t(H) * D;
   const int q0 = qt * QB + W * QW;  // first query of this wave
@@ -208,16 +264,14 @@ __device__ __forceinline__ void compute_role(const uint16_t *__restrict__ q, voi
   f32x4 oacc[7][2];
 #pragma unroll
   for (int dt = 0; dt < 7; ++dt) oacc[dt][0] = oacc[dt][1] = zero4();
+  // running maximum (log2 units) and this lane's partial sum of P, per query tile
   float m[2] = {-__builtin_inff(), -__builtin_inff()}, l[2] = {0.f, 0.f};
   const int ntiles = sg.tiles0[sg.n];
-  for (int j = 0; j < ntiles; ++j) {
-    int s, key0, nvalid;
-    tile_of(sg, j, s, key0, nvalid);
-    compute_barrier();  // tile j is in buffer j & 1
-    const char *kb_ = lds + (j & 1) * kBuf;
-    const char *vb_ = kb_ + kKTile;
-    // ---- S^T = K Q^T: key tile t (16 keys), query tile qq
-    f32x4 sacc[4][2];
+  f32x4 sacc[4][2];
+  F32 pf[2][2];  // P^T B operands [qq][key pair] of the previous tile
+  // ---- S^T = K Q^T of tile j: key tile t (16 keys), query tile qq
+  auto scores = [&](int j) {
+    const char *kb_ = lds + (j & 1) * kKTile;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const char *rowp = kb_ + (16 * t + ln) * kKRow;
@@ -237,67 +291,93 @@ __device__ __forceinline__ void compute_role(const uint16_t *__restrict__ q, voi
         sacc[t][qq] = mma(kt, qtl[qq], acc);
       }
     }
-    // ---- online softmax per query (one query per lane column)
-    F32 pf[2][2];  // P^T B operands [qq][key pair]
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      float sv[4][4];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = 16 * t + 4 * lg + e < nvalid;
-          sv[t][e] = ok ? sacc[t][qq][e] * scale2 : -__builtin_inff();
-          mx = fmaxf(mx, sv[t][e]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qq], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[qq] - mnew);
-      m[qq] = mnew;
-      float ps = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pv[t][e] = __builtin_amdgcn_exp2f(sv[t][e] - mnew);
-          ps += pv[t][e];
-        }
-      l[qq] = l[qq] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < 7; ++dt) oacc[dt][qq] = oacc[dt][qq] * alpha;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        pf[qq][pp] = F32{{pack_bf16x2(pv[2 * pp][0], pv[2 * pp][1]), pack_bf16x2(pv[2 * pp][2], pv[2 * pp][3]),
-                          pack_bf16x2(pv[2 * pp + 1][0], pv[2 * pp + 1][1]),
-                          pack_bf16x2(pv[2 * pp + 1][2], pv[2 * pp + 1][3])}};
-    }
-    // ---- O^T += V^T P^T: d tile dt, key pair pp (keys 32 pp .. 32 pp + 31)
+  };
+  // ---- O^T += V^T P^T of tile j: d tile dt, key pair pp (keys 32 pp .. 32 pp + 31)
+  auto pv = [&](int j) {
+    const char *vb_ = lds + kLdsV + (j & 1) * kVTile;
 #pragma unroll
     for (int dt = 0; dt < 7; ++dt) {
       const int d = 16 * dt + ln;
       const char *vrow = vb_ + d * (KT * 2);
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        const int p0 = 4 * pp + (lg >> 1), p1 = p0 + 2;
-        const uint2 a0 = *reinterpret_cast<const uint2 *>(vrow + 16 * (p0 ^ (d & 7)) + 8 * (lg & 1));
-        const uint2 a1 = *reinterpret_cast<const uint2 *>(vrow + 16 * (p1 ^ (d & 7)) + 8 * (lg & 1));
-        const F32 vf{{a0.x, a0.y, a1.x, a1.y}};
+        // positions 32 pp + 8 g .. + 7 hold this lane's pair-order keys
+        const uint4 a = *reinterpret_cast<const uint4 *>(vrow + 16 * ((4 * pp + lg) ^ ((d >> 1) & 7)));
+        const F32 vf{{a.x, a.y, a.z, a.w}};
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) oacc[dt][qq] = mma(vf, pf[qq][pp], oacc[dt][qq]);
       }
     }
+  };
+  // ---- softmax of tile j per query (one query per lane column), exact running maximum
+  auto softmax = [&](int j) {
+    int s_, key0, nvalid;
+    tile_of(sg, j, s_, key0, nvalid);
+    float sv[2][4][4];
+    float mnew[2];
+    bool grow = false;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = 16 * t + 4 * lg + e < nvalid;
+          sv[qq][t][e] = ok ? sacc[t][qq][e] * scale2 : -__builtin_inff();
+          mx = fmaxf(mx, sv[qq][t][e]);
+        }
+      mnew[qq] = fmaxf(m[qq], lanes4_max(mx));
+      grow |= mnew[qq] > m[qq];
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // some query of the wave has a new maximum
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const float alpha = __builtin_amdgcn_exp2f(m[qq] - mnew[qq]);  // 0 on the first tile, 1 if unchanged
+        l[qq] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 7; ++dt) oacc[dt][qq] = oacc[dt][qq] * alpha;
+      }
+    }
+    m[0] = mnew[0];
+    m[1] = mnew[1];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      float pv_[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv_[t][e] = __builtin_amdgcn_exp2f(sv[qq][t][e] - m[qq]);
+          l[qq] += pv_[t][e];
+        }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        pf[qq][pp] = F32{{pack_bf16x2(pv_[2 * pp][0], pv_[2 * pp][1]), pack_bf16x2(pv_[2 * pp][2], pv_[2 * pp][3]),
+                          pack_bf16x2(pv_[2 * pp + 1][0], pv_[2 * pp + 1][1]),
+                          pack_bf16x2(pv_[2 * pp + 1][2], pv_[2 * pp + 1][3])}};
+    }
+  };
+  // step 0: scores and softmax of tile 0; step j: scores of tile j with P V of
+  // tile j - 1 (one basic block, so their products interleave), softmax of
+  // tile j; a last step: P V of the last tile
+  compute_barrier();
+  scores(0);
+  softmax(0);
+  for (int j = 1; j < ntiles; ++j) {
+    compute_barrier();
+    scores(j);
+    pv(j - 1);
+    softmax(j);
   }
+  compute_barrier();
+  pv(ntiles - 1);
   // ---- normalise and store: lane (ln, g) of query tile qq holds d = 16 dt + 4 g .. + 3
   const auto ro = make_rsrc(static_cast<char *>(o) + size_t(b) * Lb * rowstride * (kOutBf16 ? 2 : 4),
                             uint32_t(Lb) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq) {
-    float lt = l[qq] + __shfl_xor(l[qq], 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = 1.f / lt;
+    const float inv = 1.f / lanes4_sum(l[qq]);
     const int qi = q0 + 16 * qq + ln;
     const uint32_t row = qi < Lb ? uint32_t(qi) * uint32_t(rowstride) + uint32_t(h) * D : kOutOfRange;
 #pragma unroll
@@ -320,23 +400,21 @@ template <bool kOutBf16>
 __global__ __launch_bounds__(kThreads) void attn_kernel(const uint16_t *__restrict__ q,
                                                         const char *__restrict__ cache, void *__restrict__ o,
                                                         int Lb, int H, int units, int nqt, size_t bh_bytes,
-                                                        int total_keys, Segs sg) {
+                                                        Segs sg) {
   extern __shared__ __align__(16) char lds[];
-  // the query tiles of one (b, h) run on one XCD (workgroup i on XCD i % 8), so
-  // its K and V^T are fetched into that L2 once
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int u = xcd + 8 * (slot / nqt), qt = slot % nqt;
-  if (u >= units) return;
+  // workgroup i runs on XCD i % 8; each XCD takes a contiguous range of the
+  // (b, h, query tile) list, so a (b, h)'s K and V^T are fetched into at most
+  // two L2s and every XCD gets the same number of workgroups
+  const int per_xcd = int((gridDim.x + 7) / 8);
+  const int g = (blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
+  if (g >= units * nqt) return;
+  const int u = g / nqt, qt = g % nqt;
   const int b = u / H, h = u % H;
   const char *bh = cache + size_t(u) * bh_bytes;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wave) {
-    case 0: compute_role<0, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
-    case 1: compute_role<1, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
-    case 2: compute_role<2, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
-    case 3: compute_role<3, kOutBf16>(q, o, Lb, H, b, h, qt, sg, lds); break;
-    case 4: copy_role<0>(bh, total_keys, sg, lds); break;
-    default: copy_role<1>(bh, total_keys, sg, lds); break;
+    case kComputeWaves: copy_role(bh, sg, lds); break;
+    default: compute_role<kOutBf16>(wave, q, o, Lb, H, b, h, qt, sg, lds); break;
   }
 }
 
@@ -350,12 +428,14 @@ hipError_t launch_attn(const AttnPlan &p, int block, const void *q, const void *
   const int block_tok0 = block * p.Lb;                           // first token of the block in the stream
   const int sink_len = std::max(0, std::min(p.Lb, p.Ls - block_tok0));  // block tokens that are sink tokens
   char *c = static_cast<char *>(cache);
+  // V^T slots follow the K rows: the sink slot, then the ring slots
+  auto ring_vt = [&](int r) { return p.vt0 + size_t(224) * (size_t(p.Ls_pad) + size_t(r) * p.Lb_pad); };
   {
     const unsigned grid = unsigned(units) * unsigned((p.Lb + KT - 1) / KT);
     stage_kernel<<<dim3(grid), dim3(256), 0, stream>>>(static_cast<const uint16_t *>(k),
                                                        static_cast<const uint16_t *>(v), c, p.Lb, p.H, units,
-                                                       p.bh_bytes, p.total_keys, ring_koff, 0, p.Ls, sink_len,
-                                                       block_tok0);
+                                                       p.bh_bytes, ring_koff, ring_vt(ring), p.Lb_pad, 0, p.vt0, p.Ls,
+                                                       p.Ls_pad, sink_len, block_tok0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -363,15 +443,19 @@ hipError_t launch_attn(const AttnPlan &p, int block, const void *q, const void *
   Segs sg{};
   const int first_block = std::max(0, block - p.C);
   const int sink_uncovered = std::min(p.Ls, first_block * p.Lb);  // sink keys below the window
-  auto add = [&](int koff, int len, int slot_len) {
+  auto add = [&](int koff, int len, int pad, size_t vt_off) {
     sg.koff[sg.n] = koff;
     sg.len[sg.n] = len;
-    sg.slot_len[sg.n] = slot_len;
+    sg.pad[sg.n] = pad;
+    sg.vt_off[sg.n] = int(vt_off);
     sg.tiles0[sg.n + 1] = sg.tiles0[sg.n] + (len + KT - 1) / KT;
     ++sg.n;
   };
-  if (sink_uncovered > 0) add(0, sink_uncovered, p.Ls);
-  for (int nb = first_block; nb <= block; ++nb) add(p.Ls + (nb % (p.C + 1)) * p.Lb, p.Lb, p.Lb);
+  if (sink_uncovered > 0) add(0, sink_uncovered, p.Ls_pad, p.vt0);
+  for (int nb = first_block; nb <= block; ++nb) {
+    const int r = nb % (p.C + 1);
+    add(p.Ls + r * p.Lb, p.Lb, p.Lb_pad, ring_vt(r));
+  }
   static const hipError_t lds0 = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<false>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   static const hipError_t lds1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<true>),
@@ -379,13 +463,13 @@ hipError_t launch_attn(const AttnPlan &p, int block, const void *q, const void *
   if (lds0 != hipSuccess) return lds0;
   if (lds1 != hipSuccess) return lds1;
   const int nqt = (p.Lb + QB - 1) / QB;
-  const unsigned grid = 8u * unsigned(nqt) * unsigned((units + 7) / 8);
+  const unsigned grid = 8u * unsigned((units * nqt + 7) / 8);
   if (p.o_bf16)
     attn_kernel<true><<<dim3(grid), dim3(kThreads), kLds, stream>>>(static_cast<const uint16_t *>(q), c, o, p.Lb,
-                                                                   p.H, units, nqt, p.bh_bytes, p.total_keys, sg);
+                                                                   p.H, units, nqt, p.bh_bytes, sg);
   else
     attn_kernel<false><<<dim3(grid), dim3(kThreads), kLds, stream>>>(static_cast<const uint16_t *>(q), c, o, p.Lb,
-                                                                    p.H, units, nqt, p.bh_bytes, p.total_keys, sg);
+                                                                    p.H, units, nqt, p.bh_bytes, sg);
   return hipGetLastError();
 }
 

@@ -323,9 +323,11 @@ static gdn_status_t attn_plan(const attn_problem_t *p, gdn::AttnPlan &P) {
   const long long lb = (long long)p->frame_tokens * p->frames_per_block;
   const long long ls = (long long)p->frame_tokens * p->sink_frames;
   const long long keys = ls + (long long)(p->cached_blocks + 1) * lb;
+  const long long ls_pad = (ls + 63) / 64 * 64, lb_pad = (lb + 63) / 64 * 64;
+  const long long slice = 224 * (keys + ls_pad + (long long)(p->cached_blocks + 1) * lb_pad);
   const long long rowbytes = (long long)p->num_heads * p->head_dim * 4;
   // buffer offsets inside the kernels are 32-bit: per (b, h) cache slice, per-batch q and o
-  if (keys * 448 >= (1LL << 31) || lb * rowbytes >= (1LL << 31) || (long long)p->batch * p->num_heads > (1 << 24))
+  if (slice >= (1LL << 31) || lb * rowbytes >= (1LL << 31) || (long long)p->batch * p->num_heads > (1 << 24))
     return fail(GDN_ERR_UNSUPPORTED, "attention block too large (block tokens %lld, cached keys %lld)", lb, keys);
   P.B = p->batch;
   P.H = p->num_heads;
@@ -336,7 +338,10 @@ static gdn_status_t attn_plan(const attn_problem_t *p, gdn::AttnPlan &P) {
   P.Lb = int(lb);
   P.Ls = int(ls);
   P.total_keys = int(keys);
-  P.bh_bytes = align_up(size_t(keys) * 448);
+  P.Ls_pad = int(ls_pad);
+  P.Lb_pad = int(lb_pad);
+  P.vt0 = size_t(keys) * 224;
+  P.bh_bytes = align_up(size_t(slice));
   P.o_bf16 = p->o_dtype == GDN_BF16;
   return GDN_OK;
 }

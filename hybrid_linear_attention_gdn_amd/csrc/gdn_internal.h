@@ -60,6 +60,8 @@ struct AttnPlan {
   int ft = 0, fpb = 0, C = 0, S = 0;  // frame tokens, frames per block, cached blocks, sink frames
   int Lb = 0, Ls = 0;                 // tokens per block, sink tokens
   int total_keys = 0;                 // keys per (b, h) in the cache: sink slot + C + 1 ring slots
+  int Ls_pad = 0, Lb_pad = 0;         // V^T row lengths of the sink and ring slots (multiples of 64)
+  size_t vt0 = 0;                     // byte offset of the V^T slots in a (b, h) slice (after the K rows)
   size_t bh_bytes = 0;                // cache bytes per (b, h)
   bool o_bf16 = false;
 };

@@ -151,7 +151,8 @@ def test_attention_exports_and_host_checks(lib):
     n = ctypes.c_size_t(0)
     assert lib.attn_cache_bytes(ctypes.byref(p), ctypes.byref(n)) == L.GDN_OK
     keys = 880 + 3 * 2640
-    assert n.value == 20 * ((keys * 448 + 255) // 256 * 256)
+    vt_keys = 896 + 3 * 2688  # V^T rows padded to multiples of 64 keys
+    assert n.value == 20 * ((224 * (keys + vt_keys) + 255) // 256 * 256)
     bad = L.AttnProblem(1, 20, 128, 880, 3, 2, 1, L.GDN_F32)
     assert lib.attn_cache_bytes(ctypes.byref(bad), ctypes.byref(n)) == L.GDN_ERR_UNSUPPORTED and n.value == 0
     bad = L.AttnProblem(1, 20, 112, 880, 0, 2, 1, L.GDN_F32)
