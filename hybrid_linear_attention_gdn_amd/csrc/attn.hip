@@ -83,20 +83,13 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of a column)
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of a column)
 __device__ __forceinline__ float lanes4_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float lanes4_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 __device__ __forceinline__ void bare_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
@@ -259,13 +252,18 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
       qtl[qq] = F16{{x.x, x.y}};
     }
   }
-  // scores in the log2 domain: q . k / sqrt(d) * log2(e)
+  // raw scores q . k to the log2 domain of the softmax: / sqrt(d) * log2(e)
   const float scale2 = 1.44269504088896341f / __builtin_sqrtf(float(D));
   f32x4 oacc[7][2];
 #pragma unroll
   for (int dt = 0; dt < 7; ++dt) oacc[dt][0] = oacc[dt][1] = zero4();
-  // running maximum (log2 units) and this lane's partial sum of P, per query tile
-  float m[2] = {-__builtin_inff(), -__builtin_inff()}, l[2] = {0.f, 0.f};
+  // running maximum of the raw scores per query tile, and the softmax
+  // denominators: sum of the bf16 weights, formed on the matrix cores (an
+  // all-ones A operand), so they are exactly the weights the numerator uses
+  float m[2] = {-__builtin_inff(), -__builtin_inff()};
+  f32x4 lacc[2] = {zero4(), zero4()};
+  constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 1.0
+  const F32 ones{{kOnes, kOnes, kOnes, kOnes}};
   const int ntiles = sg.tiles0[sg.n];
   f32x4 sacc[4][2];
   F32 pf[2][2];  // P^T B operands [qq][key pair] of the previous tile
@@ -308,12 +306,26 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
         for (int qq = 0; qq < 2; ++qq) oacc[dt][qq] = mma(vf, pf[qq][pp], oacc[dt][qq]);
       }
     }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) lacc[qq] = mma(ones, pf[qq][pp], lacc[qq]);
   };
-  // ---- softmax of tile j per query (one query per lane column), exact running maximum
+  // ---- softmax of tile j per query (one query per lane column), exact running
+  // maximum.  m holds the maximum raw score q . k; the weights are
+  // 2^(scale2 (s - m)) = e^((s - m) / sqrt(d)), one FMA and one exp2 per score.
   auto softmax = [&](int j) {
     int s_, key0, nvalid;
     tile_of(sg, j, s_, key0, nvalid);
-    float sv[2][4][4];
+    if (nvalid < KT) {  // a segment's last tile: keys past it score -inf (wave-uniform)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * t + 4 * lg + e >= nvalid) sacc[t][qq][e] = -__builtin_inff();
+    }
     float mnew[2];
     bool grow = false;
 #pragma unroll
@@ -322,19 +334,15 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = 16 * t + 4 * lg + e < nvalid;
-          sv[qq][t][e] = ok ? sacc[t][qq][e] * scale2 : -__builtin_inff();
-          mx = fmaxf(mx, sv[qq][t][e]);
-        }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[t][qq][e]);
       mnew[qq] = fmaxf(m[qq], lanes4_max(mx));
       grow |= mnew[qq] > m[qq];
     }
     if (__builtin_amdgcn_ballot_w64(grow)) {  // some query of the wave has a new maximum
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        const float alpha = __builtin_amdgcn_exp2f(m[qq] - mnew[qq]);  // 0 on the first tile, 1 if unchanged
-        l[qq] *= alpha;
+        const float alpha = __builtin_amdgcn_exp2f((m[qq] - mnew[qq]) * scale2);  // 0 on the first tile
+        lacc[qq] = lacc[qq] * alpha;
 #pragma unroll
         for (int dt = 0; dt < 7; ++dt) oacc[dt][qq] = oacc[dt][qq] * alpha;
       }
@@ -343,13 +351,13 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
     m[1] = mnew[1];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
+      const float mo = -m[qq] * scale2;
       float pv_[4][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pv_[t][e] = __builtin_amdgcn_exp2f(sv[qq][t][e] - m[qq]);
-          l[qq] += pv_[t][e];
+          pv_[t][e] = __builtin_amdgcn_exp2f(fmaf(sacc[t][qq][e], scale2, mo));
         }
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
@@ -358,26 +366,43 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
                           pack_bf16x2(pv_[2 * pp + 1][2], pv_[2 * pp + 1][3])}};
     }
   };
-  // step 0: scores and softmax of tile 0; step j: scores of tile j with P V of
-  // tile j - 1 (one basic block, so their products interleave), softmax of
-  // tile j; a last step: P V of the last tile
-  compute_barrier();
-  scores(0);
-  softmax(0);
-  for (int j = 1; j < ntiles; ++j) {
+  // Step j reads K tile j and V^T tile j - 1.  Waves 0-3 ("lead") run a step as
+  // scores of tile j with P V of tile j - 1, then the softmax of tile j;
+  // waves 4-6 ("lag", the second wave on SIMDs 0-2) run the softmax of tile
+  // j - 1 first, then the scores of tile j and P V of tile j - 1.  The two
+  // waves of a SIMD thus spend each step's halves on different units (one on
+  // the vector ALU while the other keeps the matrix core busy).
+  if (W < 4) {
     compute_barrier();
-    scores(j);
-    pv(j - 1);
-    softmax(j);
+    scores(0);
+    softmax(0);
+    for (int j = 1; j < ntiles; ++j) {
+      compute_barrier();
+      scores(j);
+      pv(j - 1);
+      softmax(j);
+    }
+    compute_barrier();
+    pv(ntiles - 1);
+  } else {
+    compute_barrier();
+    scores(0);
+    for (int j = 1; j < ntiles; ++j) {
+      compute_barrier();
+      softmax(j - 1);
+      scores(j);
+      pv(j - 1);
+    }
+    compute_barrier();
+    softmax(ntiles - 1);
+    pv(ntiles - 1);
   }
-  compute_barrier();
-  pv(ntiles - 1);
   // ---- normalise and store: lane (ln, g) of query tile qq holds d = 16 dt + 4 g .. + 3
   const auto ro = make_rsrc(static_cast<char *>(o) + size_t(b) * Lb * rowstride * (kOutBf16 ? 2 : 4),
                             uint32_t(Lb) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq) {
-    const float inv = 1.f / lanes4_sum(l[qq]);
+    const float inv = 1.f / lacc[qq][0];  // every row of the denominator tile holds the same sum
     const int qi = q0 + 16 * qq + ln;
     const uint32_t row = qi < Lb ? uint32_t(qi) * uint32_t(rowstride) + uint32_t(h) * D : kOutOfRange;
 #pragma unroll
