@@ -155,7 +155,24 @@ __global__ __launch_bounds__(256) void stage_kernel(const uint16_t *__restrict__
       }
     }
   };
-  put_vt(ring_vt, ring_pad, Lb, t0, n);
+  // ring slot: the tile's keys t0 .. t0 + 63 fill positions t0 .. t0 + 63 of
+  // every row (t0 is a multiple of 64); one 16-byte store per 8 positions,
+  // keys past the block zero (the last tile covers the row padding)
+  {
+    uint16_t *vt = reinterpret_cast<uint16_t *>(base + ring_vt);
+    for (int idx = tid; idx < D * (KT / 8); idx += 256) {
+      const int d = idx / (KT / 8), gp = idx % (KT / 8);
+      const int kb = 32 * (gp >> 2) + 4 * (gp & 3);  // keys kb .. kb + 3 and kb + 16 .. kb + 19
+      uint32_t w[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int ka = kb + (s2 < 2 ? 2 * s2 : 16 + 2 * (s2 - 2)), kc = ka + 1;
+        const uint32_t lo = ka < n ? vs[ka][d] : 0u, hi = kc < n ? vs[kc][d] : 0u;
+        w[s2] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4 *>(vt + size_t(d) * ring_pad + t0 + 8 * gp) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
   if (t0 < sink_len) put_vt(sink_vt, sink_pad, sink_keys, block_tok0 + t0, min(n, sink_len - t0));
 }
 

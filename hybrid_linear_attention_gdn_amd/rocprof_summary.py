@@ -107,12 +107,15 @@ def stats(args) -> str:
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
     if args.bench_log:
         b = _bench_json(args.bench_log)
-        if b:
+        if b and "stages_ms" in b:
             rl = b.get("roofline", {})
             out += ["", f"bench.py's own HIP-event timing in the same run (per launch): "
                         f"{rl.get('kernel', '?')} {1e3 * rl.get('kernel_ms', 0.0):.1f} us; "
                         f"stages {', '.join(f'{k} {1e3 * v:.1f} us' for k, v in b.get('stages_ms', {}).items())}; "
                         f"step {1e3 * b.get('ms_per_step', 0.0):.1f} us."]
+        elif b:
+            out += ["", f"bench.py's own HIP-event timing in the same run: {1e3 * b.get('ms_per_step', 0.0):.1f} us "
+                        f"per step ({b.get('value')} {b.get('unit')})."]
     return "\n".join(out) + "\n"
 
 
