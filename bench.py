@@ -28,26 +28,27 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 # Algorithmic bytes per token-head that a kernel must move by the method's own
-# definition (bf16 q/k/v = 224 B each, fp32 g and beta 4 B each, o 448 B fp32 /
-# 224 B bf16, the prep scalars 16 B), and per (batch, head) for state in/out.
+# definition (q/k/v rows of 112 elements: 224 B each in bf16, 112 B in fp8;
+# fp32 g and beta 4 B each, o 448 B fp32 / 224 B bf16, the prep scalars 16 B),
+# and per (batch, head) for state in/out.
 STATE_BYTES = 112 * 112 * 4
 
 
-def stage_algorithmic_bytes(stage: str, o_bytes: int, mfma: bool) -> int:
-    """Per token-head algorithmic bytes of one kernel stage."""
+def stage_algorithmic_bytes(stage: str, o_bytes: int, mfma: bool, row: int = 224) -> int:
+    """Per token-head algorithmic bytes of one kernel stage; `row` = bytes of one q/k/v row."""
     if stage == "prep":
-        return 2 * 224 + 8 + 16      # reads q, k, g, beta; writes 4 scalars
+        return 2 * row + 8 + 16      # reads q, k, g, beta; writes 4 scalars
     if stage == "intra":
-        return 224 + 224 + 16 if mfma else 224 + 224 + 12  # reads q, k (+v on portable) and scalars
+        return 2 * row + 16 if mfma else 2 * row + 12  # reads q, k (+v on portable) and scalars
     if stage == "state":
-        return (3 * 224 + 16 + o_bytes) if mfma else (224 + 12)  # fused state pass + output on MFMA
+        return (3 * row + 16 + o_bytes) if mfma else (row + 12)  # fused state pass + output on MFMA
     if stage == "output":
-        return 2 * 224 + 12 + o_bytes
+        return 2 * row + 12 + o_bytes
     raise KeyError(stage)
 
 
-def path_algorithmic_bytes(o_bytes: int) -> int:
-    return 3 * 224 + 8 + o_bytes
+def path_algorithmic_bytes(o_bytes: int, row: int = 224) -> int:
+    return 3 * row + 8 + o_bytes
 
 
 def flops_per_token_head(C: int = 80, d: int = 112) -> float:
@@ -186,6 +187,9 @@ def main():
     if inp.dtype == "bf16":
         up = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
         q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+    elif inp.dtype == "fp8":  # E4M3FN codes
+        up8 = lambda b: torch.from_numpy(b).to(dev).view(torch.float8_e4m3fn)  # noqa: E731
+        q, k, v = up8(inp.q_bits), up8(inp.k_bits), up8(inp.v_bits)
     else:
         q, k, v = (torch.from_numpy(a).to(dev) for a in (inp.q, inp.k, inp.v))
     g, beta = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
@@ -194,6 +198,8 @@ def main():
     o_dtype = torch.float32 if args.o_dtype == "fp32" else torch.bfloat16
     o_bytes = 448 if args.o_dtype == "fp32" else 224
     B, T, H, d = q.shape
+    row = d * q.element_size()  # bytes of one q/k/v row
+    dtype_name = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8_e4m3", torch.float32: "f32"}[q.dtype]
     calls = w.calls
     Tc = T // calls
     o = torch.empty((B, T, H, d), dtype=o_dtype, device=dev)
@@ -239,11 +245,11 @@ def main():
     dom_ms = stages[dom][0]
     dom_calls_per_step = stages[dom][1] / args.steps
     launch_th = token_heads / calls
-    dom_bytes = stage_algorithmic_bytes(dom, o_bytes, mfma) * launch_th
+    dom_bytes = stage_algorithmic_bytes(dom, o_bytes, mfma, row) * launch_th
     if dom == "state":
         dom_bytes += 2 * STATE_BYTES * B * H
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    path_bytes = path_algorithmic_bytes(o_bytes) * token_heads + 2 * STATE_BYTES * B * H * calls
+    path_bytes = path_algorithmic_bytes(o_bytes, row) * token_heads + 2 * STATE_BYTES * B * H * calls
     path_gbs = path_bytes / (ms * 1e-3) / 1e9
     tflops = flops_per_token_head() * token_heads / (ms * 1e-3) / 1e12
 
@@ -286,7 +292,7 @@ def main():
         del src, dst
 
     out = {
-        "metric": "GDN fwd tokens/s per layer (20h×112d, bf16) + % MFMA peak on 1 MI355X",
+        "metric": f"GDN fwd tokens/s per layer (20h×112d, {dtype_name}) + % MFMA peak on 1 MI355X",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -296,7 +302,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
+        "dtype": dtype_name,
         "data": "synthetic (seeded N(0,1) q/k/v/beta logits, frame-wise log-decay -softplus(N(0,1)+2))",
         "config": {"workload": f"{w.name}: {w.note}", "batch": B, "tokens": T, "heads": H, "head_dim": d,
                    "calls_per_step": calls, "o_dtype": args.o_dtype, "kernels": "mfma" if mfma else "portable",

@@ -8,7 +8,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsanawm_gdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP, GDN_ERR_INTERNAL = range(6)
-GDN_F32, GDN_BF16 = 0, 1
+GDN_F32, GDN_BF16, GDN_FP8_E4M3 = 0, 1, 2
 GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_PORTABLE_KERNELS = 1, 2, 4
 
 # every symbol include/sanawm_gdn.h declares

@@ -85,7 +85,8 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   if (p->batch < 1 || p->num_heads < 1 || p->seq_len < 0 || p->head_dim_k < 1 || p->head_dim_v < 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "bad shape: batch=%d seq_len=%d heads=%d d_k=%d d_v=%d", p->batch,
                 p->seq_len, p->num_heads, p->head_dim_k, p->head_dim_v);
-  if ((p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16) || (p->o_dtype != GDN_F32 && p->o_dtype != GDN_BF16))
+  if ((p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16 && p->qkv_dtype != GDN_FP8_E4M3) ||
+      (p->o_dtype != GDN_F32 && p->o_dtype != GDN_BF16))
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown dtype (qkv=%d, o=%d)", p->qkv_dtype, p->o_dtype);
   const uint32_t known = GDN_FLAG_BETA_IS_PROB | GDN_FLAG_QK_PRENORMALIZED | GDN_FLAG_PORTABLE_KERNELS;
   if (p->flags & ~known) return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags & ~known);
@@ -98,12 +99,15 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   P.dv = p->head_dim_v;
   P.N = (P.T + gdn::kChunk - 1) / gdn::kChunk;
   P.qkv_bf16 = p->qkv_dtype == GDN_BF16;
+  P.qkv_fp8 = p->qkv_dtype == GDN_FP8_E4M3;
   P.o_bf16 = p->o_dtype == GDN_BF16;
   P.flags = p->flags;
-  P.mfma = gdn::kHaveMfmaPath && P.qkv_bf16 && !(p->flags & GDN_FLAG_PORTABLE_KERNELS);
+  if (P.qkv_fp8 && (p->flags & GDN_FLAG_PORTABLE_KERNELS))
+    return fail(GDN_ERR_UNSUPPORTED, "fp8 q, k, v run on the MFMA kernels only");
+  P.mfma = gdn::kHaveMfmaPath && (P.qkv_bf16 || P.qkv_fp8) && !(p->flags & GDN_FLAG_PORTABLE_KERNELS);
   if (P.mfma) {
     if (P.dk != gdn::kMfmaDim || P.dv != gdn::kMfmaDim)
-      return fail(GDN_ERR_UNSUPPORTED, "bf16 MFMA kernels need d_k = d_v = %d (got %d, %d)", gdn::kMfmaDim, P.dk,
+      return fail(GDN_ERR_UNSUPPORTED, "the MFMA kernels need d_k = d_v = %d (got %d, %d)", gdn::kMfmaDim, P.dk,
                   P.dv);
     // one chunk of rows of o (fp32) must stay addressable by a 31-bit buffer offset
     if (size_t(gdn::kChunk) * P.H * gdn::kMfmaDim * sizeof(float) >= (size_t(1) << 31))

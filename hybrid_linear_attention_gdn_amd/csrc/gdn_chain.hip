@@ -29,7 +29,11 @@
 //
 // K and Q rows sit at a 256-byte stride with their 16-byte pieces permuted
 // by row (slot = piece ^ (row & 15)), so the 16-byte fragment reads of 16
-// consecutive rows hit 16 distinct bank groups.  The products K S^T and
+// consecutive rows hit 16 distinct bank groups.  With fp8 (E4M3FN) inputs the
+// rows are staged as they are (112 bytes at a 128-byte stride, slot = piece ^
+// (row & 7)) and widened to bf16 as the compute waves read their fragments:
+// the copies move half the bytes and the products are those of bf16 inputs
+// holding the same values.  The products K S^T and
 // Q S^T use the instruction's natural k-order (lane group g holds k = 8g ..
 // 8g + 7), which makes each K/Q fragment one contiguous 16-byte read; the
 // state tiles are written to LDS in that order.  The products with R keep
@@ -100,36 +104,49 @@ constexpr int kLdsS = 0;                         // S operand: hi/lo x (3 x 1 KB
 constexpr int kLdsR = 2 * (3 * 1024 + 512);      // R operand: hi/lo x (2 x 1 KB + 512 B)
 constexpr int kLdsMP = kLdsR + 2 * (2 * 1024 + 512);  // M then P' record of the current chunk
 constexpr int kLdsRows = kLdsMP + kMBytes + kPBytes;  // two row buffers
-constexpr int kRowStride = 256;                  // bytes per staged K/Q row (224 used)
-constexpr int kRowK = 0;
-constexpr int kRowQ = C * kRowStride;            // 20,480
-constexpr int kRowV = 2 * C * kRowStride;        // 40,960: V tile, 80 rows x 32 B (+ 512 B of tail zeros)
-constexpr int kRowCs = kRowV + 3 * 1024;         // 44,032: the chunk's 256 scale floats
-constexpr int kRowsBytes = kRowCs + kCsFloats * 4;  // 45,056
-constexpr int kLdsChain = kLdsRows + 2 * kRowsBytes;  // 153,600
-static_assert(kMBytes % 1024 == 0 && kPBytes % 1024 == 0 && kCsFloats * 4 == 1024, "whole 1 KB copies");
-static_assert(kLdsMP % 1024 == 0 && kLdsRows % 1024 == 0 && kRowsBytes % 1024 == 0, "copy targets 1 KB aligned");
-static_assert(kLdsChain <= 160 * 1024, "fits one CU's LDS");
+constexpr int kMInstr = kMBytes / 1024;             // 35 one-KB copies of M
+constexpr int kPInstr = kPBytes / 1024;             // 15 of P'
 
-// Copy split between the three copy waves: per chunk, a share of the M / P'
-// record and a share of the rows.
-constexpr int kMInstr = kMBytes / 1024;             // 35
-constexpr int kPInstr = kPBytes / 1024;             // 15
-constexpr int kMShare = 17;                         // waves 0, 1: M 0..16, 17..33; wave 2: M 34 and P'
-constexpr int kRowInstrKQ = C * kRowStride / 1024;  // 20 per matrix
-__device__ constexpr int kRecShare[3] = {kMShare, kMShare, kMInstr - 2 * kMShare + kPInstr};
-__device__ constexpr int kRowShare[3] = {kRowInstrKQ, kRowInstrKQ, 3 + 1};
-static_assert(kMShare + 2 * kRowInstrKQ < 64 && kMInstr - 2 * kMShare + kPInstr + 8 < 64, "vmcnt holds 63");
+// One row buffer, for bf16 (kFp8 false) or E4M3FN (kFp8 true) inputs: K rows,
+// Q rows, this workgroup's 16 columns of V and the chunk's 256 scale floats.
+template <bool kFp8>
+struct Rows {
+  static constexpr int kElem = kFp8 ? 1 : 2;      // bytes per input element
+  static constexpr int kStride = kFp8 ? 128 : 256;  // bytes per staged K/Q row (112 / 224 used)
+  static constexpr int kSlots = kStride / 16;     // 16-byte slots per staged row
+  static constexpr int kPieces = D * kElem / 16;  // 16-byte pieces per row (7 / 14); the rest read as zero
+  static constexpr int kK = 0;
+  static constexpr int kQ = C * kStride;
+  static constexpr int kV = 2 * C * kStride;      // V tile: 80 rows x 16 elements, tail rows zero
+  static constexpr int kVRow = 16 * kElem;
+  static constexpr int kVInstr = kFp8 ? 2 : 3;    // 1 KB copies of the V tile
+  static constexpr int kCs = kV + kVInstr * 1024;
+  static constexpr int kBytes = kCs + kCsFloats * 4;  // 45,056 / 23,552
+  static constexpr int kLds = kLdsRows + 2 * kBytes;  // 153,600 / 110,592
+  static constexpr int kKQInstr = C * kStride / 1024;  // 20 / 10 one-KB copies per matrix
+  // Copy split between the three copy waves, per chunk: waves 0 and 1 take
+  // kMShare KB of M each and the K, resp. Q rows; wave 2 the rest of M, P',
+  // the V tile and the scales.
+  static constexpr int kMShare = kFp8 ? 14 : 17;
+  static constexpr int rec_share(int L) { return L < 2 ? kMShare : kMInstr - 2 * kMShare + kPInstr; }
+  static constexpr int row_share(int L) { return L < 2 ? kKQInstr : kVInstr + 1; }
+  static_assert(kBytes % 1024 == 0 && kLds <= 160 * 1024, "1 KB aligned row buffers within one CU's LDS");
+  static_assert(kVInstr * 1024 >= C * kVRow, "the V copies cover its 80 rows");
+  static_assert(rec_share(0) + 2 * row_share(0) < 64 && rec_share(2) + 2 * row_share(2) < 64, "vmcnt holds 63");
+};
+static_assert(kMBytes % 1024 == 0 && kPBytes % 1024 == 0 && kCsFloats * 4 == 1024, "whole 1 KB copies");
+static_assert(kLdsMP % 1024 == 0 && kLdsRows % 1024 == 0, "copy targets 1 KB aligned");
 
 struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k = d_k)
   F32 f[3];
   F16 t;
 };
 
-template <int W, bool kOutBf16>
+template <int W, bool kOutBf16, bool kFp8>
 __device__ __forceinline__ void compute_role(const float *__restrict__ state_in, float *state_out,
                                              void *__restrict__ o, int T, int H, int cb, int ce, int b, int h,
                                              int nt, char *lds) {
+  using G = Rows<kFp8>;
   constexpr Roles ro = kRoles[W];
   constexpr int nA = ro.nY + ro.nQA;  // 16-row tiles of K or Q multiplied by S^T in phase A
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
@@ -155,18 +172,40 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
   // written by lane groups 2(g & 1) and 2(g & 1) + 1 of that tile.
   auto s_slot = [&](int j) { return (j >> 1) * 1024 + (ln + 16 * (2 * (j & 1) + (lg >> 1))) * 16 + (lg & 1) * 8; };
 
-  // A-operand fragments of a 16-row tile of the staged K (m = 0) or Q (m = 1)
+  // A-operand fragments of a 16-row tile of the staged K (m = 0) or Q (m = 1):
+  // lane (ln, lg) takes d_k = 32kb + 8lg .. + 7 of row 16 tile + ln per 32-deep
+  // block and d_k = 96 + 4lg .. + 3 for the 16-deep block
   auto rows_frag = [&](const char *rb, int m, int tile) {
-    const char *rowp = rb + (m ? kRowQ : kRowK) + (16 * tile + ln) * kRowStride;
+    const char *rowp = rb + (m ? G::kQ : G::kK) + (16 * tile + ln) * G::kStride;
     RowFrags rf;
+    if constexpr (kFp8) {
+      const int sw = ln & 7;  // (row & 7)
 #pragma unroll
-    for (int kb = 0; kb < 3; ++kb) {
-      const uint4 x = *reinterpret_cast<const uint4 *>(rowp + 16 * ((4 * kb + lg) ^ ln));
-      rf.f[kb] = F32{{x.x, x.y, x.z, x.w}};
+      for (int kb = 0; kb < 3; ++kb) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(rowp + 16 * ((2 * kb + (lg >> 1)) ^ sw) + 8 * (lg & 1));
+        const uint2 a = fp8x4_to_bf16(x.x), c = fp8x4_to_bf16(x.y);
+        rf.f[kb] = F32{{a.x, a.y, c.x, c.y}};
+      }
+      const uint32_t x1 = *reinterpret_cast<const uint32_t *>(rowp + 16 * (6 ^ sw) + 4 * lg);
+      const uint2 t = fp8x4_to_bf16(x1);
+      rf.t = F16{{t.x, t.y}};
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(rowp + 16 * ((4 * kb + lg) ^ ln));
+        rf.f[kb] = F32{{x.x, x.y, x.z, x.w}};
+      }
+      const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 16 * ((12 + (lg >> 1)) ^ ln) + 8 * (lg & 1));
+      rf.t = F16{{x2.x, x2.y}};
     }
-    const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 16 * ((12 + (lg >> 1)) ^ ln) + 8 * (lg & 1));
-    rf.t = F16{{x2.x, x2.y}};
     return rf;
+  };
+  // element (row, column ln) of the staged V tile
+  auto v_elem = [&](const char *vl, int row) {
+    if constexpr (kFp8)
+      return __builtin_amdgcn_cvt_pk_f32_fp8(uint32_t(reinterpret_cast<const uint8_t *>(vl)[row * 16 + ln]), false)[0];
+    else
+      return bf16_to_f32(reinterpret_cast<const uint16_t *>(vl)[row * 16 + ln]);
   };
   auto ldf4 = [](const float *p) {
     const float4 t = *reinterpret_cast<const float4 *>(p);
@@ -218,9 +257,9 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
   publish_S();
   for (int c = cb; c < ce; ++c) {
     const int t0 = c * C, nv = min(C, T - t0);
-    const char *rb = lds + kLdsRows + (c & 1) * kRowsBytes;
-    const float *csl = reinterpret_cast<const float *>(rb + kRowCs);
-    const uint16_t *vl = reinterpret_cast<const uint16_t *>(rb + kRowV);
+    const char *rb = lds + kLdsRows + (c & 1) * G::kBytes;
+    const float *csl = reinterpret_cast<const float *>(rb + G::kCs);
+    const char *vl = rb + G::kV;
     compute_barrier();  // X: chunk c opens (S published; its rows and record landed)
     // ---- phase A: every LDS operand of the chunk except R is read here, so
     // that both buffers are free once R is published
@@ -252,7 +291,7 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
         aa[s] = ldf4(csl + 16 * tile + 4 * lg);
         bb[s] = ldf4(csl + 80 + 16 * tile + 4 * lg);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) va[s][e] = bf16_to_f32(vl[(16 * tile + 4 * lg + e) * 16 + ln]);
+        for (int e = 0; e < 4; ++e) va[s][e] = v_elem(vl, 16 * tile + 4 * lg + e);
       }
     __builtin_amdgcn_sched_barrier(0);  // the operands of Y and R first: they are on the critical path
     RowFrags fb[2];
@@ -436,47 +475,52 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
 // complete in issue order, so each wait names the number of younger copies
 // that may still be in flight (at most a record share and two row shares:
 // 57 of the 63 the counter holds).
-template <int L>
-__device__ __forceinline__ void copy_role(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                          const uint16_t *__restrict__ v, const char *__restrict__ Mws,
+template <int L, bool kFp8>
+__device__ __forceinline__ void copy_role(const char *__restrict__ q, const char *__restrict__ k,
+                                          const char *__restrict__ v, const char *__restrict__ Mws,
                                           const char *__restrict__ Pws, const float *__restrict__ CS, int T,
                                           int H, int N, int cb, int ce, int b, int h, int nt, char *lds) {
-  constexpr int kRec = kRecShare[L], kRow = kRowShare[L];
+  using G = Rows<kFp8>;
+  constexpr int kRow = G::row_share(L);
   const int lane = threadIdx.x & 63;
   const size_t u = size_t(b) * H + h;
-  const uint32_t row_bytes = uint32_t(H) * D * 2u;
-  // K / Q: copy i fills LDS rows 4i .. 4i + 3, lane -> (row 4i + lane / 16,
-  // slot lane % 16) holding piece slot ^ (row & 15); pieces 14 and 15 of a
-  // 224-byte row do not exist and read as zero
+  const uint32_t row_bytes = uint32_t(H) * D * G::kElem;
+  const uint32_t head_off = uint32_t(h) * D * G::kElem;
+  // K / Q: copy i fills 1 KB of LDS rows, lane -> (row, slot lane % kSlots)
+  // holding piece slot ^ (row % kSlots); slots past the row's pieces read as zero
   auto kq_off = [&](int i) {
-    const int r = 4 * i + (lane >> 4), p = (lane & 15) ^ (r & 15);
-    return p < 14 ? uint32_t(r) * row_bytes + uint32_t(h) * (D * 2) + 16u * p : kOutOfRange;
+    constexpr int kRowsPerCopy = 64 / G::kSlots;
+    const int r = kRowsPerCopy * i + lane / G::kSlots, p = (lane % G::kSlots) ^ (r % G::kSlots);
+    return p < G::kPieces ? uint32_t(r) * row_bytes + head_off + 16u * p : kOutOfRange;
   };
-  // V: copy i fills rows 32i .. 32i + 31 (32 bytes each: this tile's 16 columns)
+  // V: copy i fills 1 KB of the tile's rows (kVRow bytes each: this tile's 16 columns)
   auto v_off = [&](int i) {
-    const int r = 32 * i + (lane >> 1);
-    return r < C ? uint32_t(r) * row_bytes + uint32_t(h) * (D * 2) + 32u * nt + 16u * (lane & 1) : kOutOfRange;
+    constexpr int kLanesPerRow = G::kVRow / 16;
+    const int r = (64 / kLanesPerRow) * i + lane / kLanesPerRow;
+    return r < C ? uint32_t(r) * row_bytes + head_off + uint32_t(G::kVRow) * nt + 16u * (lane % kLanesPerRow)
+                 : kOutOfRange;
   };
   // wave 0: K rows; wave 1: Q rows; wave 2: the V tile and the scales
   auto copy_rows = [&](int c) {
     const int t0 = c * C, nv = min(C, T - t0);
-    const size_t base = (size_t(b) * T + t0) * size_t(H) * D;
+    const size_t base = (size_t(b) * T + t0) * size_t(H) * D * G::kElem;
     const uint32_t bytes = uint32_t(nv) * row_bytes;  // rows past the end read as zero
-    char *rb = lds + kLdsRows + (c & 1) * kRowsBytes;
+    char *rb = lds + kLdsRows + (c & 1) * G::kBytes;
     if constexpr (L < 2) {
       const auto rs = make_rsrc((L == 0 ? k : q) + base, bytes);
 #pragma unroll
-      for (int i = 0; i < kRowInstrKQ; ++i) copy16(rs, rb + (L == 0 ? kRowK : kRowQ) + 1024 * i, kq_off(i));
+      for (int i = 0; i < G::kKQInstr; ++i) copy16(rs, rb + (L == 0 ? G::kK : G::kQ) + 1024 * i, kq_off(i));
     } else {
       const auto rv = make_rsrc(v + base, bytes);
 #pragma unroll
-      for (int i = 0; i < 3; ++i) copy16(rv, rb + kRowV + 1024 * i, v_off(i));
-      copy16(make_rsrc(CS + (u * N + c) * kCsFloats, kCsFloats * 4), rb + kRowCs, 16u * lane);
+      for (int i = 0; i < G::kVInstr; ++i) copy16(rv, rb + G::kV + 1024 * i, v_off(i));
+      copy16(make_rsrc(CS + (u * N + c) * kCsFloats, kCsFloats * 4), rb + G::kCs, 16u * lane);
     }
   };
-  // waves 0, 1: 17 KB of M each; wave 2: the last KB of M and P'
+  // waves 0, 1: kMShare KB of M each; wave 2: the rest of M and P'
   auto copy_record = [&](int c) {
     const auto rm = make_rsrc(Mws + (u * N + c) * size_t(kMBytes), kMBytes);
+    constexpr int kMShare = G::kMShare;
     constexpr int m0 = L == 0 ? 0 : (L == 1 ? kMShare : 2 * kMShare), m1 = L == 2 ? kMInstr : m0 + kMShare;
 #pragma unroll
     for (int i = m0; i < m1; ++i) copy16(rm, lds + kLdsMP + 1024 * i, 1024u * i + 16u * lane);
@@ -507,19 +551,21 @@ __device__ __forceinline__ void copy_role(const uint16_t *__restrict__ q, const 
 
 // L2 warm-up of chunk c + kAhead: the head's 7 column-tile workgroups (on
 // one XCD) split its cache lines -- 280 of M, 120 of P', 8 of scales and
-// 3 per 224-byte row of K, Q, V -- so that the copies of that chunk hit L2
+// 3 per 224-byte row of K, Q, V (2 per 112-byte fp8 row) -- so that the copies of that chunk hit L2
 // instead of all waiting on the same HBM misses.  Four dword loads per lane
 // per chunk, each at a fixed per-lane base plus a per-chunk stride, consumed a
 // chunk later.
 constexpr int kAhead = 2;
-__device__ __forceinline__ void warm_role(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                          const uint16_t *__restrict__ v, const char *__restrict__ Mws,
+template <bool kFp8>
+__device__ __forceinline__ void warm_role(const char *__restrict__ q, const char *__restrict__ k,
+                                          const char *__restrict__ v, const char *__restrict__ Mws,
                                           const char *__restrict__ Pws, const float *__restrict__ CS,
                                           void *__restrict__ o, int T, int H, int N, int cb, int ce, int b, int h,
                                           int nt) {
   const int lane = threadIdx.x & 63;
   const size_t u = size_t(b) * H + h;
-  const size_t row_bytes = size_t(H) * D * 2;
+  constexpr int kElem = kFp8 ? 1 : 2, kParts = kFp8 ? 2 : 3;  // touches per row: every 128-byte line of it
+  const size_t row_bytes = size_t(H) * D * kElem;
   const char *base[4];
   size_t stride[4];
   int prow[4];
@@ -537,11 +583,11 @@ __device__ __forceinline__ void warm_role(const uint16_t *__restrict__ q, const 
       base[j] = reinterpret_cast<const char *>(CS + u * N * kCsFloats) + 128 * (pe - 400);
       stride[j] = kCsFloats * sizeof(float);
     } else {
-      const int r = min(pe - 408, 3 * 3 * C - 1), t = r / (3 * C), part = r % 3;
-      prow[j] = (r % (3 * C)) / 3;
-      const uint16_t *src = t == 0 ? k : (t == 1 ? q : v);
-      base[j] = reinterpret_cast<const char *>(src + (size_t(b) * T * H + h) * D) +
-                (part == 0 ? 0 : (part == 1 ? 128 : 220));
+      const int r = min(pe - 408, 3 * kParts * C - 1), t = r / (kParts * C), part = r % kParts;
+      prow[j] = (r % (kParts * C)) / kParts;
+      const char *src = t == 0 ? k : (t == 1 ? q : v);
+      base[j] = src + (size_t(b) * T * H + h) * D * kElem +
+                (part == 0 ? 0 : (kFp8 ? 108 : (part == 1 ? 128 : 220)));
       stride[j] = size_t(C) * row_bytes;
     }
   }
@@ -563,10 +609,10 @@ __device__ __forceinline__ void warm_role(const uint16_t *__restrict__ q, const 
   if (T < 0 && sink != 0u) static_cast<uint32_t *>(o)[0] = sink;  // never taken: keeps the touches alive
 }
 
-template <bool kOutBf16>
-__global__ __launch_bounds__(kThreads) void chain_kernel(const uint16_t *__restrict__ q,
-                                                         const uint16_t *__restrict__ k,
-                                                         const uint16_t *__restrict__ v,
+template <bool kOutBf16, bool kFp8>
+__global__ __launch_bounds__(kThreads) void chain_kernel(const char *__restrict__ q,
+                                                         const char *__restrict__ k,
+                                                         const char *__restrict__ v,
                                                          const char *__restrict__ Mws,
                                                          const char *__restrict__ Pws,
                                                          const float *__restrict__ CS, const float *state_in,
@@ -581,14 +627,14 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint16_t *__restr
   const int b = u / H, h = u % H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wave) {
-    case 0: compute_role<0, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 1: compute_role<1, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 2: compute_role<2, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 3: compute_role<3, kOutBf16>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 4: copy_role<0>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 5: copy_role<1>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 6: copy_role<2>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    default: warm_role(q, k, v, Mws, Pws, CS, o, T, H, N, cb, ce, b, h, nt); break;
+    case 0: compute_role<0, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 1: compute_role<1, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 2: compute_role<2, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 3: compute_role<3, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 4: copy_role<0, kFp8>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 5: copy_role<1, kFp8>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 6: copy_role<2, kFp8>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    default: warm_role<kFp8>(q, k, v, Mws, Pws, CS, o, T, H, N, cb, ce, b, h, nt); break;
   }
 }
 
@@ -631,16 +677,26 @@ constexpr int kSegmentMinChunks = 64;
 
 hipError_t launch_chain(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb, int ce,
                         const float *sin, float *sout, hipStream_t st) {
-  const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
-                 *v = static_cast<const uint16_t *>(a.v);
+  const char *q = static_cast<const char *>(a.q), *k = static_cast<const char *>(a.k),
+             *v = static_cast<const char *>(a.v);
   const int units = p.B * p.H;
-  const unsigned grid = 8u * mfma::NT * unsigned((units + 7) / 8);
-  if (p.o_bf16)
-    mfma::chain_kernel<true><<<dim3(grid), dim3(mfma::kThreads), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
-                                                                           p.H, p.N, cb, ce, units);
-  else
-    mfma::chain_kernel<false><<<dim3(grid), dim3(mfma::kThreads), mfma::kLdsChain, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T,
-                                                                            p.H, p.N, cb, ce, units);
+  const dim3 grid(8u * mfma::NT * unsigned((units + 7) / 8)), block(mfma::kThreads);
+  constexpr int lds16 = mfma::Rows<false>::kLds, lds8 = mfma::Rows<true>::kLds;
+  if (p.qkv_fp8) {
+    if (p.o_bf16)
+      mfma::chain_kernel<true, true><<<grid, block, lds8, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N, cb,
+                                                                ce, units);
+    else
+      mfma::chain_kernel<false, true><<<grid, block, lds8, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N, cb,
+                                                                 ce, units);
+  } else {
+    if (p.o_bf16)
+      mfma::chain_kernel<true, false><<<grid, block, lds16, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N,
+                                                                  cb, ce, units);
+    else
+      mfma::chain_kernel<false, false><<<grid, block, lds16, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N,
+                                                                   cb, ce, units);
+  }
   return hipGetLastError();
 }
 
@@ -651,12 +707,16 @@ hipError_t launch_mfma(const Plan &p, const Args &a) {
   char *P = a.ws + p.off_P;
   float *cs = reinterpret_cast<float *>(a.ws + p.off_cs);
   float *seg_state = reinterpret_cast<float *>(a.ws + p.off_Sseg);
-  static const hipError_t lds0 = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma::chain_kernel<false>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, mfma::kLdsChain);
-  static const hipError_t lds1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma::chain_kernel<true>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, mfma::kLdsChain);
-  if (lds0 != hipSuccess) return lds0;
-  if (lds1 != hipSuccess) return lds1;
+  auto allow = [](const void *f, int bytes) {
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  };
+  static const hipError_t lds_ok[4] = {
+      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<false, false>), mfma::Rows<false>::kLds),
+      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<true, false>), mfma::Rows<false>::kLds),
+      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<false, true>), mfma::Rows<true>::kLds),
+      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<true, true>), mfma::Rows<true>::kLds)};
+  for (hipError_t le : lds_ok)
+    if (le != hipSuccess) return le;
   hipError_t e;
   int dev = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;

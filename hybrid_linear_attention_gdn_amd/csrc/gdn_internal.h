@@ -21,7 +21,7 @@ enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kPortable = 4u };
 // where each intermediate lives inside the caller's workspace.
 struct Plan {
   int B = 0, T = 0, H = 0, dk = 0, dv = 0, N = 0;  // N = ceil(T / kChunk)
-  int qkv_bf16 = 0, o_bf16 = 0;
+  int qkv_bf16 = 0, qkv_fp8 = 0, o_bf16 = 0;
   uint32_t flags = 0;
   bool mfma = false;
   // byte offsets into the workspace

@@ -1,7 +1,7 @@
 // Kernel "intra" of the MFMA family: the per-chunk operands of the state pass,
 // one workgroup (4 waves) per (b, h, chunk), fully parallel.
 //
-// With raw bf16 rows K, Q of the chunk and fp32 scales (all derived here from
+// With raw bf16 rows K, Q of the chunk (fp8 inputs are widened to bf16 exactly on load) and fp32 scales (all derived here from
 // the raw inputs: rk = 1/||k||, rq = 1/||q||, beta = sigmoid(logit), G = the
 // chunk-local inclusive cumulative floored log-decay):
 //   A_ri = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i)   (i < r)
@@ -70,7 +70,9 @@ __device__ __forceinline__ float lane_value(float x, int l) {
 // e^x on the hardware exp2 (relative error a few ulp for |x| up to ~100)
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
-__global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+// q, k: bf16 or (kFp8) E4M3FN elements, addressed in bytes
+template <bool kFp8>
+__global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ q, const char *__restrict__ k,
                                                        const float *__restrict__ g, const float *__restrict__ beta,
                                                        char *__restrict__ Mout, char *__restrict__ Pout,
                                                        float *__restrict__ CSout, int T, int H, int N,
@@ -118,29 +120,31 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
   // before any is used.
   float *sqk = Pb, *sqq = Pb + C * 14;
   uint16_t *Qr = reinterpret_cast<uint16_t *>(lds + kLdsQr);
-  const uint16_t *kbase = k + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
-  const uint16_t *qbase = q + (size_t(b) * T + t0) * rowstride + size_t(h) * D;
-  constexpr int kRowPieces = (C * 14 + 255) / 256;  // 5 pieces of 16 bytes per thread and matrix
-  uint4 kv[kRowPieces], qv[kRowPieces];
+  constexpr size_t kElem = kFp8 ? 1 : 2;  // bytes per input element
+  const char *kbase = k + ((size_t(b) * T + t0) * rowstride + size_t(h) * D) * kElem;
+  const char *qbase = q + ((size_t(b) * T + t0) * rowstride + size_t(h) * D) * kElem;
+  constexpr int kRowPieces = (C * 14 + 255) / 256;  // 5 pieces of 8 elements per thread and matrix
+  Elems8<kFp8> kraw[kRowPieces], qraw[kRowPieces];
 #pragma unroll
   for (int i = 0; i < kRowPieces; ++i) {
     const int idx = tid + 256 * i, r = idx / 14, cc = idx % 14;
     const bool ok = idx < C * 14 && r < n;
-    kv[i] = ok ? ldg16(kbase + size_t(r) * rowstride + cc * 8) : make_uint4(0, 0, 0, 0);
-    qv[i] = ok ? ldg16(qbase + size_t(r) * rowstride + cc * 8) : make_uint4(0, 0, 0, 0);
+    kraw[i] = ok ? ld_elems8<kFp8>(kbase + (size_t(r) * rowstride + cc * 8) * kElem) : Elems8<kFp8>{};
+    qraw[i] = ok ? ld_elems8<kFp8>(qbase + (size_t(r) * rowstride + cc * 8) * kElem) : Elems8<kFp8>{};
   }
 #pragma unroll
   for (int i = 0; i < kRowPieces; ++i) {
     const int idx = tid + 256 * i, r = idx / 14, cc = idx % 14;
     if (idx < C * 14) {
+      const uint4 kv = elems8_bf16<kFp8>(kraw[i]), qv = elems8_bf16<kFp8>(qraw[i]);
       uint2 *kr = reinterpret_cast<uint2 *>(Kr + r * kKrRow + cc * 8);
       uint2 *qr = reinterpret_cast<uint2 *>(Qr + r * kKrRow + cc * 8);
-      kr[0] = make_uint2(kv[i].x, kv[i].y);
-      kr[1] = make_uint2(kv[i].z, kv[i].w);
-      qr[0] = make_uint2(qv[i].x, qv[i].y);
-      qr[1] = make_uint2(qv[i].z, qv[i].w);
-      const uint32_t w[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
-      const uint32_t wq[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
+      kr[0] = make_uint2(kv.x, kv.y);
+      kr[1] = make_uint2(kv.z, kv.w);
+      qr[0] = make_uint2(qv.x, qv.y);
+      qr[1] = make_uint2(qv.z, qv.w);
+      const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+      const uint32_t wq[4] = {qv.x, qv.y, qv.z, qv.w};
       float pk = 0.f, pq = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -476,16 +480,23 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const uint16_t *__restric
 
 hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs, int c_first, int c_end,
                         hipStream_t stream) {
-  const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k);
+  const char *q = static_cast<const char *>(a.q), *k = static_cast<const char *>(a.k);
   const int n_chunks = c_end - c_first;
   const unsigned blocks = unsigned(p.B) * p.H * unsigned(n_chunks);
   // more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU)
-  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsIntra);
-  if (lds_ok != hipSuccess) return lds_ok;
+  static const hipError_t lds_bf16 = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel<false>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsIntra);
+  static const hipError_t lds_fp8 = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel<true>),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsIntra);
+  if (lds_bf16 != hipSuccess) return lds_bf16;
+  if (lds_fp8 != hipSuccess) return lds_fp8;
   if (n_chunks <= 0) return hipSuccess;
-  intra_kernel<<<dim3(blocks), dim3(256), kLdsIntra, stream>>>(q, k, a.g, a.beta, M, P, cs, p.T, p.H, p.N, c_first,
-                                                              n_chunks, p.flags);
+  if (p.qkv_fp8)
+    intra_kernel<true><<<dim3(blocks), dim3(256), kLdsIntra, stream>>>(q, k, a.g, a.beta, M, P, cs, p.T, p.H, p.N,
+                                                                      c_first, n_chunks, p.flags);
+  else
+    intra_kernel<false><<<dim3(blocks), dim3(256), kLdsIntra, stream>>>(q, k, a.g, a.beta, M, P, cs, p.T, p.H, p.N,
+                                                                       c_first, n_chunks, p.flags);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// MFMA kernel family (shared definitions): bf16 q/k/v, d_k = d_v = 112, fp32 state, on gfx950.
+// MFMA kernel family (shared definitions): bf16 or fp8 (E4M3FN) q/k/v, d_k = d_v = 112, fp32 state, on gfx950.
 //
 // The gated delta rule (the frame-wise Gated DeltaNet of the "SANA-WM"
 // cookbook page, table "Architecture & components") is evaluated chunk by
@@ -38,6 +38,8 @@
 // accumulator pair becomes a B operand without any data movement; every A
 // operand of such a product is read in the same order.
 #pragma once
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -95,6 +97,40 @@ __device__ __forceinline__ void split4(const f32x4 &v, uint32_t *hi, uint32_t *l
 
 __device__ __forceinline__ uint2 ldg8(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
 __device__ __forceinline__ uint4 ldg16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// q, k, v given as OCP E4M3FN codes: every such value is exact in bf16, so the
+// widened rows enter the same bf16 products (and give the same results) as
+// bf16 inputs holding those values.  Four codes (code j in byte j of w) -> four
+// bf16 in two packed words, element order kept.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w) {
+  return make_uint2(fp8x2_to_bf16<false>(w), fp8x2_to_bf16<true>(w));
+}
+// Eight consecutive input elements as loaded (16 bytes of bf16 or 8 bytes of
+// codes), and widened to eight bf16.  Loads and conversions are separate
+// steps so that a batch of loads can be issued before the first conversion
+// waits on its data.
+template <bool kFp8>
+using Elems8 = std::conditional_t<kFp8, uint2, uint4>;
+template <bool kFp8>
+__device__ __forceinline__ Elems8<kFp8> ld_elems8(const char *p) {
+  if constexpr (kFp8)
+    return ldg8(p);
+  else
+    return ldg16(p);
+}
+template <bool kFp8>
+__device__ __forceinline__ uint4 elems8_bf16(const Elems8<kFp8> &x) {
+  if constexpr (kFp8) {
+    const uint2 a = fp8x4_to_bf16(x.x), b = fp8x4_to_bf16(x.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+  } else {
+    return x;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Byte offsets of the fragment-ordered operands inside one chunk-head record.

@@ -26,7 +26,9 @@ def _dtype_code(t: torch.dtype) -> int:
         return L.GDN_F32
     if t == torch.bfloat16:
         return L.GDN_BF16
-    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+    if t == torch.float8_e4m3fn:
+        return L.GDN_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t} (float32, bfloat16 or float8_e4m3fn)")
 
 
 def problem(B, T, H, dk, dv, qkv_dtype, o_dtype, *, beta_is_prob=False, qk_prenormalized=False,

@@ -53,7 +53,7 @@ class Workload:
     heads: int
     frames: int
     frame_tokens: int
-    dtype: str            # "f32" or "bf16": dtype of q, k, v
+    dtype: str            # "f32", "bf16" or "fp8" (E4M3FN): dtype of q, k, v
     seed: int
     calls: int = 1        # streaming: the sequence is split into this many equal calls
     state_std: float = 0.0  # > 0: initial state ~ N(0, state_std^2)
@@ -82,6 +82,10 @@ WORKLOADS = {
                  state_std=0.02, note="10 calls of 3 latent frames (2,640 tokens), state carried"),
         Workload("minute_cfg", 2, HEADS, latent_frames(961), tokens_per_frame(), "bf16", 105,
                  note="guidance pair, 961 pixel frames = 121 latent frames = 106,480 tokens"),
+        Workload("window_2f_fp8", 1, HEADS, latent_frames(9), tokens_per_frame(), "fp8", 106,
+                 note="9 pixel frames = 2 latent frames x 880 tokens, E4M3FN q/k/v"),
+        Workload("clip_241f_fp8", 1, HEADS, latent_frames(241), tokens_per_frame(), "fp8", 107,
+                 note="241 pixel frames = 31 latent frames x 880 = 27,280 tokens, E4M3FN q/k/v"),
     )
 }
 
@@ -107,6 +111,37 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(round_bf16_bits(x))
 
 
+# OCP 8-bit floating point, E4M3FN ("OFP8" specification): 1 sign bit, 4
+# exponent bits (bias 7), 3 mantissa bits; subnormals at exponent 0; no
+# infinities; S.1111.111 is NaN; the largest finite magnitude is 448.
+def _e4m3_magnitudes() -> np.ndarray:
+    """The 127 non-negative finite E4M3FN values, indexed by code 0x00 .. 0x7E."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7))
+
+
+def e4m3_codes_to_f32(codes: np.ndarray) -> np.ndarray:
+    """Decode E4M3FN codes (uint8) to fp32."""
+    codes = np.asarray(codes, np.uint8)
+    mag = np.append(_e4m3_magnitudes(), np.nan)[codes & 0x7F]
+    return np.where(codes & 0x80, -mag, mag).astype(np.float32)
+
+
+def round_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """fp32 -> E4M3FN codes: round to nearest, ties to even (on the mantissa's
+    last bit), saturating at +-448; NaN -> 0x7F."""
+    x = np.asarray(x, np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    with np.errstate(divide="ignore"):
+        e = np.clip(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6, 8)
+    quantum = 2.0 ** (e - 3)
+    qa = np.minimum(np.round(a / quantum) * quantum, 448.0)  # np.round: half to even
+    codes = np.searchsorted(_e4m3_magnitudes(), qa).astype(np.uint8)
+    codes = np.where(np.signbit(x), codes | 0x80, codes).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), codes).astype(np.uint8)
+
+
 def _softplus(x):
     return np.logaddexp(0.0, x)
 
@@ -114,7 +149,8 @@ def _softplus(x):
 @dataclass
 class Inputs:
     """q, k, v as fp32 arrays holding exactly the values the GPU receives
-    (bf16-representable for bf16 workloads); ``*_bits`` hold the bf16 patterns."""
+    (bf16- or E4M3FN-representable); ``*_bits`` hold the bf16 patterns (uint16)
+    or the E4M3FN codes (uint8)."""
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
@@ -155,6 +191,10 @@ def make_inputs(w: Workload, *, seed: int | None = None, seq_len: int | None = N
     if w.dtype == "bf16":
         inp.q_bits, inp.k_bits, inp.v_bits = (round_bf16_bits(a) for a in (q, k, v))
         inp.q, inp.k, inp.v = (bf16_bits_to_f32(bb) for bb in (inp.q_bits, inp.k_bits, inp.v_bits))
+    elif w.dtype == "fp8":
+        # E4M3FN codes in *_bits (uint8)
+        inp.q_bits, inp.k_bits, inp.v_bits = (round_e4m3_codes(a) for a in (q, k, v))
+        inp.q, inp.k, inp.v = (e4m3_codes_to_f32(bb) for bb in (inp.q_bits, inp.k_bits, inp.v_bits))
     return inp
 
 

@@ -67,7 +67,12 @@ typedef enum {
     GDN_ERR_INTERNAL = 5
 } gdn_status_t;
 
-typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+/* GDN_FP8_E4M3: OCP 8-bit float E4M3FN (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, max 448), for q, k, v only, unit scale.  A
+ * per-tensor scale needs no argument: q and k are normalised inside (their
+ * scale cancels) and o and the state are linear in v (a scale on v factors
+ * out of both). */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype_t;
 
 enum {
     GDN_FLAG_BETA_IS_PROB = 1u,     /* beta already holds probabilities: no sigmoid */
@@ -87,9 +92,11 @@ typedef struct {
 } gdn_problem_t;
 
 /*
- * Supported problems.  qkv_dtype = GDN_BF16 with d_k = d_v = 112 (20 x 112 =
- * the DiT's hidden 2240) runs the MFMA kernels.  qkv_dtype = GDN_F32, or the
- * PORTABLE flag, runs the fp32 vector-ALU kernels, which take any
+ * Supported problems.  qkv_dtype = GDN_BF16 or GDN_FP8_E4M3 with d_k = d_v =
+ * 112 (20 x 112 = the DiT's hidden 2240) runs the MFMA kernels; fp8 inputs
+ * are widened exactly to bf16 inside them (the SGLang cookbook's FP8 Stage-1
+ * precision), the state stays fp32.  qkv_dtype = GDN_F32, or the PORTABLE
+ * flag with bf16, runs the fp32 vector-ALU kernels, which take any
  * 1 <= d_k, d_v <= 128.  Other combinations return GDN_ERR_UNSUPPORTED.
  */
 

@@ -17,6 +17,9 @@ def to_device(inp: Inputs, dev="cuda"):
     if inp.dtype == "bf16":
         up = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
         q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+    elif inp.dtype == "fp8":  # E4M3FN codes
+        up8 = lambda codes: torch.from_numpy(codes).to(dev).view(torch.float8_e4m3fn)  # noqa: E731
+        q, k, v = up8(inp.q_bits), up8(inp.k_bits), up8(inp.v_bits)
     else:
         q, k, v = (torch.from_numpy(a).to(dev) for a in (inp.q, inp.k, inp.v))
     g = torch.from_numpy(inp.g).to(dev)

@@ -126,6 +126,19 @@ def test_chunk_step_contract(lib):
     assert b"seq_len" in lib.gdn_last_error()
 
 
+def test_fp8_problems(lib):
+    # E4M3FN q, k, v: the MFMA kernels only (d = 112), same workspace as bf16
+    st, n = _ws(lib, _p(qkv_dtype=L.GDN_FP8_E4M3))
+    assert st == L.GDN_OK and n == _ws(lib, _p())[1]
+    lay = L.WorkspaceLayout()
+    assert lib.gdn_workspace_layout(ctypes.byref(_p(qkv_dtype=L.GDN_FP8_E4M3)), ctypes.byref(lay)) == L.GDN_OK
+    assert lay.mfma == 1
+    assert _ws(lib, _p(qkv_dtype=L.GDN_FP8_E4M3, flags=L.GDN_FLAG_PORTABLE_KERNELS))[0] == L.GDN_ERR_UNSUPPORTED
+    assert b"fp8" in lib.gdn_last_error()
+    assert _ws(lib, _p(qkv_dtype=L.GDN_FP8_E4M3, head_dim_k=64, head_dim_v=64))[0] == L.GDN_ERR_UNSUPPORTED
+    assert _ws(lib, _p(qkv_dtype=3))[0] == L.GDN_ERR_INVALID_ARGUMENT
+
+
 def test_unsupported_head_dim_on_mfma_path(lib):
     p = _p(head_dim_k=128, head_dim_v=128)
     st, _ = _ws(lib, p)

@@ -53,3 +53,37 @@ def test_generator_determinism_and_recipe():
     assert s.state0.shape == (1, 20, 112, 112) and 0.015 < s.state0.std() < 0.025
     t = I.make_inputs(I.WORKLOADS["tiny_fp32"])
     assert t.q_bits is None and t.q.dtype == np.float32 and t.q.shape == (1, 320, 4, 112)
+
+
+# ---- E4M3FN (OCP 8-bit floating point): values fixed by the format's definition
+from hybrid_linear_attention_gdn_amd.inputs import e4m3_codes_to_f32, round_e4m3_codes  # noqa: E402
+
+
+def test_e4m3_landmark_codes():
+    dec = e4m3_codes_to_f32(np.arange(256, dtype=np.uint8))
+    assert dec[0x00] == 0.0 and np.signbit(dec[0x80])
+    assert dec[0x01] == 2.0 ** -9          # smallest subnormal
+    assert dec[0x07] == 7 * 2.0 ** -9      # largest subnormal
+    assert dec[0x08] == 2.0 ** -6          # smallest normal
+    assert dec[0x38] == 1.0 and dec[0xC0] == -2.0 and dec[0x39] == 1.125
+    assert dec[0x7E] == 448.0 and dec[0xFE] == -448.0
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
+    finite = dec[np.isfinite(dec)]
+    assert finite.size == 254
+
+
+def test_e4m3_rounding():
+    codes = round_e4m3_codes(np.array([1.0, 1.0625, 1.1875, 1.09, 500.0, -1e-4, 2.0 ** -10, 3 * 2.0 ** -10,
+                                       -448.0, np.nan], np.float32))
+    # 1.0625 is halfway between 1 (even) and 1.125: even; 1.1875 halfway between 1.125 and 1.25 (even)
+    assert list(codes[:4]) == [0x38, 0x38, 0x3A, 0x39]
+    assert codes[4] == 0x7E                    # saturates at 448
+    assert codes[5] == 0x80                    # rounds to -0
+    assert codes[6] == 0x00 and codes[7] == 0x02  # subnormal ties to even: 0.5 -> 0, 1.5 -> 2 (x 2^-9)
+    assert codes[8] == 0xFE and codes[9] == 0x7F
+
+
+def test_e4m3_round_trip_every_finite_code():
+    c = np.arange(256, dtype=np.uint8)
+    c = c[(c & 0x7F) != 0x7F]
+    np.testing.assert_array_equal(round_e4m3_codes(e4m3_codes_to_f32(c)), c)
