@@ -1,5 +1,5 @@
-"""CPU oracles for the frame-wise Gated DeltaNet forward and the streaming
-attention block -- TEST INFRASTRUCTURE.
+"""CPU oracles for the frame-wise Gated DeltaNet forward (causal and
+bidirectional) and the streaming attention block -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import anything from this package.  The HIP library and its
@@ -17,6 +17,9 @@ Contents
 ``exact``       exact-rational brute force of the product form on tiny inputs.
 ``attention``   fp64 softmax attention of the streaming chunk-causal attention
                 block (sink frames + rolling cache of past blocks).
+``bidirectional`` the dense checkpoint's bidirectional GDN: reverse scan of the
+                same recurrence (decays on the same frame boundaries) plus the
+                forward scan.
 
 Every function pins to something other than itself in ``tests/test_oracle_*``:
 hand-derived values, closed forms, exact rationals, limits and invariants.
