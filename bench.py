@@ -56,10 +56,11 @@ def flops_per_token_head(C: int = 80, d: int = 112) -> float:
     return 6 * d * d + 5 * C * d + C * C / 3
 
 
-def cpu_baseline(w, max_tokens: int, min_seconds: float):
+def cpu_baseline(w, max_tokens: int, min_seconds: float, bidir: bool = False):
     """fp64 oracle on a bounded sample of the same workload: all heads, the first
     `max_tokens` tokens, repeated until `min_seconds` of wall time have passed."""
     from hybrid_linear_attention_gdn_amd.inputs import make_inputs
+    from oracle.bidirectional import bidirectional
     from oracle.recurrence import default_threads, gdn_recurrence
     T = min(w.seq_len, max_tokens)
     inp = make_inputs(w, seq_len=T, frame_tokens=w.frame_tokens)
@@ -67,13 +68,16 @@ def cpu_baseline(w, max_tokens: int, min_seconds: float):
     runs, dt = 0, 0.0
     while runs == 0 or dt < min_seconds:
         t0 = time.perf_counter()
-        gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, nthreads=threads, want_state=True)
+        if bidir:
+            bidirectional(inp.q, inp.k, inp.v, inp.g, inp.beta, nthreads=threads)
+        else:
+            gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, nthreads=threads, want_state=True)
         dt += time.perf_counter() - t0
         runs += 1
     return {"value": runs * w.batch * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.name}: all {w.batch}x{w.heads} (batch, head) units, first {T} of {w.seq_len} tokens, "
                       f"{runs} passes ({runs * w.batch * T * w.heads} token-heads, {dt:.1f} s wall, "
-                      f"fp64 C recurrence)",
+                      f"fp64 C recurrence{', forward and reverse scans' if bidir else ''})",
             "seconds": round(dt, 3)}
 
 
@@ -160,6 +164,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn", action="store_true", help="time the streaming attention block instead of the GDN layer")
+    ap.add_argument("--bidir", action="store_true",
+                    help="time the bidirectional layer (forward + reverse scan, gdn_bidir_fwd) instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, to calibrate memory counters under a profiler)")
@@ -201,6 +207,8 @@ def main():
     row = d * q.element_size()  # bytes of one q/k/v row
     dtype_name = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8_e4m3", torch.float32: "f32"}[q.dtype]
     calls = w.calls
+    if args.bidir and calls != 1:
+        raise SystemExit("--bidir takes a one-call workload (the bidirectional layer sees the whole clip)")
     Tc = T // calls
     o = torch.empty((B, T, H, d), dtype=o_dtype, device=dev)
     st = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
@@ -212,8 +220,13 @@ def main():
         parts = [tuple(t[:, c * Tc:(c + 1) * Tc].contiguous() for t in (q, k, v, g, beta)) for c in range(calls)]
         o_parts = [torch.empty((B, Tc, H, d), dtype=o_dtype, device=dev) for _ in range(calls)]
 
+    if args.bidir:
+        ws = torch.empty(max(gdn.bidir_workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
+
     def step():
-        if calls == 1:
+        if args.bidir:
+            gdn.gdn_bidir_fwd(q, k, v, g, beta, o, portable=args.portable, workspace=ws, stream=stream)
+        elif calls == 1:
             gdn.gdn_fwd(q, k, v, g, beta, s0, st, o, portable=args.portable, workspace=ws, stream=stream)
         else:
             st.copy_(s0)
@@ -245,13 +258,16 @@ def main():
     dom_ms = stages[dom][0]
     dom_calls_per_step = stages[dom][1] / args.steps
     launch_th = token_heads / calls
-    dom_bytes = stage_algorithmic_bytes(dom, o_bytes, mfma, row) * launch_th
-    if dom == "state":
+    # (the bidirectional layer's scans write fp32 o and carry no state in or out)
+    dom_bytes = stage_algorithmic_bytes(dom, 448 if args.bidir else o_bytes, mfma, row) * launch_th
+    if dom == "state" and not args.bidir:
         dom_bytes += 2 * STATE_BYTES * B * H
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    path_bytes = path_algorithmic_bytes(o_bytes, row) * token_heads + 2 * STATE_BYTES * B * H * calls
+    # the bidirectional layer reads its inputs and writes o once (no state in or out)
+    path_bytes = path_algorithmic_bytes(o_bytes, row) * token_heads + (
+        0 if args.bidir else 2 * STATE_BYTES * B * H * calls)
     path_gbs = path_bytes / (ms * 1e-3) / 1e9
-    tflops = flops_per_token_head() * token_heads / (ms * 1e-3) / 1e12
+    tflops = flops_per_token_head() * token_heads * (2 if args.bidir else 1) / (ms * 1e-3) / 1e12
 
     # measured HBM bytes per launch of the dominant kernel (rocprofv3 FETCH_SIZE and
     # WRITE_SIZE, calibrated on a plain copy), valid only for the sources they were taken on
@@ -292,7 +308,8 @@ def main():
         del src, dst
 
     out = {
-        "metric": f"GDN fwd tokens/s per layer (20h×112d, {dtype_name}) + % MFMA peak on 1 MI355X",
+        "metric": (f"GDN {'bidirectional ' if args.bidir else ''}fwd tokens/s per layer (20h×112d, {dtype_name}) "
+                   "+ % MFMA peak on 1 MI355X"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -304,7 +321,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype_name,
         "data": "synthetic (seeded N(0,1) q/k/v/beta logits, frame-wise log-decay -softplus(N(0,1)+2))",
-        "config": {"workload": f"{w.name}: {w.note}", "batch": B, "tokens": T, "heads": H, "head_dim": d,
+        "config": {"workload": f"{w.name}: {w.note}" + (", bidirectional (forward + reverse scan)" if args.bidir
+                                                           else ""), "batch": B, "tokens": T, "heads": H, "head_dim": d,
                    "calls_per_step": calls, "o_dtype": args.o_dtype, "kernels": "mfma" if mfma else "portable",
                    "chunk": 80},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -318,7 +336,7 @@ def main():
         "gdn_per_dit_forward_ms": {"x20_layers": round(20 * ms, 3), "x15_gdn_layers": round(15 * ms, 3)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens, args.cpu_seconds, args.bidir)
     print(json.dumps(out), flush=True)
 
 

@@ -9,13 +9,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsanawm_g
 
 GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP, GDN_ERR_INTERNAL = range(6)
 GDN_F32, GDN_BF16, GDN_FP8_E4M3 = 0, 1, 2
-GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_PORTABLE_KERNELS = 1, 2, 4
+GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_PORTABLE_KERNELS, GDN_FLAG_REVERSE = 1, 2, 4, 8
 
 # every symbol include/sanawm_gdn.h declares
 EXPORTED = ("gdn_chunk_len", "gdn_workspace_bytes", "gdn_fwd", "gdn_chunk_step", "gdn_workspace_layout",
+            "gdn_bidir_workspace_bytes", "gdn_bidir_fwd",
             "gdn_profile_begin", "gdn_profile_end", "gdn_profile_stage_name",
             "gdn_status_string", "gdn_last_error", "gdn_version")
-NUM_STAGES = 4
+NUM_STAGES = 5
 # every symbol include/sanawm_attn.h declares
 EXPORTED_ATTN = ("attn_cache_bytes", "attn_block_fwd")
 
@@ -63,6 +64,10 @@ def load():
     for fn in (lib.gdn_fwd, lib.gdn_chunk_step):
         fn.restype = ctypes.c_int
         fn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_bidir_workspace_bytes.restype = ctypes.c_int
+    lib.gdn_bidir_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+    lib.gdn_bidir_fwd.restype = ctypes.c_int
+    lib.gdn_bidir_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_profile_begin.restype = ctypes.c_int
     lib.gdn_profile_begin.argtypes = []
     lib.gdn_profile_end.restype = ctypes.c_int

@@ -88,7 +88,8 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   if ((p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16 && p->qkv_dtype != GDN_FP8_E4M3) ||
       (p->o_dtype != GDN_F32 && p->o_dtype != GDN_BF16))
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown dtype (qkv=%d, o=%d)", p->qkv_dtype, p->o_dtype);
-  const uint32_t known = GDN_FLAG_BETA_IS_PROB | GDN_FLAG_QK_PRENORMALIZED | GDN_FLAG_PORTABLE_KERNELS;
+  const uint32_t known =
+      GDN_FLAG_BETA_IS_PROB | GDN_FLAG_QK_PRENORMALIZED | GDN_FLAG_PORTABLE_KERNELS | GDN_FLAG_REVERSE;
   if (p->flags & ~known) return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags & ~known);
 
   gdn::Plan P;
@@ -155,6 +156,15 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// The launch sequence of one validated scan.
+hipError_t enqueue(const gdn::Plan &P, const gdn::Args &a) {
+  if (P.T == 0) return gdn::launch_state_passthrough(P, a);
+  if (P.mfma) return gdn::launch_mfma(P, a);
+  hipError_t e = gdn::launch_prep(P, a);
+  if (e == hipSuccess) e = gdn::launch_portable(P, a);
+  return e;
+}
+
 gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *state_in, float *state_out, void *o, void *workspace,
                  size_t workspace_bytes, void *hip_stream, bool chunk_step) {
@@ -162,6 +172,9 @@ gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const voi
   gdn_status_t s = make_plan(p, &P);
   if (s != GDN_OK) return s;
   if (chunk_step) {
+    if (P.flags & GDN_FLAG_REVERSE)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_chunk_step takes no REVERSE flag (the reverse scan needs the "
+                  "next call's first decay)");
     if (!state_in) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_chunk_step needs a non-NULL state_in");
     if (P.T % gdn::kChunk)
       return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_chunk_step needs seq_len %% %d == 0 (got %d)", gdn::kChunk, P.T);
@@ -197,16 +210,82 @@ gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const voi
               static_cast<char *>(workspace),
               static_cast<hipStream_t>(hip_stream),
               profiler().on.load(std::memory_order_relaxed)};
-  hipError_t e;
+  const hipError_t e = enqueue(P, a);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return GDN_OK;
+}
+
+// Workspace of the bidirectional layer: one scan's workspace (reused by both
+// scans, which run one after the other), then the reverse scan's fp32 output
+// and, for bf16 o, the forward scan's fp32 output.
+struct BidirPlan {
+  gdn::Plan scan;
+  size_t off_rev = 0, off_fwd = 0, total = 0;
+};
+
+gdn_status_t make_bidir_plan(const gdn_problem_t *p, BidirPlan *bp) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem descriptor is NULL");
+  if (p->flags & GDN_FLAG_REVERSE)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_bidir_fwd runs both scans itself: no REVERSE flag");
+  BidirPlan B;
+  gdn_status_t s = make_plan(p, &B.scan);
+  if (s != GDN_OK) return s;
+  const gdn::Plan &P = B.scan;
+  size_t n, bytes;
+  if (!mul_ok(size_t(P.B) * size_t(P.H), size_t(P.T), &n) || !mul_ok(n, size_t(P.dv) * sizeof(float), &bytes))
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+  B.off_rev = align_up(P.total);
+  B.off_fwd = align_up(B.off_rev + bytes);
+  B.total = P.T == 0 ? 0 : (P.o_bf16 ? align_up(B.off_fwd + bytes) : B.off_fwd);
+  *bp = B;
+  return GDN_OK;
+}
+
+gdn_status_t run_bidir(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, void *o, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  BidirPlan B;
+  gdn_status_t s = make_bidir_plan(p, &B);
+  if (s != GDN_OK) return s;
+  gdn::Plan &P = B.scan;
   if (P.T == 0) {
-    e = gdn::launch_state_passthrough(P, a);
-  } else {
-    if (P.mfma) {
-      e = gdn::launch_mfma(P, a);
-    } else {
-      e = gdn::launch_prep(P, a);
-      if (e == hipSuccess) e = gdn::launch_portable(P, a);
-    }
+    g_last_error[0] = '\0';
+    return GDN_OK;
+  }
+  const struct {
+    const void *ptr;
+    const char *name;
+  } need[] = {{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {beta, "beta"}, {o, "o"}};
+  for (const auto &n : need) {
+    if (!n.ptr) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is NULL", n.name);
+    if (!aligned16(n.ptr)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n.name);
+  }
+  if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", B.total);
+  if (workspace_bytes < B.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, B.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not %zu-byte aligned", kAlign);
+
+  char *ws = static_cast<char *>(workspace);
+  const bool o_bf16 = P.o_bf16;
+  float *rev_o = reinterpret_cast<float *>(ws + B.off_rev);
+  float *fwd_o = o_bf16 ? reinterpret_cast<float *>(ws + B.off_fwd) : static_cast<float *>(o);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const bool prof = profiler().on.load(std::memory_order_relaxed);
+  // both scans write fp32; the combine kernel writes o in its own type
+  P.o_bf16 = 0;
+  gdn::Args a{q, k, v, g, beta, nullptr, nullptr, fwd_o, ws, st, prof};
+  hipError_t e = enqueue(P, a);
+  if (e == hipSuccess) {
+    gdn::Plan R = P;
+    R.flags |= GDN_FLAG_REVERSE;
+    a.o = rev_o;
+    e = enqueue(R, a);
+  }
+  if (e == hipSuccess) {
+    gdn::stage_begin(a, gdn::kStageCombine);
+    e = gdn::launch_combine(fwd_o, rev_o, o, o_bf16, size_t(P.B) * P.T * P.H * P.dv, st);
+    gdn::stage_end(a, gdn::kStageCombine);
   }
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
@@ -257,6 +336,19 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
                             const float *beta, const float *state_in, float *state_out, void *o,
                             void *workspace, size_t workspace_bytes, void *hip_stream) {
   return run(p, q, k, v, g, beta, state_in, state_out, o, workspace, workspace_bytes, hip_stream, true);
+}
+
+gdn_status_t gdn_bidir_workspace_bytes(const gdn_problem_t *p, size_t *bytes) {
+  if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  BidirPlan B;
+  gdn_status_t s = make_bidir_plan(p, &B);
+  if (s == GDN_OK) *bytes = B.total;
+  return s;
+}
+
+gdn_status_t gdn_bidir_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, void *o, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return run_bidir(p, q, k, v, g, beta, o, workspace, workspace_bytes, hip_stream);
 }
 
 const char *gdn_status_string(gdn_status_t s) {
@@ -390,7 +482,7 @@ gdn_status_t attn_block_fwd(const attn_problem_t *p, int32_t block, const void *
 }
 
 const char *gdn_profile_stage_name(int32_t stage) {
-  static const char *names[gdn::kNumStages] = {"prep", "intra", "state", "output"};
+  static const char *names[gdn::kNumStages] = {"prep", "intra", "state", "output", "combine"};
   return (stage >= 0 && stage < gdn::kNumStages) ? names[stage] : "";
 }
 

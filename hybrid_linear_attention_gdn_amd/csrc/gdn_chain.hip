@@ -142,7 +142,7 @@ struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k 
   F16 t;
 };
 
-template <int W, bool kOutBf16, bool kFp8>
+template <int W, bool kOutBf16, bool kFp8, bool kRev>
 __device__ __forceinline__ void compute_role(const float *__restrict__ state_in, float *state_out,
                                              void *__restrict__ o, int T, int H, int cb, int ce, int b, int h,
                                              int nt, char *lds) {
@@ -441,21 +441,27 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
         o1[s] = mma(Pt[s][0], rl, o1[s]);
         o2[s] = mma(Pt[s][1], rh, o2[s]);
       }
-    const auto ro_ = make_rsrc(static_cast<char *>(o) + (size_t(b) * T + t0) * rowstride * (kOutBf16 ? 2 : 4),
-                               uint32_t(nv) * uint32_t(rowstride) * (kOutBf16 ? 2u : 4u));
+    // the chunk's rows of o: physical rows p0 .. p0 + nv - 1 (logical row r at
+    // p0 + r, or at p0 + nv - 1 - r in the reverse scan)
+    const int p0 = kRev ? T - t0 - nv : t0;
+    constexpr uint32_t kOutBytes = kOutBf16 ? 2u : 4u;
+    const auto ro_ = make_rsrc(static_cast<char *>(o) + (size_t(b) * T + p0) * rowstride * kOutBytes,
+                               uint32_t(nv) * uint32_t(rowstride) * kOutBytes);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < ro.nO) {
         const int R = ro.O[s];
         const f32x4 acc = o0[s] + o1[s] + o2[s];
-        // rows past the chunk's end fall outside the store descriptor and are dropped
+        // rows past the chunk's end are aimed outside the store descriptor and dropped
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t oi = uint32_t(16 * R + 4 * lg + e) * uint32_t(rowstride) + uint32_t(h) * D + 16u * nt + ln;
+          const int r = 16 * R + 4 * lg + e;
+          const uint32_t oi = uint32_t(kRev ? nv - 1 - r : r) * uint32_t(rowstride) + uint32_t(h) * D + 16u * nt + ln;
+          const uint32_t ob = !kRev || r < nv ? oi * kOutBytes : kOutOfRange;
           if constexpr (kOutBf16)
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), ro_, int(oi * 2u), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[e]), ro_, int(ob), 0, 0);
           else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), ro_, int(oi * 4u), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), ro_, int(ob), 0, 0);
         }
       }
     }
@@ -475,7 +481,7 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
 // complete in issue order, so each wait names the number of younger copies
 // that may still be in flight (at most a record share and two row shares:
 // 57 of the 63 the counter holds).
-template <int L, bool kFp8>
+template <int L, bool kFp8, bool kRev>
 __device__ __forceinline__ void copy_role(const char *__restrict__ q, const char *__restrict__ k,
                                           const char *__restrict__ v, const char *__restrict__ Mws,
                                           const char *__restrict__ Pws, const float *__restrict__ CS, int T,
@@ -486,34 +492,40 @@ __device__ __forceinline__ void copy_role(const char *__restrict__ q, const char
   const size_t u = size_t(b) * H + h;
   const uint32_t row_bytes = uint32_t(H) * D * G::kElem;
   const uint32_t head_off = uint32_t(h) * D * G::kElem;
+  // Logical row r of a chunk with nv rows sits at physical row p0 + r (p0 + nv
+  // - 1 - r in the reverse scan) of the buffer that starts at row p0; rows at
+  // or past nv read as zero (forward: they lie past the buffer's end).
+  auto row_ok = [&](int r, int nv) { return !kRev || r < nv; };
+  auto row_at = [&](int r, int nv) { return uint32_t(kRev ? nv - 1 - r : r) * row_bytes; };
   // K / Q: copy i fills 1 KB of LDS rows, lane -> (row, slot lane % kSlots)
   // holding piece slot ^ (row % kSlots); slots past the row's pieces read as zero
-  auto kq_off = [&](int i) {
+  auto kq_off = [&](int i, int nv) {
     constexpr int kRowsPerCopy = 64 / G::kSlots;
     const int r = kRowsPerCopy * i + lane / G::kSlots, p = (lane % G::kSlots) ^ (r % G::kSlots);
-    return p < G::kPieces ? uint32_t(r) * row_bytes + head_off + 16u * p : kOutOfRange;
+    return p < G::kPieces && row_ok(r, nv) ? row_at(r, nv) + head_off + 16u * p : kOutOfRange;
   };
   // V: copy i fills 1 KB of the tile's rows (kVRow bytes each: this tile's 16 columns)
-  auto v_off = [&](int i) {
+  auto v_off = [&](int i, int nv) {
     constexpr int kLanesPerRow = G::kVRow / 16;
     const int r = (64 / kLanesPerRow) * i + lane / kLanesPerRow;
-    return r < C ? uint32_t(r) * row_bytes + head_off + uint32_t(G::kVRow) * nt + 16u * (lane % kLanesPerRow)
-                 : kOutOfRange;
+    return r < C && row_ok(r, nv) ? row_at(r, nv) + head_off + uint32_t(G::kVRow) * nt + 16u * (lane % kLanesPerRow)
+                                  : kOutOfRange;
   };
   // wave 0: K rows; wave 1: Q rows; wave 2: the V tile and the scales
   auto copy_rows = [&](int c) {
     const int t0 = c * C, nv = min(C, T - t0);
-    const size_t base = (size_t(b) * T + t0) * size_t(H) * D * G::kElem;
-    const uint32_t bytes = uint32_t(nv) * row_bytes;  // rows past the end read as zero
+    const int p0 = kRev ? T - t0 - nv : t0;  // first physical row of the chunk
+    const size_t base = (size_t(b) * T + p0) * size_t(H) * D * G::kElem;
+    const uint32_t bytes = uint32_t(nv) * row_bytes;
     char *rb = lds + kLdsRows + (c & 1) * G::kBytes;
     if constexpr (L < 2) {
       const auto rs = make_rsrc((L == 0 ? k : q) + base, bytes);
 #pragma unroll
-      for (int i = 0; i < G::kKQInstr; ++i) copy16(rs, rb + (L == 0 ? G::kK : G::kQ) + 1024 * i, kq_off(i));
+      for (int i = 0; i < G::kKQInstr; ++i) copy16(rs, rb + (L == 0 ? G::kK : G::kQ) + 1024 * i, kq_off(i, nv));
     } else {
       const auto rv = make_rsrc(v + base, bytes);
 #pragma unroll
-      for (int i = 0; i < G::kVInstr; ++i) copy16(rv, rb + G::kV + 1024 * i, v_off(i));
+      for (int i = 0; i < G::kVInstr; ++i) copy16(rv, rb + G::kV + 1024 * i, v_off(i, nv));
       copy16(make_rsrc(CS + (u * N + c) * kCsFloats, kCsFloats * 4), rb + G::kCs, 16u * lane);
     }
   };
@@ -556,7 +568,7 @@ __device__ __forceinline__ void copy_role(const char *__restrict__ q, const char
 // per chunk, each at a fixed per-lane base plus a per-chunk stride, consumed a
 // chunk later.
 constexpr int kAhead = 2;
-template <bool kFp8>
+template <bool kFp8, bool kRev>
 __device__ __forceinline__ void warm_role(const char *__restrict__ q, const char *__restrict__ k,
                                           const char *__restrict__ v, const char *__restrict__ Mws,
                                           const char *__restrict__ Pws, const float *__restrict__ CS,
@@ -588,7 +600,7 @@ __device__ __forceinline__ void warm_role(const char *__restrict__ q, const char
       const char *src = t == 0 ? k : (t == 1 ? q : v);
       base[j] = src + (size_t(b) * T * H + h) * D * kElem +
                 (part == 0 ? 0 : (kFp8 ? 108 : (part == 1 ? 128 : 220)));
-      stride[j] = size_t(C) * row_bytes;
+      stride[j] = 0;  // rows: addressed by physical row below
     }
   }
   uint32_t pf[4] = {0u, 0u, 0u, 0u}, sink = 0;
@@ -598,8 +610,9 @@ __device__ __forceinline__ void warm_role(const char *__restrict__ q, const char
     for (int j = 0; j < 4; ++j) {
       sink ^= pf[j];  // consumed a chunk after its load was issued
       // a row past the end of the last chunk touches the chunk's last row instead
-      const int rr = prow[j] < 0 ? 0 : min(prow[j], T - 1 - cp * C);
-      pf[j] = *reinterpret_cast<const uint32_t *>(base[j] + size_t(cp) * stride[j] + size_t(rr) * row_bytes);
+      const size_t off = prow[j] < 0 ? size_t(cp) * stride[j]
+                                     : size_t(phys_token(min(cp * C + prow[j], T - 1), T, kRev)) * row_bytes;
+      pf[j] = *reinterpret_cast<const uint32_t *>(base[j] + off);
     }
     bare_barrier();
     bare_barrier();
@@ -609,7 +622,7 @@ __device__ __forceinline__ void warm_role(const char *__restrict__ q, const char
   if (T < 0 && sink != 0u) static_cast<uint32_t *>(o)[0] = sink;  // never taken: keeps the touches alive
 }
 
-template <bool kOutBf16, bool kFp8>
+template <bool kOutBf16, bool kFp8, bool kRev>
 __global__ __launch_bounds__(kThreads) void chain_kernel(const char *__restrict__ q,
                                                          const char *__restrict__ k,
                                                          const char *__restrict__ v,
@@ -627,14 +640,14 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const char *__restrict_
   const int b = u / H, h = u % H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wave) {
-    case 0: compute_role<0, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 1: compute_role<1, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 2: compute_role<2, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 3: compute_role<3, kOutBf16, kFp8>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 4: copy_role<0, kFp8>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 5: copy_role<1, kFp8>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 6: copy_role<2, kFp8>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    default: warm_role<kFp8>(q, k, v, Mws, Pws, CS, o, T, H, N, cb, ce, b, h, nt); break;
+    case 0: compute_role<0, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 1: compute_role<1, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 2: compute_role<2, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 3: compute_role<3, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 4: copy_role<0, kFp8, kRev>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 5: copy_role<1, kFp8, kRev>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 6: copy_role<2, kFp8, kRev>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    default: warm_role<kFp8, kRev>(q, k, v, Mws, Pws, CS, o, T, H, N, cb, ce, b, h, nt); break;
   }
 }
 
@@ -675,29 +688,38 @@ void segment_bounds(int N, std::vector<int> &bounds) {
 }
 constexpr int kSegmentMinChunks = 64;
 
-hipError_t launch_chain(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb, int ce,
-                        const float *sin, float *sout, hipStream_t st) {
+template <bool kOutBf16, bool kFp8, bool kRev>
+hipError_t launch_chain_typed(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb,
+                              int ce, const float *sin, float *sout, hipStream_t st) {
   const char *q = static_cast<const char *>(a.q), *k = static_cast<const char *>(a.k),
              *v = static_cast<const char *>(a.v);
   const int units = p.B * p.H;
   const dim3 grid(8u * mfma::NT * unsigned((units + 7) / 8)), block(mfma::kThreads);
-  constexpr int lds16 = mfma::Rows<false>::kLds, lds8 = mfma::Rows<true>::kLds;
-  if (p.qkv_fp8) {
-    if (p.o_bf16)
-      mfma::chain_kernel<true, true><<<grid, block, lds8, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N, cb,
-                                                                ce, units);
-    else
-      mfma::chain_kernel<false, true><<<grid, block, lds8, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N, cb,
-                                                                 ce, units);
-  } else {
-    if (p.o_bf16)
-      mfma::chain_kernel<true, false><<<grid, block, lds16, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N,
-                                                                  cb, ce, units);
-    else
-      mfma::chain_kernel<false, false><<<grid, block, lds16, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H, p.N,
-                                                                   cb, ce, units);
-  }
+  constexpr int lds = mfma::Rows<kFp8>::kLds;
+  // more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU), once per instantiation
+  static const hipError_t lds_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&mfma::chain_kernel<kOutBf16, kFp8, kRev>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  mfma::chain_kernel<kOutBf16, kFp8, kRev><<<grid, block, lds, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H,
+                                                                     p.N, cb, ce, units);
   return hipGetLastError();
+}
+
+template <bool kOutBf16, bool kFp8>
+hipError_t launch_chain_rev(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb,
+                            int ce, const float *sin, float *sout, hipStream_t st) {
+  return (p.flags & kReverse) ? launch_chain_typed<kOutBf16, kFp8, true>(p, a, M, P, cs, cb, ce, sin, sout, st)
+                              : launch_chain_typed<kOutBf16, kFp8, false>(p, a, M, P, cs, cb, ce, sin, sout, st);
+}
+
+hipError_t launch_chain(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb, int ce,
+                        const float *sin, float *sout, hipStream_t st) {
+  if (p.qkv_fp8)
+    return p.o_bf16 ? launch_chain_rev<true, true>(p, a, M, P, cs, cb, ce, sin, sout, st)
+                    : launch_chain_rev<false, true>(p, a, M, P, cs, cb, ce, sin, sout, st);
+  return p.o_bf16 ? launch_chain_rev<true, false>(p, a, M, P, cs, cb, ce, sin, sout, st)
+                  : launch_chain_rev<false, false>(p, a, M, P, cs, cb, ce, sin, sout, st);
 }
 
 }  // namespace
@@ -707,16 +729,6 @@ hipError_t launch_mfma(const Plan &p, const Args &a) {
   char *P = a.ws + p.off_P;
   float *cs = reinterpret_cast<float *>(a.ws + p.off_cs);
   float *seg_state = reinterpret_cast<float *>(a.ws + p.off_Sseg);
-  auto allow = [](const void *f, int bytes) {
-    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  };
-  static const hipError_t lds_ok[4] = {
-      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<false, false>), mfma::Rows<false>::kLds),
-      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<true, false>), mfma::Rows<false>::kLds),
-      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<false, true>), mfma::Rows<true>::kLds),
-      allow(reinterpret_cast<const void *>(&mfma::chain_kernel<true, true>), mfma::Rows<true>::kLds)};
-  for (hipError_t le : lds_ok)
-    if (le != hipSuccess) return le;
   hipError_t e;
   int dev = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;

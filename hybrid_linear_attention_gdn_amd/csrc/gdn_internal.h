@@ -15,7 +15,7 @@ constexpr int kMfmaDim = 112;     // head_dim of the SANA-WM DiT (20 heads x 112
 constexpr float kLogDecayFloor = -80.0f;
 constexpr bool kHaveMfmaPath = true;
 
-enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kPortable = 4u };
+enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kPortable = 4u, kReverse = 8u };
 
 // Everything a launch sequence needs: the problem, the selected kernels and
 // where each intermediate lives inside the caller's workspace.
@@ -43,7 +43,14 @@ struct Args {
 };
 
 // Timing stages (see gdn_profile_begin in include/sanawm_gdn.h).
-enum Stage : int { kStagePrep = 0, kStageIntra = 1, kStageState = 2, kStageOutput = 3, kNumStages = 4 };
+enum Stage : int {
+  kStagePrep = 0,
+  kStageIntra = 1,
+  kStageState = 2,
+  kStageOutput = 3,
+  kStageCombine = 4,
+  kNumStages = 5
+};
 // timing events around a stage, on `stream` (default: the call's stream)
 void stage_begin(const Args &a, Stage s, hipStream_t stream = nullptr);
 void stage_end(const Args &a, Stage s, hipStream_t stream = nullptr);
@@ -53,6 +60,8 @@ hipError_t launch_prep(const Plan &p, const Args &a);
 hipError_t launch_portable(const Plan &p, const Args &a);
 hipError_t launch_mfma(const Plan &p, const Args &a);
 hipError_t launch_state_passthrough(const Plan &p, const Args &a);
+// o = o_type(x + y) over n elements (fp32 x, y; o fp32 or bf16): the two scans of the bidirectional layer
+hipError_t launch_combine(const float *x, const float *y, void *o, bool o_bf16, size_t n, hipStream_t stream);
 
 // Streaming attention block (attn.hip): the validated geometry of one call.
 struct AttnPlan {
@@ -76,6 +85,10 @@ size_t mfma_chunk_bytes_P();
 size_t mfma_chunk_bytes_cs();
 
 // ---- small device helpers shared by the kernel files ----
+// Physical token index of logical token tau: the reverse scan (kReverse)
+// walks the tokens from last to first, every kernel indexing its chunks and
+// rows by the logical order.
+__device__ __forceinline__ int phys_token(int tau, int T, bool rev) { return rev ? T - 1 - tau : tau; }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32

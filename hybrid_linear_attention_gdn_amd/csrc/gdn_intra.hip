@@ -107,12 +107,18 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
   const int ln = lane & 15, lg = lane >> 4;
   const size_t rowstride = size_t(H) * D;  // elements between consecutive tokens
 
-  // ---- (0) raw decays and beta inputs of this chunk (scratch in the D region)
+  // ---- (0) raw decays and beta inputs of this chunk (scratch in the D region).
+  // The reverse scan reads its tokens last to first and takes each token's
+  // decay from its successor in the original order (none for the last token).
+  const bool rev = flags & kReverse;
   float *gl = Dm, *bl = Dm + 80;
   if (tid < C) {
     const bool ok = tid < n;
-    const size_t th = (size_t(b) * T + t0 + tid) * H + h;
-    gl[tid] = ok ? fmaxf(g[th], kLogDecayFloor) : 0.f;
+    const int tau = t0 + tid;
+    const size_t th = (size_t(b) * T + phys_token(tau, T, rev)) * H + h;
+    float gv = 0.f;
+    if (ok) gv = !rev ? g[th] : (tau > 0 ? g[th + H] : 0.f);
+    gl[tid] = ok ? fmaxf(gv, kLogDecayFloor) : 0.f;
     bl[tid] = ok ? beta[th] : 0.f;
   }
   // ---- (1) K and Q rows -> LDS (row-major); partial sums of squares over 14
@@ -121,16 +127,17 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
   float *sqk = Pb, *sqq = Pb + C * 14;
   uint16_t *Qr = reinterpret_cast<uint16_t *>(lds + kLdsQr);
   constexpr size_t kElem = kFp8 ? 1 : 2;  // bytes per input element
-  const char *kbase = k + ((size_t(b) * T + t0) * rowstride + size_t(h) * D) * kElem;
-  const char *qbase = q + ((size_t(b) * T + t0) * rowstride + size_t(h) * D) * kElem;
+  const char *kbase = k + (size_t(b) * T * rowstride + size_t(h) * D) * kElem;
+  const char *qbase = q + (size_t(b) * T * rowstride + size_t(h) * D) * kElem;
   constexpr int kRowPieces = (C * 14 + 255) / 256;  // 5 pieces of 8 elements per thread and matrix
   Elems8<kFp8> kraw[kRowPieces], qraw[kRowPieces];
 #pragma unroll
   for (int i = 0; i < kRowPieces; ++i) {
     const int idx = tid + 256 * i, r = idx / 14, cc = idx % 14;
     const bool ok = idx < C * 14 && r < n;
-    kraw[i] = ok ? ld_elems8<kFp8>(kbase + (size_t(r) * rowstride + cc * 8) * kElem) : Elems8<kFp8>{};
-    qraw[i] = ok ? ld_elems8<kFp8>(qbase + (size_t(r) * rowstride + cc * 8) * kElem) : Elems8<kFp8>{};
+    const size_t off = (size_t(phys_token(t0 + r, T, rev)) * rowstride + cc * 8) * kElem;
+    kraw[i] = ok ? ld_elems8<kFp8>(kbase + off) : Elems8<kFp8>{};
+    qraw[i] = ok ? ld_elems8<kFp8>(qbase + off) : Elems8<kFp8>{};
   }
 #pragma unroll
   for (int i = 0; i < kRowPieces; ++i) {

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, c
                                                     const float *__restrict__ s_rk,
                                                     const float *__restrict__ s_gcum, float *__restrict__ W,
                                                     float *__restrict__ Ut, int T, int H, int dk, int dv,
-                                                    int N) {
+                                                    int N, bool rev) {
   __shared__ float A[C][C + 1];
   __shared__ float Tm[C][C + 1];
   __shared__ float sb[C], srk[C], sG[C];
@@ -61,8 +61,8 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, c
     sG[r] = ok ? s_gcum[sbase + r] : 0.f;
   }
   __syncthreads();
-  auto krow = [&](int r) { return ((size_t(ci.b) * T + ci.t0 + r) * H + ci.h) * size_t(dk); };
-  auto vrow = [&](int r) { return ((size_t(ci.b) * T + ci.t0 + r) * H + ci.h) * size_t(dv); };
+  auto krow = [&](int r) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(dk); };
+  auto vrow = [&](int r) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(dv); };
   // A (strictly lower), padded rows/cols are zero
   for (int idx = threadIdx.x; idx < C * C; idx += blockDim.x) {
     const int r = idx / C, i = idx % C;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void state_kernel(const TIn *__restrict__ k, c
                                                     const float *__restrict__ W, const float *__restrict__ Ut,
                                                     const float *state_in, float *state_out,
                                                     float *__restrict__ U, float *__restrict__ S0, int T, int H,
-                                                    int dk, int dv, int N) {
+                                                    int dk, int dv, int N, bool rev) {
   constexpr int R = 16;
   __shared__ float S[R][kMaxPortableDim + 1];
   __shared__ float Us[C][R + 1];
@@ -171,7 +171,8 @@ __global__ __launch_bounds__(256) void state_kernel(const TIn *__restrict__ k, c
       const int ii = idx / dk, d = idx % dk;
       float s = 0.f;
       for (int r = 0; r < n; ++r)
-        s = fmaf(Us[r][ii] * coef[r], load_f32(k, ((size_t(b) * T + t0 + r) * H + h) * size_t(dk) + d), s);
+        s = fmaf(Us[r][ii] * coef[r], load_f32(k, ((size_t(b) * T + phys_token(t0 + r, T, rev)) * H + h) * size_t(dk) + d),
+                 s);
       S[ii][d] = fmaf(gammaC, S[ii][d], s);
     }
   }
@@ -189,12 +190,13 @@ __global__ __launch_bounds__(256) void output_kernel(const TIn *__restrict__ q, 
                                                      const float *__restrict__ s_rk,
                                                      const float *__restrict__ s_gcum,
                                                      const float *__restrict__ U, const float *__restrict__ S0,
-                                                     TOut *__restrict__ o, int T, int H, int dk, int dv, int N) {
+                                                     TOut *__restrict__ o, int T, int H, int dk, int dv, int N,
+                                                     bool rev) {
   __shared__ float P[C][C + 1];
   __shared__ float sc[C];
   const ChunkIdx ci = chunk_of_block(H, N, T);
   const size_t sbase = (size_t(ci.b) * H + ci.h) * T + ci.t0;
-  auto row = [&](int r, int d) { return ((size_t(ci.b) * T + ci.t0 + r) * H + ci.h) * size_t(d); };
+  auto row = [&](int r, int d) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(d); };
   for (int idx = threadIdx.x; idx < C * C; idx += blockDim.x) {
     const int r = idx / C, i = idx % C;
     float val = 0.f;
@@ -240,26 +242,27 @@ hipError_t launch_typed(const Plan &p, const Args &a) {
   float *U = reinterpret_cast<float *>(a.ws + p.off_U);
   float *S0 = reinterpret_cast<float *>(a.ws + p.off_S0);
   const unsigned chunks = unsigned(p.B) * p.H * p.N;
+  const bool rev = p.flags & kReverse;
   stage_begin(a, kStageIntra);
   intra_kernel<TIn><<<dim3(chunks), dim3(256), 0, a.stream>>>(k, v, beta, rk, gc, W, Ut, p.T, p.H, p.dk, p.dv,
-                                                              p.N);
+                                                              p.N, rev);
   stage_end(a, kStageIntra);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned tiles = unsigned(p.B) * p.H * ((p.dv + 15) / 16);
   stage_begin(a, kStageState);
   state_kernel<TIn><<<dim3(tiles), dim3(256), 0, a.stream>>>(k, rk, gc, W, Ut, a.state_in, a.state_out, U, S0,
-                                                             p.T, p.H, p.dk, p.dv, p.N);
+                                                             p.T, p.H, p.dk, p.dv, p.N, rev);
   stage_end(a, kStageState);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(a, kStageOutput);
   if (p.o_bf16)
     output_kernel<TIn, uint16_t><<<dim3(chunks), dim3(256), 0, a.stream>>>(
-        q, k, rq, rk, gc, U, S0, static_cast<uint16_t *>(a.o), p.T, p.H, p.dk, p.dv, p.N);
+        q, k, rq, rk, gc, U, S0, static_cast<uint16_t *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
   else
     output_kernel<TIn, float><<<dim3(chunks), dim3(256), 0, a.stream>>>(
-        q, k, rq, rk, gc, U, S0, static_cast<float *>(a.o), p.T, p.H, p.dk, p.dv, p.N);
+        q, k, rq, rk, gc, U, S0, static_cast<float *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
   stage_end(a, kStageOutput);
   return hipGetLastError();
 }

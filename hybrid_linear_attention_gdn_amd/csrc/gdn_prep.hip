@@ -26,10 +26,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn *__restrict__ q, co
   const int b = blockIdx.x / N, c = blockIdx.x % N;
   const int t0 = c * kChunk;
   const int n = min(kChunk, T - t0);
+  const bool rev = flags & kReverse;
   // one thread per token-head row; consecutive threads read consecutive rows
   for (int idx = threadIdx.x; idx < n * H; idx += blockDim.x) {
     const int tt = idx / H, h = idx % H;
-    const size_t th = (size_t(b) * T + t0 + tt) * H + h;
+    const size_t th = (size_t(b) * T + phys_token(t0 + tt, T, rev)) * H + h;
     float rq = 1.f, rk = 1.f;
     if (!(flags & kQkPrenormalized)) {
       float sq = 0.f, sk = 0.f;
@@ -49,14 +50,43 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn *__restrict__ q, co
     o_rq[out] = rq;
     o_rk[out] = rk;
   }
-  // chunk-local inclusive cumsum of the floored log-decay, one thread per head
+  // chunk-local inclusive cumsum of the floored log-decay, one thread per head.
+  // The reverse scan takes each token's decay from its successor in the
+  // original order (the same frame boundary), and none for the last token.
   for (int h = threadIdx.x; h < H; h += blockDim.x) {
     float G = 0.f;
     const size_t out = (size_t(b) * H + h) * T + t0;
     for (int tt = 0; tt < n; ++tt) {
-      G += fmaxf(g[(size_t(b) * T + t0 + tt) * H + h], kLogDecayFloor);
+      const int tau = t0 + tt;
+      const float gv = !rev ? g[(size_t(b) * T + tau) * H + h] : (tau > 0 ? g[(size_t(b) * T + T - tau) * H + h] : 0.f);
+      G += fmaxf(gv, kLogDecayFloor);
       o_gcum[out + tt] = G;
     }
+  }
+}
+
+// o = x + y (the forward and reverse scans of the bidirectional layer): four
+// elements per thread and step, the last n % 4 one by one
+// (x may be o itself: each element is read before it is written, by the same thread)
+template <bool kBf16>
+__global__ __launch_bounds__(256) void combine_kernel(const float *x, const float *__restrict__ y, void *o,
+                                                      size_t n) {
+  const size_t n4 = n / 4;
+  const float4 *x4 = reinterpret_cast<const float4 *>(x), *y4 = reinterpret_cast<const float4 *>(y);
+  for (size_t i = blockIdx.x * size_t(blockDim.x) + threadIdx.x; i < n4; i += size_t(gridDim.x) * blockDim.x) {
+    const float4 a = x4[i], b = y4[i];
+    const float4 s = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    if constexpr (kBf16)
+      static_cast<uint2 *>(o)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+    else
+      reinterpret_cast<float4 *>(o)[i] = s;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - 4 * n4) {
+    const size_t i = 4 * n4 + threadIdx.x;
+    if constexpr (kBf16)
+      static_cast<uint16_t *>(o)[i] = f32_to_bf16(x[i] + y[i]);
+    else
+      static_cast<float *>(o)[i] = x[i] + y[i];
   }
 }
 
@@ -84,6 +114,17 @@ hipError_t launch_prep(const Plan &p, const Args &a) {
                                                      static_cast<const float *>(a.k), a.g, a.beta, beta, rq,
                                                      rk, gc, p.T, p.H, p.dk, p.N, p.flags);
   stage_end(a, kStagePrep);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *x, const float *y, void *o, bool o_bf16, size_t n, hipStream_t stream) {
+  // every pointer is 16-byte aligned
+  const size_t want = (n / 4 + 255) / 256;
+  const dim3 grid(unsigned(want < 8192 ? (want ? want : 1) : 8192)), block(256);
+  if (o_bf16)
+    combine_kernel<true><<<grid, block, 0, stream>>>(x, y, o, n);
+  else
+    combine_kernel<false><<<grid, block, 0, stream>>>(x, y, o, n);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-"""Python binding of libsanawm_gdn: ``gdn_fwd`` and ``gdn_chunk_step``.
+"""Python binding of libsanawm_gdn: ``gdn_fwd``, ``gdn_chunk_step`` and ``gdn_bidir_fwd``.
 
 Argument marshalling only.  Every step of the forward runs in the HIP
 kernels behind the C ABI (include/sanawm_gdn.h); PyTorch provides the device
@@ -32,10 +32,11 @@ def _dtype_code(t: torch.dtype) -> int:
 
 
 def problem(B, T, H, dk, dv, qkv_dtype, o_dtype, *, beta_is_prob=False, qk_prenormalized=False,
-            portable=False) -> L.Problem:
+            portable=False, reverse=False) -> L.Problem:
     flags = ((L.GDN_FLAG_BETA_IS_PROB if beta_is_prob else 0) |
              (L.GDN_FLAG_QK_PRENORMALIZED if qk_prenormalized else 0) |
-             (L.GDN_FLAG_PORTABLE_KERNELS if portable else 0))
+             (L.GDN_FLAG_PORTABLE_KERNELS if portable else 0) |
+             (L.GDN_FLAG_REVERSE if reverse else 0))
     return L.Problem(B, T, H, dk, dv, _dtype_code(qkv_dtype), _dtype_code(o_dtype), flags)
 
 
@@ -47,6 +48,12 @@ def _check(status: int):
 def workspace_bytes(p: L.Problem) -> int:
     n = ctypes.c_size_t(0)
     _check(L.load().gdn_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def bidir_workspace_bytes(p: L.Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(L.load().gdn_bidir_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
     return n.value
 
 
@@ -79,7 +86,7 @@ def _ptr(t):
 
 
 def _call(entry, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob, qk_prenormalized,
-          portable, workspace, stream):
+          portable, workspace, stream, reverse=False, bidir=False):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, d_k]")
     B, T, H, dk = q.shape
@@ -104,38 +111,50 @@ def _call(entry, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob
     elif tuple(o.shape) != (B, T, H, dv) or not o.is_contiguous() or o.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("o must be a contiguous float32/bfloat16 tensor of shape [B, T, H, d_v]")
     p = problem(B, T, H, dk, dv, q.dtype, o.dtype, beta_is_prob=beta_is_prob,
-                qk_prenormalized=qk_prenormalized, portable=portable)
-    need = workspace_bytes(p)
+                qk_prenormalized=qk_prenormalized, portable=portable, reverse=reverse)
+    need = bidir_workspace_bytes(p) if bidir else workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    status = entry(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                   _ptr(state_out), _ptr(o), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+    states = () if bidir else (_ptr(state_in), _ptr(state_out))
+    status = entry(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), *states,
+                   _ptr(o), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
                    ctypes.c_void_p(stream.cuda_stream))
     _check(status)
     return o, state_out
 
 
 def gdn_fwd(q, k, v, g, beta, state_in=None, state_out="new", o=None, *, o_dtype=torch.float32,
-            beta_is_prob=False, qk_prenormalized=False, portable=False, workspace=None, stream=None):
-    """Frame-wise GDN forward over q, k [B,T,H,d_k], v [B,T,H,d_v] (bf16 or fp32),
-    g (log-decay), beta (logits) [B,T,H] fp32.  ``state_out``: "new" allocates the
+            beta_is_prob=False, qk_prenormalized=False, portable=False, reverse=False, workspace=None,
+            stream=None):
+    """Frame-wise GDN forward over q, k [B,T,H,d_k], v [B,T,H,d_v] (bf16, fp8 E4M3FN or
+    fp32), g (log-decay), beta (logits) [B,T,H] fp32.  ``state_out``: "new" allocates the
     final state, None skips it, a tensor receives it (may be ``state_in``).
-    Returns (o, state_out)."""
+    ``reverse``: the reverse scan (GDN_FLAG_REVERSE).  Returns (o, state_out)."""
     if isinstance(state_out, str):
         B, _, H, dk = q.shape
         state_out = torch.empty((B, H, v.shape[-1], dk), dtype=torch.float32, device=q.device)
     return _call(L.load().gdn_fwd, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob,
-                 qk_prenormalized, portable, workspace, stream)
+                 qk_prenormalized, portable, workspace, stream, reverse=reverse)
+
+
+def gdn_bidir_fwd(q, k, v, g, beta, o=None, *, o_dtype=torch.float32, beta_is_prob=False,
+                  qk_prenormalized=False, portable=False, workspace=None, stream=None):
+    """Bidirectional layer (gdn_bidir_fwd): the forward scan plus the reverse scan,
+    both from a zero state.  Returns o."""
+    o, _ = _call(L.load().gdn_bidir_fwd, q, k, v, g, beta, None, None, o, o_dtype, beta_is_prob,
+                 qk_prenormalized, portable, workspace, stream, bidir=True)
+    return o
 
 
 def gdn_chunk_step(q, k, v, g, beta, state_in, state_out="new", o=None, *, o_dtype=torch.float32,
-                   beta_is_prob=False, qk_prenormalized=False, portable=False, workspace=None, stream=None):
+                   beta_is_prob=False, qk_prenormalized=False, portable=False, reverse=False, workspace=None,
+                   stream=None):
     """One streaming call: like gdn_fwd with state_in required and T a multiple of
     the chunk length (80), which makes a rollout bitwise equal to one pass."""
     if isinstance(state_out, str):
         B, _, H, dk = q.shape
         state_out = torch.empty((B, H, v.shape[-1], dk), dtype=torch.float32, device=q.device)
     return _call(L.load().gdn_chunk_step, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob,
-                 qk_prenormalized, portable, workspace, stream)
+                 qk_prenormalized, portable, workspace, stream, reverse=reverse)

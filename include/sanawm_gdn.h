@@ -77,7 +77,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype_t;
 enum {
     GDN_FLAG_BETA_IS_PROB = 1u,     /* beta already holds probabilities: no sigmoid */
     GDN_FLAG_QK_PRENORMALIZED = 2u, /* q, k already unit length: no normalisation */
-    GDN_FLAG_PORTABLE_KERNELS = 4u  /* force the fp32 vector-ALU kernels for bf16 too */
+    GDN_FLAG_PORTABLE_KERNELS = 4u, /* force the fp32 vector-ALU kernels for bf16 too */
+    GDN_FLAG_REVERSE = 8u           /* the reverse scan (gdn_fwd only; see below) */
 };
 
 typedef struct {
@@ -133,6 +134,38 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
                             float *state_out, void *o, void *workspace, size_t workspace_bytes,
                             void *hip_stream);
 
+/*
+ * The reverse scan (GDN_FLAG_REVERSE, gdn_fwd only).  The same recurrence run
+ * over the tokens from last to first: S'_t = alpha'_t S'_{t+1} (I - beta_t k_t
+ * k_t^T) + beta_t v_t k_t^T, o_t = S'_t q_t, where alpha'_t = exp(g[t + 1])
+ * for t < T - 1 and alpha'_{T-1} = 1, so that the decays sit on the same
+ * frame boundaries as the forward scan's (with frame-wise g, a token's
+ * contribution to another decays by the gates of the frame starts between
+ * them, on either side).  state_in is the state after the last token, o and
+ * state_out (the state after token 0) keep the layouts above and the original
+ * token order.  gdn_chunk_step rejects the flag: a call's last decay would
+ * come from the next call.
+ *
+ * The bidirectional layer of the dense checkpoint (the SGLang cookbook page
+ * "SANA-WM", serving-mode table, row "Dense bidirectional": one-shot
+ * generation with full bidirectional context).  The pages do not say how the
+ * recurrent mixer is made bidirectional; this library takes the reading
+ *     o_t = o_t(forward scan) + o_t(reverse scan),
+ * both scans from a zero state, on the same q, k, v, g, beta.  A caller that
+ * wants another combination (other inputs per direction, a weighted sum) runs
+ * gdn_fwd with and without GDN_FLAG_REVERSE itself.
+ *
+ * gdn_bidir_fwd: o [B, T, H, d_v] (fp32 or bf16) for every token; the flags
+ * may not include GDN_FLAG_REVERSE.  Both scans accumulate in fp32; for bf16
+ * o the sum is rounded once.  Size the workspace with
+ * gdn_bidir_workspace_bytes (the scan's workspace plus one or two fp32 copies
+ * of o).  Same validation, ownership and asynchrony contract as gdn_fwd.
+ */
+gdn_status_t gdn_bidir_workspace_bytes(const gdn_problem_t *p, size_t *bytes);
+gdn_status_t gdn_bidir_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, void *o, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
 /* Where the intermediates live inside the workspace (byte offsets; 0 size =
  * not used by the selected kernels).  For tests and profiling. */
 typedef struct {
@@ -156,7 +189,7 @@ gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t
  * the number of calls that ran stage i into calls[i] (i < n; unused stages get
  * 0), then releases the events.  Stages: 0 "prep", 1 "intra", 2 "state"
  * (the fused state pass + output on the MFMA path), 3 "output" (portable
- * path only).  The events are the only host resources the library creates.
+ * path only), 4 "combine" (gdn_bidir_fwd's sum of the two scans).  The events are the only host resources the library creates.
  */
 gdn_status_t gdn_profile_begin(void);
 gdn_status_t gdn_profile_end(float *ms, int32_t *calls, int32_t n);

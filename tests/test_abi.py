@@ -139,6 +139,39 @@ def test_fp8_problems(lib):
     assert _ws(lib, _p(qkv_dtype=3))[0] == L.GDN_ERR_INVALID_ARGUMENT
 
 
+def test_reverse_flag_and_bidirectional_host_checks(lib):
+    # the reverse scan: a gdn_fwd flag, same workspace; gdn_chunk_step rejects it
+    rev = _p(flags=L.GDN_FLAG_REVERSE)
+    assert _ws(lib, rev) == _ws(lib, _p())
+    assert _call(lib, "gdn_chunk_step", rev) == L.GDN_ERR_INVALID_ARGUMENT
+    assert b"REVERSE" in lib.gdn_last_error()
+    # the bidirectional layer: the scan's workspace + the reverse scan's fp32 o
+    # (+ the forward scan's for bf16 o), each 256-byte aligned
+    o_bytes = 1 * 160 * 20 * 112 * 4
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    n = ctypes.c_size_t(0)
+    for o_dtype, copies in ((L.GDN_F32, 1), (L.GDN_BF16, 2)):
+        p = _p(o_dtype=o_dtype)
+        assert lib.gdn_bidir_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == L.GDN_OK
+        assert n.value == up(_ws(lib, p)[1]) + copies * up(o_bytes)
+    assert lib.gdn_bidir_workspace_bytes(ctypes.byref(rev), ctypes.byref(n)) == L.GDN_ERR_INVALID_ARGUMENT
+    assert lib.gdn_bidir_workspace_bytes(ctypes.byref(_p(seq_len=0)), ctypes.byref(n)) == L.GDN_OK and n.value == 0
+    vp = lambda x: ctypes.c_void_p(x)  # noqa: E731
+    p = _p()
+    lib.gdn_bidir_workspace_bytes(ctypes.byref(p), ctypes.byref(n))
+    good = dict(q=0x10000, k=0x20000, v=0x30000, g=0x40000, beta=0x50000, o=0x80000, ws=0x100000)
+
+    def bidir(**over):
+        a = dict(good, **over)
+        return lib.gdn_bidir_fwd(ctypes.byref(p), *(vp(a[x]) for x in ("q", "k", "v", "g", "beta", "o", "ws")),
+                                 ctypes.c_size_t(over.get("bytes", n.value)), None)
+    assert bidir(q=None) == L.GDN_ERR_INVALID_ARGUMENT and b"q" in lib.gdn_last_error()
+    assert bidir(o=0x80008) == L.GDN_ERR_INVALID_ARGUMENT
+    assert bidir(bytes=n.value - 1) == L.GDN_ERR_WORKSPACE
+    assert bidir(ws=None) == L.GDN_ERR_WORKSPACE
+    assert lib.gdn_profile_stage_name(4) == b"combine"
+
+
 def test_unsupported_head_dim_on_mfma_path(lib):
     p = _p(head_dim_k=128, head_dim_v=128)
     st, _ = _ws(lib, p)
