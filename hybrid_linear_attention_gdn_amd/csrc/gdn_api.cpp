@@ -216,12 +216,13 @@ gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const voi
   return GDN_OK;
 }
 
-// Workspace of the bidirectional layer: one scan's workspace (reused by both
-// scans, which run one after the other), then the reverse scan's fp32 output
+// Workspace of the bidirectional layer: one scan's workspace, on the MFMA
+// path a second one (the reverse scan's intra kernel runs next to the forward
+// state pass and needs its own records), then the reverse scan's fp32 output
 // and, for bf16 o, the forward scan's fp32 output.
 struct BidirPlan {
   gdn::Plan scan;
-  size_t off_rev = 0, off_fwd = 0, total = 0;
+  size_t off_scan2 = 0, off_rev = 0, off_fwd = 0, total = 0;
 };
 
 gdn_status_t make_bidir_plan(const gdn_problem_t *p, BidirPlan *bp) {
@@ -235,7 +236,8 @@ gdn_status_t make_bidir_plan(const gdn_problem_t *p, BidirPlan *bp) {
   size_t n, bytes;
   if (!mul_ok(size_t(P.B) * size_t(P.H), size_t(P.T), &n) || !mul_ok(n, size_t(P.dv) * sizeof(float), &bytes))
     return fail(GDN_ERR_UNSUPPORTED, "problem too large");
-  B.off_rev = align_up(P.total);
+  B.off_scan2 = align_up(P.total);
+  B.off_rev = P.mfma ? align_up(B.off_scan2 + P.total) : B.off_scan2;
   B.off_fwd = align_up(B.off_rev + bytes);
   B.total = P.T == 0 ? 0 : (P.o_bf16 ? align_up(B.off_fwd + bytes) : B.off_fwd);
   *bp = B;
@@ -275,12 +277,20 @@ gdn_status_t run_bidir(const gdn_problem_t *p, const void *q, const void *k, con
   // both scans write fp32; the combine kernel writes o in its own type
   P.o_bf16 = 0;
   gdn::Args a{q, k, v, g, beta, nullptr, nullptr, fwd_o, ws, st, prof};
-  hipError_t e = enqueue(P, a);
-  if (e == hipSuccess) {
-    gdn::Plan R = P;
-    R.flags |= GDN_FLAG_REVERSE;
-    a.o = rev_o;
-    e = enqueue(R, a);
+  gdn::Plan R = P;
+  R.flags |= GDN_FLAG_REVERSE;
+  hipError_t e;
+  if (P.mfma && gdn::mfma_bidir_overlaps(P)) {
+    gdn::Args ar = a;
+    ar.o = rev_o;
+    ar.ws = ws + B.off_scan2;
+    e = gdn::launch_mfma_bidir(P, a, R, ar);
+  } else {
+    e = enqueue(P, a);
+    if (e == hipSuccess) {
+      a.o = rev_o;
+      e = enqueue(R, a);
+    }
   }
   if (e == hipSuccess) {
     gdn::stage_begin(a, gdn::kStageCombine);

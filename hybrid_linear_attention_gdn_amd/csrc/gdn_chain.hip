@@ -722,7 +722,74 @@ hipError_t launch_chain(const Plan &p, const Args &a, const char *M, const char 
                   : launch_chain_rev<false, false>(p, a, M, P, cs, cb, ce, sin, sout, st);
 }
 
+
+// the current device and its CU count (cached per device)
+hipError_t device_cus(int *dev, int *cus) {
+  hipError_t e;
+  if ((e = hipGetDevice(dev)) != hipSuccess) return e;
+  if (*dev < 0 || *dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if (g_side[*dev].cus < 0 &&
+      hipDeviceGetAttribute(&g_side[*dev].cus, hipDeviceAttributeMultiprocessorCount, *dev) != hipSuccess)
+    g_side[*dev].cus = 0;
+  *cus = g_side[*dev].cus;
+  return hipSuccess;
+}
+
+// the side stream and at least `n` events of device `dev` (caller holds g_side_mu)
+hipError_t side_resources(int dev, int n) {
+  SideResources &R = g_side[dev];
+  hipError_t e;
+  if (!R.side && (e = hipStreamCreateWithFlags(&R.side, hipStreamNonBlocking)) != hipSuccess) {
+    R.side = nullptr;
+    return e;
+  }
+  while (int(R.ev.size()) < n) {
+    hipEvent_t ev;
+    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
+    R.ev.push_back(ev);
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+bool mfma_bidir_overlaps(const Plan &p) {
+  int dev = 0, cus = 0;
+  if (device_cus(&dev, &cus) != hipSuccess) return false;
+  return long(p.B) * p.H * mfma::NT <= cus;
+}
+
+hipError_t launch_mfma_bidir(const Plan &F, const Args &af, const Plan &R, const Args &ar) {
+  char *Mf = af.ws + F.off_M, *Pf = af.ws + F.off_P, *Mr = ar.ws + R.off_M, *Pr = ar.ws + R.off_P;
+  float *csf = reinterpret_cast<float *>(af.ws + F.off_cs), *csr = reinterpret_cast<float *>(ar.ws + R.off_cs);
+  hipError_t e;
+  int dev = 0, cus = 0;
+  if ((e = device_cus(&dev, &cus)) != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if ((e = side_resources(dev, 2)) != hipSuccess) return e;
+  SideResources &S = g_side[dev];
+  // intra (forward) on the caller's stream; the reverse scan's intra on the
+  // side stream once it is done, next to the forward state pass
+  stage_begin(af, kStageIntra);
+  if ((e = mfma::launch_intra(F, af, Mf, Pf, csf, 0, F.N, af.stream)) != hipSuccess) return e;
+  stage_end(af, kStageIntra);
+  if ((e = hipEventRecord(S.ev[0], af.stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(S.side, S.ev[0], 0)) != hipSuccess) return e;
+  stage_begin(af, kStageState);
+  if ((e = launch_chain(F, af, Mf, Pf, csf, 0, F.N, af.state_in, af.state_out, af.stream)) != hipSuccess) return e;
+  stage_end(af, kStageState);
+  stage_begin(ar, kStageIntra, S.side);
+  if ((e = mfma::launch_intra(R, ar, Mr, Pr, csr, 0, R.N, S.side)) != hipSuccess) return e;
+  stage_end(ar, kStageIntra, S.side);
+  if ((e = hipEventRecord(S.ev[1], S.side)) != hipSuccess) return e;
+  // the reverse state pass after both (this wait also joins the side stream back)
+  if ((e = hipStreamWaitEvent(ar.stream, S.ev[1], 0)) != hipSuccess) return e;
+  stage_begin(ar, kStageState);
+  e = launch_chain(R, ar, Mr, Pr, csr, 0, R.N, ar.state_in, ar.state_out, ar.stream);
+  stage_end(ar, kStageState);
+  return e;
+}
 
 hipError_t launch_mfma(const Plan &p, const Args &a) {
   char *M = a.ws + p.off_M;
@@ -730,17 +797,8 @@ hipError_t launch_mfma(const Plan &p, const Args &a) {
   float *cs = reinterpret_cast<float *>(a.ws + p.off_cs);
   float *seg_state = reinterpret_cast<float *>(a.ws + p.off_Sseg);
   hipError_t e;
-  int dev = 0;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int cus;
-  {
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    if (g_side[dev].cus < 0 &&
-        hipDeviceGetAttribute(&g_side[dev].cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      g_side[dev].cus = 0;
-    cus = g_side[dev].cus;
-  }
+  int dev = 0, cus = 0;
+  if ((e = device_cus(&dev, &cus)) != hipSuccess) return e;
   const long chain_blocks = long(p.B) * p.H * mfma::NT;
   if (p.N < kSegmentMinChunks || chain_blocks <= cus) {
     stage_begin(a, kStageIntra);
@@ -757,16 +815,8 @@ hipError_t launch_mfma(const Plan &p, const Args &a) {
   const int segs = int(bounds.size()) - 1;
   // one caller at a time per device enqueues on the shared side stream and events
   std::lock_guard<std::mutex> lk(g_side_mu);
+  if ((e = side_resources(dev, segs + 1)) != hipSuccess) return e;
   SideResources &R = g_side[dev];
-  if (!R.side && (e = hipStreamCreateWithFlags(&R.side, hipStreamNonBlocking)) != hipSuccess) {
-    R.side = nullptr;
-    return e;
-  }
-  while (int(R.ev.size()) < segs + 1) {
-    hipEvent_t ev;
-    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
-    R.ev.push_back(ev);
-  }
   // fork: the side stream starts after the caller's earlier work (the inputs)
   if ((e = hipEventRecord(R.ev[segs], a.stream)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(R.side, R.ev[segs], 0)) != hipSuccess) return e;

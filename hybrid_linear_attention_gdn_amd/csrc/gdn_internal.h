@@ -60,6 +60,12 @@ hipError_t launch_prep(const Plan &p, const Args &a);
 hipError_t launch_portable(const Plan &p, const Args &a);
 hipError_t launch_mfma(const Plan &p, const Args &a);
 hipError_t launch_state_passthrough(const Plan &p, const Args &a);
+// The bidirectional layer on the MFMA path with the reverse scan's intra kernel
+// beside the forward state pass (on a second stream): possible when the state
+// pass leaves CUs free (one round of workgroups).  F and R use separate record
+// regions (af.ws + F.off_*, ar.ws + R.off_*).
+bool mfma_bidir_overlaps(const Plan &p);
+hipError_t launch_mfma_bidir(const Plan &F, const Args &af, const Plan &R, const Args &ar);
 // o = o_type(x + y) over n elements (fp32 x, y; o fp32 or bf16): the two scans of the bidirectional layer
 hipError_t launch_combine(const float *x, const float *y, void *o, bool o_bf16, size_t n, hipStream_t stream);
 

@@ -158,8 +158,9 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
  * gdn_bidir_fwd: o [B, T, H, d_v] (fp32 or bf16) for every token; the flags
  * may not include GDN_FLAG_REVERSE.  Both scans accumulate in fp32; for bf16
  * o the sum is rounded once.  Size the workspace with
- * gdn_bidir_workspace_bytes (the scan's workspace plus one or two fp32 copies
- * of o).  Same validation, ownership and asynchrony contract as gdn_fwd.
+ * gdn_bidir_workspace_bytes: the scan's workspace (twice with the MFMA
+ * kernels, whose reverse scan prepares its operands while the forward scan's
+ * state pass runs) plus one or two fp32 copies of o.  Same validation, ownership and asynchrony contract as gdn_fwd.
  */
 gdn_status_t gdn_bidir_workspace_bytes(const gdn_problem_t *p, size_t *bytes);
 gdn_status_t gdn_bidir_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,

@@ -145,15 +145,18 @@ def test_reverse_flag_and_bidirectional_host_checks(lib):
     assert _ws(lib, rev) == _ws(lib, _p())
     assert _call(lib, "gdn_chunk_step", rev) == L.GDN_ERR_INVALID_ARGUMENT
     assert b"REVERSE" in lib.gdn_last_error()
-    # the bidirectional layer: the scan's workspace + the reverse scan's fp32 o
-    # (+ the forward scan's for bf16 o), each 256-byte aligned
+    # the bidirectional layer: the scan's workspace (twice on the MFMA path) +
+    # the reverse scan's fp32 o (+ the forward scan's for bf16 o), each
+    # 256-byte aligned
     o_bytes = 1 * 160 * 20 * 112 * 4
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     n = ctypes.c_size_t(0)
-    for o_dtype, copies in ((L.GDN_F32, 1), (L.GDN_BF16, 2)):
-        p = _p(o_dtype=o_dtype)
+    for o_dtype, flags, scans, copies in ((L.GDN_F32, 0, 2, 1), (L.GDN_BF16, 0, 2, 2),
+                                          (L.GDN_F32, L.GDN_FLAG_PORTABLE_KERNELS, 1, 1),
+                                          (L.GDN_BF16, L.GDN_FLAG_PORTABLE_KERNELS, 1, 2)):
+        p = _p(o_dtype=o_dtype, flags=flags)
         assert lib.gdn_bidir_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == L.GDN_OK
-        assert n.value == up(_ws(lib, p)[1]) + copies * up(o_bytes)
+        assert n.value == scans * up(_ws(lib, p)[1]) + copies * up(o_bytes)
     assert lib.gdn_bidir_workspace_bytes(ctypes.byref(rev), ctypes.byref(n)) == L.GDN_ERR_INVALID_ARGUMENT
     assert lib.gdn_bidir_workspace_bytes(ctypes.byref(_p(seq_len=0)), ctypes.byref(n)) == L.GDN_OK and n.value == 0
     vp = lambda x: ctypes.c_void_p(x)  # noqa: E731
