@@ -81,6 +81,87 @@ def cpu_baseline(w, max_tokens: int, min_seconds: float, bidir: bool = False):
             "seconds": round(dt, 3)}
 
 
+def layer_bench(args):
+    """The whole layer around the scan (gdn_layer_fwd): in-projection, scan,
+    out-projection on the 241-frame shape (B = 1, 27,280 tokens, 20 heads,
+    880-token frames) with seeded synthetic bf16 weights.  The projections are
+    dense contractions, so their roofline is the bf16 MFMA peak.  Prints one
+    JSON line of its own."""
+    import numpy as np
+    import torch
+
+    from hybrid_linear_attention_gdn_amd import gdn, layer
+    from hybrid_linear_attention_gdn_amd.inputs import make_layer_inputs
+
+    B, T, H, ft = 1, 27280, 20, 880
+    HD = H * 112
+    dev = torch.device("cuda:0")
+    li = make_layer_inputs(B, T, H, ft, 900)
+    up = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    x, w_in, w_out = up(li.x_bits), up(li.w_in_bits), up(li.w_out_bits)
+    y_dtype = torch.float32 if args.o_dtype == "fp32" else torch.bfloat16
+    bidir = args.bidir
+    p = layer.problem(B, T, H, ft, y_dtype, bidir)
+    ws = torch.empty(layer.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    st = None if bidir else torch.zeros((B, H, 112, 112), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        layer.layer_fwd(x, w_in, w_out, ft, st, st, y_dtype=y_dtype, bidirectional=bidir, workspace=ws,
+                        stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gdn.profile_begin()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    stages = gdn.profile_end()
+    ms = start.elapsed_time(end) / args.steps
+    n_in = 3 * HD + 2 * H
+    flops = {"in_proj": 2.0 * B * T * HD * n_in, "out_proj": 2.0 * B * T * HD * HD}
+    proj = {k: {"ms": round(stages[k][0], 5), "tflops": round(flops[k] / (stages[k][0] * 1e-3) / 1e12, 1)}
+            for k in flops if k in stages}
+    dom = "in_proj"
+    achieved = proj[dom]["tflops"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import layer as LY
+        Ts = min(T, 2640)
+        t0 = time.perf_counter()
+        runs = 0
+        while runs == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            LY.layer(li.x[:, :Ts], li.w_in, li.w_out, H, ft, bidirectional_scan=bidir)
+            runs += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(runs * B * Ts / dt, 1), "unit": "tokens/s", "cores": os.cpu_count(),
+               "kind": "oracle", "sample": f"layer: first {Ts} of {T} tokens, all {H} heads, {runs} passes, "
+                                           f"{dt:.1f} s wall (numpy fp64 projections + C recurrence)"}
+    out = {
+        "metric": f"GDN layer (projections + {'bidirectional ' if bidir else ''}scan) tokens/s, 20h x 112d, bf16, "
+                  "on 1 MI355X",
+        "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) x, N(0, 1/2240) weights in bf16)",
+        "config": {"workload": "layer_clip_241f: 27,280 tokens, W_in 6,760 x 2,240, W_out 2,240 x 2,240"
+                               + (", bidirectional scan" if bidir else ""),
+                   "batch": B, "tokens": T, "heads": H, "head_dim": 112, "y_dtype": args.o_dtype},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": proj[dom]["ms"], "launches_per_step": 1.0},
+        "projections": proj,
+        "stages_ms": {k: round(v[0], 5) for k, v in stages.items()},
+    }
+    if cpu:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
 def attn_bench(args):
     """The streaming attention block (include/sanawm_attn.h) at the page geometry:
     880-token frames, 3 frames per block, 2 cached blocks, 1 sink frame, 20
@@ -164,6 +245,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn", action="store_true", help="time the streaming attention block instead of the GDN layer")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the whole layer (projections + scan, gdn_layer_fwd) instead")
     ap.add_argument("--bidir", action="store_true",
                     help="time the bidirectional layer (forward + reverse scan, gdn_bidir_fwd) instead")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -178,6 +261,9 @@ def main():
         sys.exit(2)
     if args.attn:
         attn_bench(args)
+        return
+    if args.layer:
+        layer_bench(args)
         return
 
     import numpy as np

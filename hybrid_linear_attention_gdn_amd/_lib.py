@@ -14,9 +14,11 @@ GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_PORTABLE_KERNELS, GDN
 # every symbol include/sanawm_gdn.h declares
 EXPORTED = ("gdn_chunk_len", "gdn_workspace_bytes", "gdn_fwd", "gdn_chunk_step", "gdn_workspace_layout",
             "gdn_bidir_workspace_bytes", "gdn_bidir_fwd",
+            "gdn_in_proj", "gdn_out_proj", "gdn_layer_workspace_bytes", "gdn_layer_fwd",
             "gdn_profile_begin", "gdn_profile_end", "gdn_profile_stage_name",
             "gdn_status_string", "gdn_last_error", "gdn_version")
-NUM_STAGES = 5
+NUM_STAGES = 7
+GDN_LAYER_BIDIRECTIONAL = 16
 # every symbol include/sanawm_attn.h declares
 EXPORTED_ATTN = ("attn_cache_bytes", "attn_block_fwd")
 
@@ -25,6 +27,11 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class LayerProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("frame_tokens", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class AttnProblem(ctypes.Structure):
@@ -68,6 +75,15 @@ def load():
     lib.gdn_bidir_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
     lib.gdn_bidir_fwd.restype = ctypes.c_int
     lib.gdn_bidir_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    LP = ctypes.POINTER(LayerProblem)
+    lib.gdn_in_proj.restype = ctypes.c_int
+    lib.gdn_in_proj.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_out_proj.restype = ctypes.c_int
+    lib.gdn_out_proj.argtypes = [LP, vp, vp, vp, vp]
+    lib.gdn_layer_workspace_bytes.restype = ctypes.c_int
+    lib.gdn_layer_workspace_bytes.argtypes = [LP, ctypes.POINTER(sz)]
+    lib.gdn_layer_fwd.restype = ctypes.c_int
+    lib.gdn_layer_fwd.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_profile_begin.restype = ctypes.c_int
     lib.gdn_profile_begin.argtypes = []
     lib.gdn_profile_end.restype = ctypes.c_int

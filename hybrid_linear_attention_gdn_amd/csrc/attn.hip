@@ -38,7 +38,7 @@
 // some query of the wave has a new maximum (a wave-uniform branch).
 //
 // Precision: q, k, v enter the matrix cores as the exact bf16 inputs; scores
-// and the softmax are fp32; P is rounded to bf16 (relative 2^-9 per weight)
+// and the softmax are fp32; P is rounded to bf16 (relative 2^-8 at most per weight)
 // for the P V product, accumulated in fp32.
 #include "gdn_mfma_common.h"
 
@@ -48,10 +48,16 @@ namespace gdn {
 namespace attn {
 namespace {
 
+using mfma::bare_barrier;
+using mfma::compute_barrier;
+using mfma::copy16;
 using mfma::F16;
 using mfma::F32;
 using mfma::f32x4;
+using mfma::kOutOfRange;
+using mfma::make_rsrc;
 using mfma::mma;
+using mfma::wait_vm;
 using mfma::zero4;
 
 constexpr int D = 112;
@@ -67,38 +73,16 @@ constexpr int kLdsV = 2 * kKTile;           // two K tile buffers, then two V^T 
 constexpr int kLds = kLdsV + 2 * kVTile;    // 60 KB
 constexpr int kKInstr = kKTile / 1024;      // 16 copies of 1 KB per K tile
 constexpr int kVInstr = kVTile / 1024;      // 14 per V^T tile
-constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), 0x00020000);
-}
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, int(off), 0, 0, 0);
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 // max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of a column)
 __device__ __forceinline__ float lanes4_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ void bare_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void compute_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------------------

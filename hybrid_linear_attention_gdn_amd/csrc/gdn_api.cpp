@@ -348,6 +348,164 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
   return run(p, q, k, v, g, beta, state_in, state_out, o, workspace, workspace_bytes, hip_stream, true);
 }
 
+// ---- the layer around the scan ----
+namespace {
+
+struct LayerPlan {
+  gdn_problem_t scan;  // the inner scan: bf16 q, k, v and o, d = 112
+  int M = 0, H = 0, HD = 0;
+  bool bidir = false, y_bf16 = false;
+  size_t off_q = 0, off_k = 0, off_v = 0, off_beta = 0, off_g = 0, off_o = 0, off_scan = 0, total = 0;
+};
+
+gdn_status_t make_layer_plan(const gdn_layer_t *L, LayerPlan *lp) {
+  if (!L) return fail(GDN_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
+  if (L->batch < 1 || L->seq_len < 0 || L->num_heads < 1 || L->frame_tokens < 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "bad layer shape: batch=%d seq_len=%d heads=%d frame_tokens=%d",
+                L->batch, L->seq_len, L->num_heads, L->frame_tokens);
+  if (L->y_dtype != GDN_F32 && L->y_dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown y dtype %d", L->y_dtype);
+  if (L->flags & ~uint32_t(GDN_LAYER_BIDIRECTIONAL))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown layer flag bits 0x%x", L->flags & ~uint32_t(GDN_LAYER_BIDIRECTIONAL));
+  LayerPlan P;
+  P.H = L->num_heads;
+  P.HD = P.H * gdn::kMfmaDim;
+  P.bidir = L->flags & GDN_LAYER_BIDIRECTIONAL;
+  P.y_bf16 = L->y_dtype == GDN_BF16;
+  const long long M = (long long)L->batch * L->seq_len;
+  // token and column indices of the projection kernels are 32-bit
+  if (M > (1LL << 30) || P.HD > 65536)
+    return fail(GDN_ERR_UNSUPPORTED, "layer too large (tokens %lld, heads %d)", M, P.H);
+  P.M = int(M);
+  P.scan = gdn_problem_t{L->batch, L->seq_len, L->num_heads, gdn::kMfmaDim, gdn::kMfmaDim, GDN_BF16, GDN_BF16, 0u};
+  size_t scan_bytes = 0;
+  BidirPlan Bp;
+  gdn::Plan Sp;
+  gdn_status_t s = P.bidir ? make_bidir_plan(&P.scan, &Bp) : make_plan(&P.scan, &Sp);
+  if (s != GDN_OK) return s;
+  scan_bytes = P.bidir ? Bp.total : Sp.total;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t rows = size_t(M) * P.HD * 2, scal = size_t(M) * P.H * 4;
+  P.off_q = take(rows);
+  P.off_k = take(rows);
+  P.off_v = take(rows);
+  P.off_beta = take(scal);
+  P.off_g = take(scal);
+  P.off_o = take(rows);
+  P.off_scan = take(scan_bytes);
+  P.total = M == 0 ? 0 : off;
+  *lp = P;
+  return GDN_OK;
+}
+
+}  // namespace
+
+gdn_status_t gdn_layer_workspace_bytes(const gdn_layer_t *L, size_t *bytes) {
+  if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  LayerPlan P;
+  gdn_status_t s = make_layer_plan(L, &P);
+  if (s == GDN_OK) *bytes = P.total;
+  return s;
+}
+
+gdn_status_t gdn_in_proj(const gdn_layer_t *L, const void *x, const void *w_in, void *q, void *k, void *v,
+                         float *beta, float *g, void *hip_stream) {
+  LayerPlan P;
+  gdn_status_t s = make_layer_plan(L, &P);
+  if (s != GDN_OK) return s;
+  if (P.M == 0) return GDN_OK;
+  const struct {
+    const void *ptr;
+    const char *name;
+  } need[] = {{x, "x"}, {w_in, "w_in"}, {q, "q"}, {k, "k"}, {v, "v"}, {beta, "beta"}, {g, "g"}};
+  for (const auto &n : need) {
+    if (!n.ptr) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is NULL", n.name);
+    if (!aligned16(n.ptr)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n.name);
+  }
+  gdn::Args a{};
+  a.stream = static_cast<hipStream_t>(hip_stream);
+  a.profile = profiler().on.load(std::memory_order_relaxed);
+  gdn::stage_begin(a, gdn::kStageInProj);
+  const hipError_t e = gdn::proj::launch_in_proj(
+      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_in), P.M, P.H, L->seq_len, L->frame_tokens,
+      static_cast<uint16_t *>(q), static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), beta, g, a.stream);
+  gdn::stage_end(a, gdn::kStageInProj);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return GDN_OK;
+}
+
+gdn_status_t gdn_out_proj(const gdn_layer_t *L, const void *o, const void *w_out, void *y, void *hip_stream) {
+  LayerPlan P;
+  gdn_status_t s = make_layer_plan(L, &P);
+  if (s != GDN_OK) return s;
+  if (P.M == 0) return GDN_OK;
+  const struct {
+    const void *ptr;
+    const char *name;
+  } need[] = {{o, "o"}, {w_out, "w_out"}, {y, "y"}};
+  for (const auto &n : need) {
+    if (!n.ptr) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is NULL", n.name);
+    if (!aligned16(n.ptr)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n.name);
+  }
+  gdn::Args a{};
+  a.stream = static_cast<hipStream_t>(hip_stream);
+  a.profile = profiler().on.load(std::memory_order_relaxed);
+  gdn::stage_begin(a, gdn::kStageOutProj);
+  const hipError_t e = gdn::proj::launch_out_proj(static_cast<const uint16_t *>(o),
+                                                  static_cast<const uint16_t *>(w_out), P.M, P.HD, y, P.y_bf16,
+                                                  a.stream);
+  gdn::stage_end(a, gdn::kStageOutProj);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return GDN_OK;
+}
+
+gdn_status_t gdn_layer_fwd(const gdn_layer_t *L, const void *x, const void *w_in, const void *w_out,
+                           const float *state_in, float *state_out, void *y, void *workspace, size_t workspace_bytes,
+                           void *hip_stream) {
+  LayerPlan P;
+  gdn_status_t s = make_layer_plan(L, &P);
+  if (s != GDN_OK) return s;
+  if (P.bidir && (state_in || state_out))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "the bidirectional layer takes no state_in / state_out");
+  if (P.M == 0) {  // no tokens: the state passes through
+    if (P.bidir) return GDN_OK;
+    return run(&P.scan, nullptr, nullptr, nullptr, nullptr, nullptr, state_in, state_out, nullptr, nullptr, 0,
+               hip_stream, false);
+  }
+  const struct {
+    const void *ptr;
+    const char *name;
+  } need[] = {{x, "x"}, {w_in, "w_in"}, {w_out, "w_out"}, {y, "y"}};
+  for (const auto &n : need) {
+    if (!n.ptr) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is NULL", n.name);
+    if (!aligned16(n.ptr)) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n.name);
+  }
+  if (state_in && !aligned16(state_in)) return fail(GDN_ERR_INVALID_ARGUMENT, "state_in is not 16-byte aligned");
+  if (state_out && !aligned16(state_out))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is not 16-byte aligned");
+  if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", P.total);
+  if (workspace_bytes < P.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, P.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not %zu-byte aligned", kAlign);
+  char *ws = static_cast<char *>(workspace);
+  void *q = ws + P.off_q, *k = ws + P.off_k, *v = ws + P.off_v, *o = ws + P.off_o;
+  float *beta = reinterpret_cast<float *>(ws + P.off_beta), *g = reinterpret_cast<float *>(ws + P.off_g);
+  if ((s = gdn_in_proj(L, x, w_in, q, k, v, beta, g, hip_stream)) != GDN_OK) return s;
+  const size_t scan_ws = P.total - P.off_scan;
+  s = P.bidir ? run_bidir(&P.scan, q, k, v, g, beta, o, ws + P.off_scan, scan_ws, hip_stream)
+              : run(&P.scan, q, k, v, g, beta, state_in, state_out, o, ws + P.off_scan, scan_ws, hip_stream, false);
+  if (s != GDN_OK) return s;
+  return gdn_out_proj(L, o, w_out, y, hip_stream);
+}
+
 gdn_status_t gdn_bidir_workspace_bytes(const gdn_problem_t *p, size_t *bytes) {
   if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes is NULL");
   BidirPlan B;
@@ -492,7 +650,8 @@ gdn_status_t attn_block_fwd(const attn_problem_t *p, int32_t block, const void *
 }
 
 const char *gdn_profile_stage_name(int32_t stage) {
-  static const char *names[gdn::kNumStages] = {"prep", "intra", "state", "output", "combine"};
+  static const char *names[gdn::kNumStages] = {"prep",    "intra",   "state",   "output",
+                                               "combine", "in_proj", "out_proj"};
   return (stage >= 0 && stage < gdn::kNumStages) ? names[stage] : "";
 }
 

@@ -48,39 +48,6 @@ namespace gdn {
 namespace mfma {
 namespace {
 
-// Raw buffer access (gfx9 descriptor, stride 0): an offset at or past
-// `bytes` reads zero and drops a store.
-constexpr uint32_t kOutOfRange = 0x7ffffff0u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), 0x00020000);
-}
-// 16 bytes per lane from buffer offset `off` into LDS at dst + 16 * lane
-// (dst is wave-uniform); an out-of-range lane writes zeros.
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, int(off), 0, 0, 0);
-}
-// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Workgroup barrier for the compute waves that also keeps the scheduler from
-// moving register-only work (the matrix products) across it: each phase's
-// products must stay on their side of the barrier that hands buffers back.
-__device__ __forceinline__ void compute_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
-}
-// Barrier for the waves that touch LDS only through the copy engine (or not
-// at all): no fence, so no wait on the copies still in flight is implied.
-__device__ __forceinline__ void bare_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 struct Roles {
   int nY, Y[2];    // token tiles whose Y = K S^T and R this wave computes (phase A)
   int nQA, QA[1];  // token tiles whose Q S^T it computes in phase A

@@ -49,7 +49,9 @@ enum Stage : int {
   kStageState = 2,
   kStageOutput = 3,
   kStageCombine = 4,
-  kNumStages = 5
+  kStageInProj = 5,
+  kStageOutProj = 6,
+  kNumStages = 7
 };
 // timing events around a stage, on `stream` (default: the call's stream)
 void stage_begin(const Args &a, Stage s, hipStream_t stream = nullptr);
@@ -66,6 +68,14 @@ hipError_t launch_state_passthrough(const Plan &p, const Args &a);
 // regions (af.ws + F.off_*, ar.ws + R.off_*).
 bool mfma_bidir_overlaps(const Plan &p);
 hipError_t launch_mfma_bidir(const Plan &F, const Args &af, const Plan &R, const Args &ar);
+// The layer's projections (proj.hip): x [M, H*112] -> q, k, v [M, H*112] bf16,
+// beta, g [M, H] fp32; o [M, HD] bf16 -> y [M, HD].  Weights are [out, in] bf16.
+namespace proj {
+hipError_t launch_in_proj(const uint16_t *x, const uint16_t *w_in, int M, int H, int T, int frame_tokens,
+                          uint16_t *q, uint16_t *k, uint16_t *v, float *beta, float *g, hipStream_t stream);
+hipError_t launch_out_proj(const uint16_t *o, const uint16_t *w_out, int M, int HD, void *y, bool y_bf16,
+                           hipStream_t stream);
+}  // namespace proj
 // o = o_type(x + y) over n elements (fp32 x, y; o fp32 or bf16): the two scans of the bidirectional layer
 hipError_t launch_combine(const float *x, const float *y, void *o, bool o_bf16, size_t n, hipStream_t stream);
 

@@ -26,8 +26,8 @@
 // Precision: q, k, v enter the matrix cores as the exact bf16 inputs; every
 // derived operand (S, R, M, P', T) is split x = hi + lo with hi = bf16(x),
 // lo = bf16(x - hi) and multiplied as hi*hi + hi*lo + lo*hi (or hi*raw +
-// lo*raw), accumulating in fp32 -- a relative error near 2^-16 per product
-// instead of bf16's 2^-9.
+// lo*raw), accumulating in fp32 -- a relative error near 2^-16 per operand
+// instead of bf16's unit roundoff 2^-8.
 //
 // MFMA lane layouts (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16, lane l,
 // g = l >> 4): A row l & 15 and B column l & 15 hold k = 8g..8g+7 (4g..4g+3
@@ -145,6 +145,40 @@ __device__ __forceinline__ int p_base(int R) {
 }
 __device__ __forceinline__ int p_off32(int R, int kb, int hl) { return p_base(R) + kb * 2048 + hl * 1024; }
 __device__ __forceinline__ int p_off16(int R, int hl) { return p_base(R) + (R / 2) * 2048 + hl * 512; }
+
+// Raw buffer access (gfx9 descriptor, stride 0): an offset at or past
+// `bytes` reads zero and drops a store.
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), int(bytes), 0x00020000);
+}
+// 16 bytes per lane from buffer offset `off` into LDS at dst + 16 * lane
+// (dst is wave-uniform); an out-of-range lane writes zeros.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, int(off), 0, 0, 0);
+}
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier for waves that compute on LDS operands; it also keeps the
+// scheduler from moving register-only work (the matrix products) across it,
+// so each phase's products stay on their side of the barrier that hands
+// buffers back.
+__device__ __forceinline__ void compute_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Barrier for the waves that touch LDS only through the copy engine (or not
+// at all): no fence, so no wait on the copies still in flight is implied.
+__device__ __forceinline__ void bare_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // lower-triangular 16x16 block index (I >= J)
 __device__ __forceinline__ constexpr int tri(int I, int J) { return I * (I + 1) / 2 + J; }

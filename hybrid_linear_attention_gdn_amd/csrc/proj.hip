@@ -1,0 +1,246 @@
+// The GDN layer's projections on the matrix cores: C = A W^T with A [M, K]
+// (tokens x features, bf16) and W [N, K] (the weight in output-major order,
+// bf16), fp32 accumulation, and an epilogue that writes C where the layer
+// wants it (see include/sanawm_gdn.h, "The layer around the scan").
+//
+//   in-projection : [q | k | v | beta | a] = x W_in^T, written as q, k, v
+//                   [B, T, H, 112] bf16 and beta, g [B, T, H] fp32, with the
+//                   frame-wise log-decay g = -softplus(a) on a frame's first
+//                   token and 0 elsewhere
+//   out-projection: y = o W_out^T, fp32 or bf16
+//
+// One workgroup computes a 256 x 256 tile of C with eight waves (2 x 4, each
+// 128 x 64 = 8 x 4 accumulator tiles of v_mfma_f32_16x16x32_bf16).  K runs in
+// steps of 64: the step's A and W rows (32 KB each) are brought into LDS with
+// buffer-to-LDS loads, double-buffered, each wave issuing an eighth of them
+// spread between the products of the step before (one copy every four
+// MFMAs: issuing all eight at once held up the matrix pipe by ~700 cycles).  A staged row is 128 bytes, its
+// 16-byte pieces permuted by row (slot = piece ^ ((row >> 1) & 7)), so the
+// 16-byte fragment reads of 16 consecutive rows fall on distinct banks.
+// Rows past M or N and pieces past K are read as zeros (buffer range checks)
+// and never stored.  Workgroups are mapped XCD by XCD to consecutive tile
+// indices, and tile indices run over groups of eight M bands, M fastest, so
+// the ~32 tiles one XCD runs at a time share both their A bands and their W
+// tiles in that XCD's L2.
+#include "gdn_mfma_common.h"
+
+namespace gdn {
+namespace proj {
+namespace {
+
+using mfma::compute_barrier;
+using mfma::copy16;
+using mfma::F32;
+using mfma::f32x4;
+using mfma::kOutOfRange;
+using mfma::make_rsrc;
+using mfma::mma;
+using mfma::wait_vm;
+using mfma::zero4;
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kNS = 2;                         // stages in the ring
+constexpr int kGroupM = 8;                     // M bands per tile group
+constexpr int kThreads = 512;                  // 8 waves: 2 along M x 4 along N
+constexpr int TM = 8, TN = 4;                  // accumulator tiles per wave (128 x 64)
+constexpr int kRow = BK * 2;                   // 128 bytes per staged row
+constexpr int kPieces = kRow / 16;             // 8
+constexpr int kStage = (BM + BN) * kRow;       // 64 KB: A rows, then W rows
+constexpr int kOutRow = BN * 4 + 16;           // staged fp32 output row (padded: lane groups on distinct banks)
+constexpr int kLds = 128 * kOutRow;            // 130 KB: two K stages, or half of the output tile
+static_assert(kLds >= kNS * kStage, "the output staging reuses the K stages");
+constexpr int kCopies = kStage / 1024 / 8;     // 8 one-KB copies per wave and step
+constexpr int kRowsPerCopy = 1024 / kRow;      // 8
+constexpr int kCopiesA = BM / kRowsPerCopy;    // 32 copies of A rows, then 32 of W rows
+
+// staged rows sharing one 256-byte bank line get different slots
+__device__ __forceinline__ int slot_of(int row, int piece) { return piece ^ ((row / (256 / kRow)) % kPieces); }
+
+// ---- epilogues: store(m, n, x) writes C[m][n .. n + 3] = x[0 .. 3] (m < M,
+// n < N; columns past N are dropped), n a multiple of 4 ----
+struct StoreOut {  // y [M, N] fp32 or bf16, N a multiple of 4
+  void *y;
+  int ldy;
+  bool bf16;
+  __device__ void store(int m, int n, int N, float4 x) const {
+    const size_t i = size_t(m) * ldy + n;
+    if (bf16)
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + i) = make_uint2(pack_bf16x2(x.x, x.y),
+                                                                               pack_bf16x2(x.z, x.w));
+    else
+      *reinterpret_cast<float4 *>(static_cast<float *>(y) + i) = x;
+  }
+};
+
+struct InProj {  // columns: q, k, v (HD each, HD a multiple of 4), beta (H), a (H)
+  uint16_t *q, *k, *v;
+  float *beta, *g;
+  int HD, H, T, frame_tokens;
+  __device__ void one(int m, int n, float x) const {
+    if (n < 3 * HD + H) {
+      beta[size_t(m) * H + (n - 3 * HD)] = x;
+    } else {
+      // softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(e^-|x|)
+      const bool first = (m % T) % frame_tokens == 0;
+      g[size_t(m) * H + (n - 3 * HD - H)] = first ? -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : 0.f;
+    }
+  }
+  __device__ void store(int m, int n, int N, float4 x) const {
+    if (n < 3 * HD) {  // four columns of one of q, k, v
+      const int which = n / HD, c = n - which * HD;
+      uint16_t *dst = which == 0 ? q : (which == 1 ? k : v);
+      *reinterpret_cast<uint2 *>(dst + size_t(m) * HD + c) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+    } else {
+      const float e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < N) one(m, n + i, e[i]);
+    }
+  }
+};
+
+template <class Epi>
+__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const uint16_t *__restrict__ A,
+                                                           const uint16_t *__restrict__ W, int M, int N, int K,
+                                                           int tiles_m, int tiles_n, Epi epi) {
+  extern __shared__ __align__(16) char lds[];
+  // workgroup i runs on XCD i % 8: XCD x takes tiles [x * per, (x + 1) * per)
+  const int per = int(gridDim.x) / 8;
+  const int t = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
+  if (t >= tiles_m * tiles_n) return;
+  const int group = t / (kGroupM * tiles_n), in_group = t % (kGroupM * tiles_n);
+  const int gm = min(kGroupM, tiles_m - group * kGroupM);
+  const int tm = group * kGroupM + in_group % gm, tn = in_group / gm;
+  const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+
+  const uint32_t row_bytes = uint32_t(K) * 2u;
+  const auto ra = make_rsrc(A + size_t(tm) * BM * K, uint32_t(min(BM, M - tm * BM)) * row_bytes);
+  const auto rw = make_rsrc(W + size_t(tn) * BN * K, uint32_t(min(BN, N - tn * BN)) * row_bytes);
+  // copy c (0 .. 31) fills staged rows 16 c' .. 16 c' + 15 of A (c' = c < 16) or W (c' = c - 16)
+  // copy i (0 .. kCopies - 1) of this wave for step `step`
+  auto issue_one = [&](int step, int i) {
+    char *buf = lds + (step % kNS) * kStage;
+    const int k0 = step * BK;
+    const int c = wave * kCopies + i;
+    const bool isw = c >= kCopiesA;
+    const int cc = isw ? c - kCopiesA : c;
+    const int row = kRowsPerCopy * cc + lane / kPieces;
+    const int piece = slot_of(row, lane % kPieces);
+    const uint32_t off = k0 + 8 * piece < K ? uint32_t(row) * row_bytes + uint32_t(k0 + 8 * piece) * 2u
+                                            : kOutOfRange;
+    copy16(isw ? rw : ra, buf + (isw ? BM * kRow : 0) + 1024 * cc, off);
+  };
+  auto issue = [&](int step) {
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) issue_one(step, i);
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+
+  const int steps = (K + BK - 1) / BK;
+#pragma unroll
+  for (int i = 0; i < kNS - 1; ++i)
+    if (i < steps) issue(i);
+  for (int s = 0; s < steps; ++s) {
+    const char *buf = lds + (s % kNS) * kStage;
+    // this wave's copies of step s have landed: the copies of the later steps
+    // already issued (up to kNS - 2 of them) may stay in flight
+    const int later = min(kNS - 2, steps - 1 - s);
+    if (later >= 2)
+      wait_vm<2 * kCopies>();
+    else if (later == 1)
+      wait_vm<kCopies>();
+    else
+      wait_vm<0>();
+    compute_barrier();  // ... every wave's; and the stage of step s - 1 is no longer read
+    // the copies of step s + kNS - 1 go out between this step's products (one
+    // every four MFMAs): issuing them takes time the matrix pipe can use
+    const bool next = s + kNS - 1 < steps;
+#pragma unroll
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      F32 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * 128 + 16 * i + ln;
+        const uint4 x = *reinterpret_cast<const uint4 *>(buf + row * kRow + 16 * slot_of(row, 4 * kb + lg));
+        af[i] = F32{{x.x, x.y, x.z, x.w}};
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * 64 + 16 * j + ln;
+        const uint4 x =
+            *reinterpret_cast<const uint4 *>(buf + BM * kRow + row * kRow + 16 * slot_of(row, 4 * kb + lg));
+        bfr[j] = F32{{x.x, x.y, x.z, x.w}};
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mma(af[i], bfr[j], acc[i][j]);
+        constexpr int kPer = TM * (BK / 32) / kCopies;  // MFMA rows per copy
+        if (next && i % kPer == kPer - 1) issue_one(s + kNS - 1, (kb * TM + i) / kPer);
+      }
+    }
+  }
+  // Output through LDS, half a tile (128 rows x 256 columns, fp32) at a time:
+  // the waves of that half write their accumulators -- tile (i, j) holds rows
+  // 16 i + 4 lg + e of the wave's 128, column 16 j + ln of its 64 -- then every
+  // wave stores whole rows, 16 bytes per lane.
+  float *out = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    compute_barrier();  // the K stages (or the previous half) are no longer read
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            out[(16 * i + 4 * lg + e) * (kOutRow / 4) + wn * 64 + 16 * j + ln] = acc[i][j][e];
+    }
+    compute_barrier();
+    const int n = tn * BN + 4 * lane;
+#pragma unroll 4
+    for (int r = wave; r < 128; r += 8) {
+      const int m = tm * BM + half * 128 + r;
+      if (m < M && n < N) epi.store(m, n, N, *reinterpret_cast<const float4 *>(out + r * (kOutRow / 4) + 4 * lane));
+    }
+  }
+}
+
+template <class Epi>
+hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, int M, int N, int K, const Epi &epi,
+                       hipStream_t stream) {
+  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_nt_kernel<Epi>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  const unsigned grid = 8u * unsigned((tiles_m * tiles_n + 7) / 8);
+  gemm_nt_kernel<Epi><<<dim3(grid), dim3(kThreads), kLds, stream>>>(A, W, M, N, K, tiles_m, tiles_n, epi);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_in_proj(const uint16_t *x, const uint16_t *w_in, int M, int H, int T, int frame_tokens,
+                          uint16_t *q, uint16_t *k, uint16_t *v, float *beta, float *g, hipStream_t stream) {
+  const int HD = H * kMfmaDim;
+  InProj epi{q, k, v, beta, g, HD, H, T, frame_tokens};
+  return launch_gemm(x, w_in, M, 3 * HD + 2 * H, HD, epi, stream);
+}
+
+hipError_t launch_out_proj(const uint16_t *o, const uint16_t *w_out, int M, int HD, void *y, bool y_bf16,
+                           hipStream_t stream) {
+  StoreOut epi{y, HD, y_bf16};
+  return launch_gemm(o, w_out, M, HD, HD, epi, stream);
+}
+
+}  // namespace proj
+}  // namespace gdn

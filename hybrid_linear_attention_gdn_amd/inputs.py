@@ -224,3 +224,32 @@ def make_attn_stream(B: int, H: int, frame_tokens: int, frames_per_block: int, b
     bits = [round_bf16_bits(a) for a in arrs]
     vals = [bf16_bits_to_f32(x) for x in bits]
     return AttnStream(*bits, *vals, block_tokens=frames_per_block * frame_tokens)
+
+
+@dataclass
+class LayerInputs:
+    """x [B, T, H*112] and the layer's weights w_in [3 H 112 + 2 H, H 112],
+    w_out [H 112, H 112] ([out, in] order): bf16 patterns (``*_bits``) and
+    their fp32 values."""
+    x_bits: np.ndarray
+    w_in_bits: np.ndarray
+    w_out_bits: np.ndarray
+    x: np.ndarray
+    w_in: np.ndarray
+    w_out: np.ndarray
+    heads: int
+    frame_tokens: int
+
+
+def make_layer_inputs(B: int, T: int, H: int, frame_tokens: int, seed: int) -> LayerInputs:
+    """Seeded synthetic layer inputs: x ~ N(0, 1), weights ~ N(0, 1 / (H 112))
+    (so every projected value is ~N(0, 1)), drawn in the order x, w_in, w_out
+    and rounded to bf16.  Synthetic: no trained weights exist here."""
+    rng = np.random.default_rng(seed)
+    HD = H * HEAD_DIM
+    x = rng.standard_normal((B, T, HD), dtype=np.float32)
+    w_in = rng.standard_normal((3 * HD + 2 * H, HD), dtype=np.float32) * np.float32(1.0 / np.sqrt(HD))
+    w_out = rng.standard_normal((HD, HD), dtype=np.float32) * np.float32(1.0 / np.sqrt(HD))
+    bits = [round_bf16_bits(a) for a in (x, w_in, w_out)]
+    vals = [bf16_bits_to_f32(b) for b in bits]
+    return LayerInputs(*bits, *vals, heads=H, frame_tokens=frame_tokens)

@@ -167,6 +167,46 @@ gdn_status_t gdn_bidir_fwd(const gdn_problem_t *p, const void *q, const void *k,
                            const float *g, const float *beta, void *o, void *workspace,
                            size_t workspace_bytes, void *hip_stream);
 
+/*
+ * The layer around the scan (projections of the DiT's token mixer).  The
+ * SGLang cookbook page "SANA-WM" (table "Architecture & components") gives
+ * the DiT's width, hidden 2240 = 20 heads x 112, and names the mixer; it does
+ * not print the layer's projections.  Readings taken (plain linear maps, no
+ * biases, weights in [out, in] order, bf16, fp32 accumulation):
+ *   [q | k | v | b | a] = x W_in^T,  W_in [3 H 112 + 2 H, H 112]
+ *     q, k, v  [B, T, H, 112] bf16   (the scan normalises q and k itself)
+ *     beta     = b (the logits the scan passes through its sigmoid)
+ *     g        = -softplus(a) on a frame's first token (t % frame_tokens == 0),
+ *                0 on the others: one log-decay per (frame, head), read from
+ *                the frame's first token -- the frame-wise gate
+ *   o = scan(q, k, v, g, beta)  (bf16, causal with state; or bidirectional)
+ *   y = o W_out^T,  W_out [H 112, H 112],  y [B, T, H 112] fp32 or bf16
+ * Both projections run on hand-written MFMA kernels (256 x 256 tiles).
+ */
+typedef struct {
+    int32_t batch;        /* B >= 1 */
+    int32_t seq_len;      /* T >= 0 */
+    int32_t num_heads;    /* H >= 1; the model width is H * 112 */
+    int32_t frame_tokens; /* tokens per latent frame (880 at 704 x 1280), >= 1 */
+    int32_t y_dtype;      /* GDN_F32 or GDN_BF16 */
+    uint32_t flags;       /* 0, or GDN_LAYER_BIDIRECTIONAL */
+} gdn_layer_t;
+#define GDN_LAYER_BIDIRECTIONAL 16u /* the scan is gdn_bidir_fwd's (no state in or out) */
+
+/* x [B, T, H 112] bf16, w_in [3 H 112 + 2 H, H 112] bf16 -> q, k, v [B, T, H,
+ * 112] bf16 and beta, g [B, T, H] fp32 (all device pointers, 16-byte aligned). */
+gdn_status_t gdn_in_proj(const gdn_layer_t *L, const void *x, const void *w_in, void *q, void *k, void *v,
+                         float *beta, float *g, void *hip_stream);
+/* o [B, T, H 112] bf16, w_out [H 112, H 112] bf16 -> y [B, T, H 112] (y_dtype). */
+gdn_status_t gdn_out_proj(const gdn_layer_t *L, const void *o, const void *w_out, void *y, void *hip_stream);
+/* The whole layer: in-projection, scan, out-projection.  state_in / state_out
+ * as in gdn_fwd (both NULL for the bidirectional layer).  Workspace: q, k, v,
+ * beta, g and o of the layer plus the scan's own (gdn_layer_workspace_bytes). */
+gdn_status_t gdn_layer_workspace_bytes(const gdn_layer_t *L, size_t *bytes);
+gdn_status_t gdn_layer_fwd(const gdn_layer_t *L, const void *x, const void *w_in, const void *w_out,
+                           const float *state_in, float *state_out, void *y, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
 /* Where the intermediates live inside the workspace (byte offsets; 0 size =
  * not used by the selected kernels).  For tests and profiling. */
 typedef struct {
@@ -190,7 +230,8 @@ gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t
  * the number of calls that ran stage i into calls[i] (i < n; unused stages get
  * 0), then releases the events.  Stages: 0 "prep", 1 "intra", 2 "state"
  * (the fused state pass + output on the MFMA path), 3 "output" (portable
- * path only), 4 "combine" (gdn_bidir_fwd's sum of the two scans).  The events are the only host resources the library creates.
+ * path only), 4 "combine" (gdn_bidir_fwd's sum of the two scans), 5 "in_proj", 6
+ * "out_proj" (the layer's projections).  The events are the only host resources the library creates.
  */
 gdn_status_t gdn_profile_begin(void);
 gdn_status_t gdn_profile_end(float *ms, int32_t *calls, int32_t n);

@@ -15,7 +15,11 @@ projection.  Readings taken (plain linear maps without biases, weights in
     o    = the scan over (q, k, v, g, beta) (``recurrence``, or ``bidirectional``)
     y    = o W_out^T                        W_out: [H d, H d]
 
-Everything in fp64 on the values given (no rounding of the intermediates).
+The DiT runs in bf16 (the diffusers "SANA-WM" page loads its checkpoints as
+torch.bfloat16), so q, k, v and o are bf16 tensors between the steps: with
+``bf16_intermediates`` (the default) they are rounded to bf16 (nearest, ties
+to even) where the model stores them.  Everything else is fp64 on the values
+given.
 """
 from __future__ import annotations
 
@@ -25,6 +29,13 @@ from oracle.bidirectional import bidirectional
 from oracle.recurrence import gdn_recurrence
 
 D = 112
+
+
+def round_bf16(x):
+    """x rounded to the nearest bfloat16 (8 significant bits, ties to even),
+    as float64; straight from fp64, without an fp32 step."""
+    m, e = np.frexp(np.asarray(x, np.float64))  # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0), e - 8)
 
 
 def softplus(x):
@@ -46,13 +57,17 @@ def in_proj(x, w_in, H, frame_tokens):
     return q, k, v, beta, g
 
 
-def layer(x, w_in, w_out, H, frame_tokens, state_in=None, *, bidirectional_scan=False):
+def layer(x, w_in, w_out, H, frame_tokens, state_in=None, *, bidirectional_scan=False, bf16_intermediates=True):
     """(y [B, T, H d], exit state or None)."""
     q, k, v, beta, g = in_proj(x, w_in, H, frame_tokens)
+    if bf16_intermediates:
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     B, T = q.shape[:2]
     if bidirectional_scan:
         o, st = bidirectional(q, k, v, g, beta), None
     else:
         o, st = gdn_recurrence(q, k, v, g, beta, state_in)
+    if bf16_intermediates:
+        o = round_bf16(o)
     y = o.reshape(B, T, H * D) @ np.asarray(w_out, np.float64).T
     return y, st

@@ -3,10 +3,10 @@
 
 Bar: max |o - o_ref| <= 1e-2 * rms(o_ref) per block for fp32 o (the bar the
 bf16 GDN path meets).  The kernel takes bf16 inputs exactly, keeps scores and
-the softmax in fp32 and rounds P to bf16 for the P V product (a relative 2^-9
+the softmax in fp32 and rounds P to bf16 for the P V product (at most a relative 2^-8
 per weight): measured maxima are 5e-3 .. 8.5e-3 of rms(o_ref).  For bf16 o the
 bar adds 2^-8 |o_ref| per element, since rounding an element to bf16 moves it
-by at most 2^-9 of itself.  The stream geometries cover every context shape:
+by at most 2^-8 of itself.  The stream geometries cover every context shape:
 the first blocks (no sink segment, partial window), steady state (sink frame
 + two cached blocks + current), ragged 64-key tiles and ragged 128-query tiles."""
 import numpy as np
@@ -32,7 +32,7 @@ def _rel(o, ref):
 
 def _run_stream(B, H, ft, fpb, C, S, blocks, seed, o_dtype=torch.float32, check_blocks=None):
     """Streams `blocks` blocks; returns per checked block max(|o - ref| / (TOL rms + r |ref|)),
-    r = 0 for fp32 o and 2^-8 for bf16 o (whose rounding moves an element by at most 2^-9 of it)."""
+    r = 0 for fp32 o and 2^-8 for bf16 o (whose rounding moves an element by at most 2^-8 of it)."""
     s = make_attn_stream(B, H, ft, fpb, blocks, seed)
     p = attn.problem(B, H, ft, fpb, C, S, o_dtype)
     cache = attn.new_cache(p)

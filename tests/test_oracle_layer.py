@@ -18,6 +18,22 @@ def test_softplus_values():
     np.testing.assert_allclose(LY.softplus(x), want, rtol=1e-15, atol=0)
 
 
+def test_round_bf16_values():
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -9, -(2 - 2.0 ** -9), 3.0e-5, 0.0,
+                  1 + 2.0 ** -8 + 2.0 ** -30])
+    want = [1.0, 1.0, 1 + 2.0 ** -6, 1.0, -2.0, 3.0e-5, 0.0, 1 + 2.0 ** -7]
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to the even 1; 1 + 3 2^-8
+    # halfway between 1 + 2^-7 and 1 + 2^-6 (even); just above a tie rounds up
+    got = LY.round_bf16(x)
+    np.testing.assert_array_equal(got[[0, 1, 2, 3, 4, 6, 7]], np.array(want)[[0, 1, 2, 3, 4, 6, 7]])
+    assert abs(got[5] - 3.0e-5) <= 2.0 ** -8 * 3.0e-5  # within half a bf16 ulp (unit roundoff 2^-8)
+    r = np.random.default_rng(0).normal(size=1000)
+    assert (np.abs(LY.round_bf16(r) - r) <= 2.0 ** -8 * np.abs(r)).all()
+    # exactly 8 significant bits: every result is a multiple of 2^(e - 7) for its binade 2^e
+    m, e = np.frexp(LY.round_bf16(r))
+    np.testing.assert_array_equal(m * 256, np.round(m * 256))
+
+
 def _weights(rng, H):
     HD = H * D
     return rng.normal(size=(3 * HD + 2 * H, HD)) / math.sqrt(HD), rng.normal(size=(HD, HD)) / math.sqrt(HD)
@@ -49,7 +65,7 @@ def test_block_row_order_and_orientation():
     w_in = np.concatenate([np.eye(HD), Pm, 2 * np.eye(HD), np.zeros((H, HD)), 0.1 * np.ones((H, HD))])
     w_out = np.triu(rng.normal(size=(HD, HD)))
     x = rng.normal(size=(1, T, HD))
-    y, st = LY.layer(x, w_in, w_out, H, ft)
+    y, st = LY.layer(x, w_in, w_out, H, ft, bf16_intermediates=False)
     q = x.reshape(1, T, H, D)
     k = x[..., perm].reshape(1, T, H, D)
     a = 0.1 * x.sum(-1, keepdims=True)
@@ -64,8 +80,8 @@ def test_bidirectional_layer_uses_both_scans():
     H, T, ft = 1, 9, 3
     w_in, w_out = _weights(rng, H)
     x = rng.normal(size=(1, T, H * D))
-    yb, none = LY.layer(x, w_in, w_out, H, ft, bidirectional_scan=True)
-    yf, _ = LY.layer(x, w_in, w_out, H, ft)
+    yb, none = LY.layer(x, w_in, w_out, H, ft, bidirectional_scan=True, bf16_intermediates=False)
+    yf, _ = LY.layer(x, w_in, w_out, H, ft, bf16_intermediates=False)
     assert none is None
     # the last token's reverse scan sees only itself: y_b - y_f there is the
     # single-token write of the last token projected through W_out
