@@ -162,26 +162,31 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const uint16_t *__res
     // the copies of step s + kNS - 1 go out between this step's products (one
     // every four MFMAs): issuing them takes time the matrix pipe can use
     const bool next = s + kNS - 1 < steps;
+    // every fragment of the step is read up front, so the reads of the second
+    // 32-deep block are in flight while the first block's products run
+    F32 af[BK / 32][TM], bfr[BK / 32][TN];
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb) {
-      F32 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * 128 + 16 * i + ln;
-        const uint4 x = *reinterpret_cast<const uint4 *>(buf + row * kRow + 16 * slot_of(row, 4 * kb + lg));
-        af[i] = F32{{x.x, x.y, x.z, x.w}};
-      }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int row = wn * 64 + 16 * j + ln;
         const uint4 x =
             *reinterpret_cast<const uint4 *>(buf + BM * kRow + row * kRow + 16 * slot_of(row, 4 * kb + lg));
-        bfr[j] = F32{{x.x, x.y, x.z, x.w}};
+        bfr[kb][j] = F32{{x.x, x.y, x.z, x.w}};
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
+        const int row = wm * 128 + 16 * i + ln;
+        const uint4 x = *reinterpret_cast<const uint4 *>(buf + row * kRow + 16 * slot_of(row, 4 * kb + lg));
+        af[kb][i] = F32{{x.x, x.y, x.z, x.w}};
+      }
+    }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mma(af[i], bfr[j], acc[i][j]);
+    for (int kb = 0; kb < BK / 32; ++kb) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mma(af[kb][i], bfr[kb][j], acc[i][j]);
         constexpr int kPer = TM * (BK / 32) / kCopies;  // MFMA rows per copy
         if (next && i % kPer == kPer - 1) issue_one(s + kNS - 1, (kb * TM + i) / kPer);
       }
