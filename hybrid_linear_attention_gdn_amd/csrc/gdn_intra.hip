@@ -230,142 +230,160 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
     const float4 t = *reinterpret_cast<const float4 *>(p);
     return f32x4{t.x, t.y, t.z, t.w};
   };
-  const int I = 4 - wave;  // block-row of T owned by this wave (4, 3, 2, 1)
-  // K tile I: the B operand of every A_IK (K < I) and both operands of A_II
-  F32 kI[3];
+  // Steps 2 and 3 depend on the wave's block-row I = 4 - wave; they are
+  // instantiated per wave so that the block loops unroll with constant bounds
+  // and the independent tiles' products and loads interleave.
+  auto blockrow = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    constexpr int I = 4 - W;  // block-row of T owned by this wave (4, 3, 2, 1)
+    // K tile I: the B operand of every A_IK (K < I) and both operands of A_II
+    F32 kI[3];
 #pragma unroll
-  for (int kb = 0; kb < 3; ++kb) kI[kb] = kfrag32(16 * I + ln, kb);
-  const F16 kIt = kfrag16(16 * I + ln);
-  // tile with rows from tile Ka of K and the columns held in (b, bt): acc[e] = k_{16Ka+4lg+e} . col_{ln}
-  auto rows_times = [&](int Ka, const F32 *b, const F16 &bt) {
-    f32x4 acc = zero4();
+    for (int kb = 0; kb < 3; ++kb) kI[kb] = kfrag32(16 * I + ln, kb);
+    const F16 kIt = kfrag16(16 * I + ln);
+    // tile with rows from tile Ka of K and the columns held in (b, bt): acc[e] = k_{16Ka+4lg+e} . col_{ln}
+    auto rows_times = [&](int Ka, const F32 *b, const F16 &bt) {
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * Ka + ln, kb), b[kb], acc);
-    return mma(kfrag16(16 * Ka + ln), bt, acc);
-  };
-  // A_{r i} = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i) for i < r, with r = 16Ir + ln, i = 16K + 4lg + e
-  auto a_scale = [&](const f32x4 &acc, int Ir, int K, float *out) {
-    const int r = 16 * Ir + ln;
-    const float fr = sbeta[r] * srk[r], Gr = sG[r];
-    const f32x4 rk4 = ld4(srk + 16 * K + 4 * lg), G4 = ld4(sG + 16 * K + 4 * lg);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * K + 4 * lg + e;
-      out[e] = (i < r) ? fr * rk4[e] * decay(Gr - G4[e]) * acc[e] : 0.f;
-    }
-  };
-  F16 Ah[4], Al[4];  // A_IK, K < I, as 16-deep A-operand fragments (hi, lo)
-#pragma unroll
-  for (int K = 0; K < 4; ++K) {
-    Ah[K] = F16{{0, 0}};
-    Al[K] = F16{{0, 0}};
-    if (K < I) {
-      float v[4];
-      a_scale(rows_times(K, kI, kIt), I, K, v);
-      uint32_t hi[2], lo[2];
-      split4(v, hi, lo);
-      Ah[K] = f16_of(hi);
-      Al[K] = f16_of(lo);
-    }
-  }
-  // diagonal blocks A_II (and A_00 by the last wave) -> LDS, row-major
-  {
-    float v[4];
-    a_scale(rows_times(I, kI, kIt), I, I, v);
-    *reinterpret_cast<float4 *>(Ad + I * kBlkF + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
-    if (wave == 3) {
-      F32 k0[3];
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb) k0[kb] = kfrag32(ln, kb);
-      a_scale(rows_times(0, k0, kfrag16(ln)), 0, 0, v);
-      *reinterpret_cast<float4 *>(Ad + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-  }
-  // P^T tiles (kk-tile It <= query tile Rt): acc[e] = k_{16It+4lg+e} . q_{16Rt+ln}
-#pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2) {
-    const int tix = wave + 4 * s2;
-    if (tix < 15) {
-      int Rt = 0;
-      while (tri(Rt + 1, 0) <= tix) ++Rt;
-      const int It = tix - tri(Rt, 0);
-      F32 qR[3];
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb) qR[kb] = qfrag32(16 * Rt + ln, kb);
-      const f32x4 acc = rows_times(It, qR, qfrag16(16 * Rt + ln));
-      const int r = 16 * Rt + ln;
-      const float fr = srq[r], Gr = sG[r];
-      const f32x4 rk4 = ld4(srk + 16 * It + 4 * lg), G4 = ld4(sG + 16 * It + 4 * lg);
-      float v[4];
+      for (int kb = 0; kb < 3; ++kb) acc = mma(kfrag32(16 * Ka + ln, kb), b[kb], acc);
+      return mma(kfrag16(16 * Ka + ln), bt, acc);
+    };
+    // A_{r i} = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i) for i < r, with r = 16Ir + ln, i = 16K + 4lg + e
+    auto a_scale = [&](const f32x4 &acc, int Ir, int K, float *out) {
+      const int r = 16 * Ir + ln;
+      const float fr = sbeta[r] * srk[r], Gr = sG[r];
+      const f32x4 rk4 = ld4(srk + 16 * K + 4 * lg), G4 = ld4(sG + 16 * K + 4 * lg);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * It + 4 * lg + e;
-        v[e] = (i <= r) ? fr * rk4[e] * decay(Gr - G4[e]) * acc[e] : 0.f;
+        const int i = 16 * K + 4 * lg + e;
+        out[e] = (i < r) ? fr * rk4[e] * decay(Gr - G4[e]) * acc[e] : 0.f;
       }
-      *reinterpret_cast<float4 *>(blk(Pb, Rt, It) + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+    };
+    F16 Ah[4], Al[4];  // A_IK, K < I, as 16-deep A-operand fragments (hi, lo)
+#pragma unroll
+    for (int K = 0; K < 4; ++K) {
+      Ah[K] = F16{{0, 0}};
+      Al[K] = F16{{0, 0}};
+      if (K < I) {
+        float v[4];
+        a_scale(rows_times(K, kI, kIt), I, K, v);
+        uint32_t hi[2], lo[2];
+        split4(v, hi, lo);
+        Ah[K] = f16_of(hi);
+        Al[K] = f16_of(lo);
+      }
     }
-  }
-  __syncthreads();
-  // Q rows are dead: K^T (d-major, for step 4) takes their place, built from the K rows
-  for (int idx = tid; idx < C * 14; idx += 256) {
-    const int r = idx / 14, cc = idx % 14;
-    const uint2 *kr = reinterpret_cast<const uint2 *>(Kr + r * kKrRow + cc * 8);
-    const uint2 lo = kr[0], hi = kr[1];
-    const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+    // diagonal blocks A_II (and A_00 by the last wave) -> LDS, row-major
+    {
+      float v[4];
+      a_scale(rows_times(I, kI, kIt), I, I, v);
+      *reinterpret_cast<float4 *>(Ad + I * kBlkF + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+      if constexpr (W == 3) {
+        F32 k0[3];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) Kt[(cc * 8 + j) * kKtRow + r] = uint16_t(w[j >> 1] >> (16 * (j & 1)));
-  }
-  __syncthreads();  // K rows are dead from here on: their LDS now holds the T blocks
-
-  // ---- (3a) diagonal blocks of T by forward substitution, one column per thread
-  if (tid < C) {
-    const int Ib = tid >> 4, cc = tid & 15;
-    const float *A = Ad + Ib * kBlkF;
-    float xv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) s = fmaf(A[r * kBs + m], xv[m], s);
-      xv[r] = (r < cc) ? 0.f : (r == cc ? 1.f : -s);
+        for (int kb = 0; kb < 3; ++kb) k0[kb] = kfrag32(ln, kb);
+        a_scale(rows_times(0, k0, kfrag16(ln)), 0, 0, v);
+        *reinterpret_cast<float4 *>(Ad + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
-    float *Dr = Dm + Ib * kBlkF;
+    // P^T tiles (kk-tile It <= query tile Rt): acc[e] = k_{16It+4lg+e} . q_{16Rt+ln}
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Dr[r * kBs + cc] = xv[r];
-    float4 *Tr = reinterpret_cast<float4 *>(blk(Tt, Ib, Ib) + cc * kBs);
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int tix = W + 4 * s2;
+      if (tix < 15) {
+        int Rt = 0;
+        while (tri(Rt + 1, 0) <= tix) ++Rt;
+        const int It = tix - tri(Rt, 0);
+        F32 qR[3];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) Tr[q4] = make_float4(xv[4 * q4], xv[4 * q4 + 1], xv[4 * q4 + 2], xv[4 * q4 + 3]);
-  }
-  __syncthreads();
-  // ---- (3b) off-diagonal blocks, one block-distance per step
+        for (int kb = 0; kb < 3; ++kb) qR[kb] = qfrag32(16 * Rt + ln, kb);
+        const f32x4 acc = rows_times(It, qR, qfrag16(16 * Rt + ln));
+        const int r = 16 * Rt + ln;
+        const float fr = srq[r], Gr = sG[r];
+        const f32x4 rk4 = ld4(srk + 16 * It + 4 * lg), G4 = ld4(sG + 16 * It + 4 * lg);
+        float v[4];
 #pragma unroll
-  for (int L = 1; L < CT; ++L) {
-    const int J = I - L;
-    if (J >= 0) {
-      f32x4 X = zero4();
-#pragma unroll
-      for (int K = 0; K < 4; ++K) {
-        if (K >= J && K < I) {
-          // B operand T_KJ: lane (column jj = ln, group lg) holds T[16K + 4lg + j][16J + ln]
-          uint32_t th[2], tl[2];
-          split4(ld4(blk(Tt, K, J) + ln * kBs + 4 * lg), th, tl);
-          const F16 bh = f16_of(th), bl = f16_of(tl);
-          X = mma(Ah[K], bh, X);
-          X = mma(Ah[K], bl, X);
-          X = mma(Al[K], bh, X);
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * It + 4 * lg + e;
+          v[e] = (i <= r) ? fr * rk4[e] * decay(Gr - G4[e]) * acc[e] : 0.f;
         }
+        *reinterpret_cast<float4 *>(blk(Pb, Rt, It) + ln * kBs + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
       }
-      uint32_t xh[2], xl[2], dh[2], dl[2];
-      split4(X, xh, xl);
-      split4(ld4(Dm + I * kBlkF + ln * kBs + 4 * lg), dh, dl);
-      f32x4 Tij = zero4();
-      Tij = mma(f16_of(dh), f16_of(xh), Tij);
-      Tij = mma(f16_of(dh), f16_of(xl), Tij);
-      Tij = mma(f16_of(dl), f16_of(xh), Tij);
-      // accumulator: column jj = ln, rows ii = 4lg + e -> T[16I + 4lg + e][16J + ln]
-      *reinterpret_cast<float4 *>(blk(Tt, I, J) + ln * kBs + 4 * lg) = make_float4(-Tij[0], -Tij[1], -Tij[2], -Tij[3]);
     }
     __syncthreads();
+    // Q rows are dead: K^T (d-major, for step 4) takes their place, built from the
+    // K rows two tokens at a time (one 32-bit LDS write per d), consecutive lanes
+    // on consecutive token pairs of the same 8 columns
+    for (int idx = tid; idx < (C / 2) * 14; idx += 256) {
+      const int r = 2 * (idx % (C / 2)), cc = idx / (C / 2);
+      const uint2 *k0 = reinterpret_cast<const uint2 *>(Kr + r * kKrRow + cc * 8);
+      const uint2 *k1 = reinterpret_cast<const uint2 *>(Kr + (r + 1) * kKrRow + cc * 8);
+      const uint2 a0 = k0[0], a1 = k0[1], b0 = k1[0], b1 = k1[1];
+      const uint32_t wa[4] = {a0.x, a0.y, a1.x, a1.y}, wb[4] = {b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t lo = (wa[j >> 1] >> (16 * (j & 1))) & 0xffffu, hi = (wb[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        *reinterpret_cast<uint32_t *>(Kt + (cc * 8 + j) * kKtRow + r) = lo | (hi << 16);
+      }
+    }
+    __syncthreads();  // K rows are dead from here on: their LDS now holds the T blocks
+
+    // ---- (3a) diagonal blocks of T by forward substitution, one column per thread
+    if (tid < C) {
+      const int Ib = tid >> 4, cc = tid & 15;
+      const float *A = Ad + Ib * kBlkF;
+      float xv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) s = fmaf(A[r * kBs + m], xv[m], s);
+        xv[r] = (r < cc) ? 0.f : (r == cc ? 1.f : -s);
+      }
+      float *Dr = Dm + Ib * kBlkF;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Dr[r * kBs + cc] = xv[r];
+      float4 *Tr = reinterpret_cast<float4 *>(blk(Tt, Ib, Ib) + cc * kBs);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) Tr[q4] = make_float4(xv[4 * q4], xv[4 * q4 + 1], xv[4 * q4 + 2], xv[4 * q4 + 3]);
+    }
+    __syncthreads();
+    // ---- (3b) off-diagonal blocks, one block-distance per step
+#pragma unroll
+    for (int L = 1; L < CT; ++L) {
+      const int J = I - L;
+      if (J >= 0) {
+        f32x4 X = zero4();
+#pragma unroll
+        for (int K = 0; K < 4; ++K) {
+          if (K >= J && K < I) {
+            // B operand T_KJ: lane (column jj = ln, group lg) holds T[16K + 4lg + j][16J + ln]
+            uint32_t th[2], tl[2];
+            split4(ld4(blk(Tt, K, J) + ln * kBs + 4 * lg), th, tl);
+            const F16 bh = f16_of(th), bl = f16_of(tl);
+            X = mma(Ah[K], bh, X);
+            X = mma(Ah[K], bl, X);
+            X = mma(Al[K], bh, X);
+          }
+        }
+        uint32_t xh[2], xl[2], dh[2], dl[2];
+        split4(X, xh, xl);
+        split4(ld4(Dm + I * kBlkF + ln * kBs + 4 * lg), dh, dl);
+        f32x4 Tij = zero4();
+        Tij = mma(f16_of(dh), f16_of(xh), Tij);
+        Tij = mma(f16_of(dh), f16_of(xl), Tij);
+        Tij = mma(f16_of(dl), f16_of(xh), Tij);
+        // accumulator: column jj = ln, rows ii = 4lg + e -> T[16I + 4lg + e][16J + ln]
+        *reinterpret_cast<float4 *>(blk(Tt, I, J) + ln * kBs + 4 * lg) = make_float4(-Tij[0], -Tij[1], -Tij[2], -Tij[3]);
+      }
+      __syncthreads();
+    }
+  };
+  switch (wave) {
+    case 0: blockrow(std::integral_constant<int, 0>{}); break;
+    case 1: blockrow(std::integral_constant<int, 1>{}); break;
+    case 2: blockrow(std::integral_constant<int, 2>{}); break;
+    default: blockrow(std::integral_constant<int, 3>{}); break;
   }
 
   // ---- (4) M^T = T^T diag(s) K  and  P'^T = T^T P^T, split and stored.
