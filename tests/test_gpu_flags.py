@@ -1,0 +1,63 @@
+"""GPU parity of the scan's input flags (include/sanawm_gdn.h): beta given as
+probabilities (GDN_FLAG_BETA_IS_PROB) and q, k given already normalised
+(GDN_FLAG_QK_PRENORMALIZED), alone and together, forward and reverse, on both
+kernel families, against the fp64 oracle run with the same flags."""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_linear_attention_gdn_amd import gdn
+from hybrid_linear_attention_gdn_amd.inputs import Workload, bf16_bits_to_f32, make_inputs, round_bf16_bits
+from oracle import bidirectional as BD
+from oracle.recurrence import gdn_recurrence
+from tests.helpers import TOL_BF16, rel_max_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _flagged_inputs(T, seed):
+    w = Workload("flags", 1, 4, 1, 10**9, "bf16", seed, state_std=0.05)
+    inp = make_inputs(w, seq_len=T, frame_tokens=97)
+    # probabilities in (0, 1); unit-length q, k, then stored in bf16 (the scan
+    # uses the stored values as they are)
+    inp.beta = (1.0 / (1.0 + np.exp(-inp.beta.astype(np.float64)))).astype(np.float32)
+    for name in ("q", "k"):
+        x = getattr(inp, name).astype(np.float64)
+        x /= np.linalg.norm(x, axis=-1, keepdims=True)
+        bits = round_bf16_bits(x.astype(np.float32))
+        setattr(inp, name + "_bits", bits)
+        setattr(inp, name, bf16_bits_to_f32(bits))
+    return inp
+
+
+@pytest.mark.parametrize("beta_is_prob,qk_pre", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_flags_match_oracle(beta_is_prob, qk_pre, reverse):
+    inp = _flagged_inputs(421, 90 + 2 * beta_is_prob + qk_pre + 4 * reverse)
+    if not beta_is_prob:  # logits again for this case
+        inp.beta = np.log(inp.beta / (1 - inp.beta)).astype(np.float32)
+    q, k, v, g, beta, s0 = to_device(inp)
+    kw = dict(beta_is_prob=beta_is_prob, qk_prenormalized=qk_pre)
+    if reverse:
+        o_ref, s_ref = BD.reverse_scan(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, **kw)
+    else:
+        o_ref, s_ref = gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, **kw)
+    for portable in (False, True):
+        o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=reverse, portable=portable, **kw)
+        torch.cuda.synchronize()
+        eo, es = rel_max_err(o.cpu().numpy(), o_ref), rel_max_err(st.cpu().numpy(), s_ref)
+        print(f"flags prob={beta_is_prob} pre={qk_pre} reverse={reverse} portable={portable}: "
+              f"o {eo:.3e} state {es:.3e}", flush=True)
+        assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_prenormalized_equals_inside_normalisation_for_unit_rows():
+    """Rows that are exactly unit length in fp32 give the same result with and
+    without QK_PRENORMALIZED up to the normalisation's own rounding."""
+    inp = _flagged_inputs(300, 97)
+    q, k, v, g, beta, s0 = to_device(inp)
+    a, _ = gdn.gdn_fwd(q, k, v, g, beta, s0, beta_is_prob=True, qk_prenormalized=True)
+    b, _ = gdn.gdn_fwd(q, k, v, g, beta, s0, beta_is_prob=True)
+    torch.cuda.synchronize()
+    # the bf16 rows are unit length to about 2^-8, so the two differ by about that
+    assert rel_max_err(a.cpu().numpy(), b.cpu().numpy()) <= 2e-2
