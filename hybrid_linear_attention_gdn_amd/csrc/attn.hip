@@ -9,11 +9,13 @@
 //          slots of the cached blocks, the current block's slot), one
 //          workgroup per (b, h, 224 queries): seven compute waves (32 queries
 //          each, two per SIMD) and a copy wave that brings 64-key tiles of K
-//          and V^T into LDS with buffer-to-LDS loads, one barrier per tile.  The compute
-//          waves are software-pipelined: step j forms S^T of tile j while it
-//          accumulates P V of tile j - 1 (independent products), then takes
-//          the softmax of tile j.  K tiles therefore run one tile ahead of V^T
-//          tiles; each kind is double-buffered.
+//          and V^T into LDS with buffer-to-LDS loads, two barriers per tile
+//          (the two waves of a SIMD trade matrix and vector work at the
+//          second).  The compute waves are software-pipelined: step j forms
+//          S^T of tile j while it accumulates P V of tile j - 1 (independent
+//          products) and takes the softmax of tile j in the other half.  K
+//          tiles therefore run one tile ahead of V^T tiles; each kind is
+//          double-buffered.
 //
 // The compute waves work in transposed form.  S^T = K Q^T puts one query per
 // lane (the accumulator column), so the running max and sum of a query stay
@@ -220,9 +222,10 @@ __device__ __forceinline__ void copy_role(const char *__restrict__ bh, const Seg
   issue_k(0);
   for (int j = 0; j <= ntiles; ++j) {
     wait_vm<0>();
-    bare_barrier();
+    bare_barrier();  // step j opens
     if (j + 1 < ntiles) issue_k(j + 1);
     if (j < ntiles) issue_v(j);
+    bare_barrier();  // the compute waves' mid-step turn
   }
 }
 
@@ -367,35 +370,49 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
                           pack_bf16x2(pv_[2 * pp + 1][2], pv_[2 * pp + 1][3])}};
     }
   };
-  // Step j reads K tile j and V^T tile j - 1.  Waves 0-3 ("lead") run a step as
-  // scores of tile j with P V of tile j - 1, then the softmax of tile j;
-  // waves 4-6 ("lag", the second wave on SIMDs 0-2) run the softmax of tile
-  // j - 1 first, then the scores of tile j and P V of tile j - 1.  The two
-  // waves of a SIMD thus spend each step's halves on different units (one on
-  // the vector ALU while the other keeps the matrix core busy).
+  // Step j reads K tile j and V^T tile j - 1, in two halves separated by a
+  // barrier.  Waves 0-3 ("lead") run the scores of tile j with P V of tile
+  // j - 1 in the first half and the softmax of tile j in the second; waves 4-6
+  // ("lag", the second wave on SIMDs 0-2) run the softmax of tile j - 1 in the
+  // first half and the scores of tile j with P V of tile j - 1 in the second.
+  // The two waves of a SIMD thus take turns on the matrix core while the other
+  // works on the vector ALU; the mid-step barrier keeps them in turn (left
+  // free-running they drifted into overlapping matrix phases), and the wave in
+  // its matrix phase runs at raised priority so its MFMAs issue ahead of the
+  // other wave's vector work.
   if (W < 4) {
     compute_barrier();
     scores(0);
+    compute_barrier();
     softmax(0);
     for (int j = 1; j < ntiles; ++j) {
       compute_barrier();
+      __builtin_amdgcn_s_setprio(2);
       scores(j);
       pv(j - 1);
+      __builtin_amdgcn_s_setprio(0);
+      compute_barrier();
       softmax(j);
     }
     compute_barrier();
     pv(ntiles - 1);
+    compute_barrier();
   } else {
+    compute_barrier();
     compute_barrier();
     scores(0);
     for (int j = 1; j < ntiles; ++j) {
       compute_barrier();
       softmax(j - 1);
+      compute_barrier();
+      __builtin_amdgcn_s_setprio(2);
       scores(j);
       pv(j - 1);
+      __builtin_amdgcn_s_setprio(0);
     }
     compute_barrier();
     softmax(ntiles - 1);
+    compute_barrier();
     pv(ntiles - 1);
   }
   // ---- normalise and store: lane (ln, g) of query tile qq holds d = 16 dt + 4 g .. + 3
