@@ -5,6 +5,12 @@ Kernel times of a ``rocprofv3 --kernel-trace --stats`` run::
     python -m hybrid_linear_attention_gdn_amd.rocprof_summary stats RUN_DIR \\
         --command "<the rocprofv3 command>" [--bench-log LOG] > profiles/<kernel>_<workload>_kernel_trace.md
 
+Per-kernel means of a ``rocprofv3 --pmc`` run of rocprofv3's derived metrics
+(MfmaUtil, LdsBankConflict, ...)::
+
+    python -m hybrid_linear_attention_gdn_amd.rocprof_summary counters RUN_DIR \
+        --command "<the rocprofv3 command>" > profiles/counters_<workload>.md
+
 HBM bytes of one kernel from two ``rocprofv3 --pmc`` runs (FETCH_SIZE, then
 WRITE_SIZE), each scaled by what the same counter reads for the elementwise
 copy of known size that ``bench.py --copy-mib N`` runs in the same process::
@@ -134,6 +140,42 @@ def counter_by_kernel(directory: str, counter: str):
     return out
 
 
+# what each derived metric of rocprofv3 means, for the table's legend
+_METRIC_NOTES = {
+    "MfmaUtil": "% of SIMD-cycles with the matrix core busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs))",
+    "LdsBankConflict": "bank-conflict cycles per LDS access cycle (SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - "
+                       "SQ_LDS_BANK_CONFLICT))",
+    "LDSBankConflict": "% of CU-cycles the LDS spent stalled on bank conflicts",
+    "LdsUtil": "% of CU-cycles the LDS was active (SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE x CUs))",
+    "MfmaFlopsBF16": "bf16 matrix-core flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)",
+}
+
+
+def counters(args) -> str:
+    path = _one(args.run_dir, "counter_collection.csv")
+    per = {}
+    names = []
+    for r in csv.DictReader(open(path)):
+        c = r["Counter_Name"]
+        if c not in names:
+            names.append(c)
+        per.setdefault(short_name(r["Kernel_Name"]), {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    out = ["# rocprofv3 counters per kernel", "", "Command (from the repository root, on one MI355X):", "",
+           "    " + args.command, "", "Mean over each kernel's dispatches in the run.", "",
+           "| kernel | dispatches | " + " | ".join(names) + " |", "|---|---:|" + "---:|" * len(names)]
+    for kern, vals in sorted(per.items(), key=lambda kv: kv[0]):
+        if all(max(v) == 0.0 for v in vals.values()):
+            continue
+        n = max(len(v) for v in vals.values())
+        cells = []
+        for c in names:
+            v = statistics.mean(vals[c]) if c in vals else float("nan")
+            cells.append(f"{v:.4g}")
+        out.append(f"| `{kern}` | {n} | " + " | ".join(cells) + " |")
+    out += [""] + [f"- {c}: {_METRIC_NOTES[c]}" for c in names if c in _METRIC_NOTES]
+    return "\n".join(out) + "\n"
+
+
 def _match(table, kernel: str):
     hits = [n for n in table if kernel in n]
     if not hits:
@@ -190,6 +232,9 @@ def main(argv=None):
     s.add_argument("run_dir")
     s.add_argument("--command", required=True)
     s.add_argument("--bench-log")
+    c = sub.add_parser("counters")
+    c.add_argument("run_dir")
+    c.add_argument("--command", required=True)
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--kernel", "--stage", "--workload", "--fetch-command", "--write-command",
               "--json", "--md"):
@@ -199,6 +244,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         sys.stdout.write(stats(args))
+    elif args.cmd == "counters":
+        sys.stdout.write(counters(args))
     else:
         traffic(args)
 
