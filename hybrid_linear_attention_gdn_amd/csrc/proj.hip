@@ -12,9 +12,10 @@
 // One workgroup computes a 256 x 256 tile of C with eight waves (2 x 4, each
 // 128 x 64 = 8 x 4 accumulator tiles of v_mfma_f32_16x16x32_bf16).  K runs in
 // steps of 64: the step's A and W rows (32 KB each) are brought into LDS with
-// buffer-to-LDS loads, double-buffered, each wave issuing an eighth of them
-// spread between the products of the step before (one copy every four
-// MFMAs: issuing all eight at once held up the matrix pipe by ~700 cycles).  A staged row is 128 bytes, its
+// buffer-to-LDS loads, double-buffered.  The two waves on each SIMD belong to
+// two groups that run half a step apart (ping-pong): while one multiplies,
+// the other reads its next fragments from LDS and issues copies, so the matrix
+// pipe is not left idle during the reads.  A staged row is 128 bytes, its
 // 16-byte pieces permuted by row (slot = piece ^ ((row >> 1) & 7)), so the
 // 16-byte fragment reads of 16 consecutive rows fall on distinct banks.
 // Rows past M or N and pieces past K are read as zeros (buffer range checks)
@@ -52,6 +53,15 @@ static_assert(kLds >= kNS * kStage, "the output staging reuses the K stages");
 constexpr int kCopies = kStage / 1024 / 8;     // 8 one-KB copies per wave and step
 constexpr int kRowsPerCopy = 1024 / kRow;      // 8
 constexpr int kCopiesA = BM / kRowsPerCopy;    // 32 copies of A rows, then 32 of W rows
+
+// Workgroup barrier that waits for this wave's LDS reads but not for its
+// buffer-to-LDS copies in flight (those are waited for with wait_vm).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // staged rows sharing one 256-byte bank line get different slots
 __device__ __forceinline__ int slot_of(int row, int piece) { return piece ^ ((row / (256 / kRow)) % kPieces); }
@@ -118,23 +128,25 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const uint16_t *__res
   const uint32_t row_bytes = uint32_t(K) * 2u;
   const auto ra = make_rsrc(A + size_t(tm) * BM * K, uint32_t(min(BM, M - tm * BM)) * row_bytes);
   const auto rw = make_rsrc(W + size_t(tn) * BN * K, uint32_t(min(BN, N - tn * BN)) * row_bytes);
-  // copy c (0 .. 31) fills staged rows 16 c' .. 16 c' + 15 of A (c' = c < 16) or W (c' = c - 16)
-  // copy i (0 .. kCopies - 1) of this wave for step `step`
-  auto issue_one = [&](int step, int i) {
+  // Copy c (0 .. 63) of a step fills staged rows 8 c' .. 8 c' + 7 of A
+  // (c' = c < 32) or W (c' = c - 32); lane l takes row 8 c' + l / 8.  The
+  // slot permutation of a row depends on c' only through its parity, so each
+  // lane keeps two byte offsets (even / odd c') and adds the copy's row and
+  // the step's k as wave-uniform terms.
+  const int lrow = lane / kPieces;
+  const int piece_e[2] = {(lane % kPieces) ^ (lrow >> 1), (lane % kPieces) ^ (4 + (lrow >> 1))};
+  const uint32_t lane_off[2] = {uint32_t(lrow) * row_bytes + 16u * uint32_t(piece_e[0]),
+                                uint32_t(lrow) * row_bytes + 16u * uint32_t(piece_e[1])};
+  auto issue_copy = [&](int step, int c) {
     char *buf = lds + (step % kNS) * kStage;
     const int k0 = step * BK;
-    const int c = wave * kCopies + i;
     const bool isw = c >= kCopiesA;
     const int cc = isw ? c - kCopiesA : c;
-    const int row = kRowsPerCopy * cc + lane / kPieces;
-    const int piece = slot_of(row, lane % kPieces);
-    const uint32_t off = k0 + 8 * piece < K ? uint32_t(row) * row_bytes + uint32_t(k0 + 8 * piece) * 2u
-                                            : kOutOfRange;
+    const int e = cc & 1;
+    const uint32_t off = k0 + 8 * piece_e[e] < K
+                             ? lane_off[e] + uint32_t(cc) * (kRowsPerCopy * row_bytes) + uint32_t(k0) * 2u
+                             : kOutOfRange;
     copy16(isw ? rw : ra, buf + (isw ? BM * kRow : 0) + 1024 * cc, off);
-  };
-  auto issue = [&](int step) {
-#pragma unroll
-    for (int i = 0; i < kCopies; ++i) issue_one(step, i);
   };
 
   f32x4 acc[TM][TN];
@@ -143,28 +155,20 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const uint16_t *__res
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
 
+  // Ping-pong.  The lead group (wm 0) and the lag group (wm 1) each hold one
+  // wave on every SIMD, and a barrier opens every half step ("period"):
+  //   period 2s    : lead reads the fragments of step s, then issues all
+  //                  copies of step s + 1;  lag multiplies step s - 1;
+  //   period 2s + 1: lead multiplies step s;  lag reads step s.
+  // The stage of step s + 1 holds step s - 1, whose last reads (lag, period
+  // 2s - 1) end before period 2s.  Only the lead copies inside the loop: the
+  // compiler makes a wave's LDS reads wait for that wave's copies in flight,
+  // so copies from the lag would stall its reads one period later.
   const int steps = (K + BK - 1) / BK;
-#pragma unroll
-  for (int i = 0; i < kNS - 1; ++i)
-    if (i < steps) issue(i);
-  for (int s = 0; s < steps; ++s) {
+  const bool lead = wm == 0;
+  F32 af[BK / 32][TM], bfr[BK / 32][TN];
+  auto read = [&](int s) {
     const char *buf = lds + (s % kNS) * kStage;
-    // this wave's copies of step s have landed: the copies of the later steps
-    // already issued (up to kNS - 2 of them) may stay in flight
-    const int later = min(kNS - 2, steps - 1 - s);
-    if (later >= 2)
-      wait_vm<2 * kCopies>();
-    else if (later == 1)
-      wait_vm<kCopies>();
-    else
-      wait_vm<0>();
-    compute_barrier();  // ... every wave's; and the stage of step s - 1 is no longer read
-    // the copies of step s + kNS - 1 go out between this step's products (one
-    // every four MFMAs): issuing them takes time the matrix pipe can use
-    const bool next = s + kNS - 1 < steps;
-    // every fragment of the step is read up front, so the reads of the second
-    // 32-deep block are in flight while the first block's products run
-    F32 af[BK / 32][TM], bfr[BK / 32][TN];
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb) {
 #pragma unroll
@@ -181,15 +185,48 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(const uint16_t *__res
         af[kb][i] = F32{{x.x, x.y, x.z, x.w}};
       }
     }
+  };
+  auto multiply = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < BK / 32; ++kb) {
+    for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mma(af[kb][i], bfr[kb][j], acc[i][j]);
-        constexpr int kPer = TM * (BK / 32) / kCopies;  // MFMA rows per copy
-        if (next && i % kPer == kPer - 1) issue_one(s + kNS - 1, (kb * TM + i) / kPer);
+  };
+  // steps 0 and 1 before the loop, an eighth from each wave
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+    if (st < steps) {
+#pragma unroll
+      for (int i = 0; i < kCopies; ++i) issue_copy(st, kCopies * wave + i);
+    }
+  if (steps > 1)
+    wait_vm<kCopies>();  // this wave's copies of step 0 have landed
+  else
+    wait_vm<0>();
+  if (lead) {
+    for (int s = 0; s < steps; ++s) {
+      lds_barrier();  // period 2s
+      read(s);
+      if (s >= 1 && s + 1 < steps) {
+#pragma unroll
+        for (int i = 0; i < 2 * kCopies; ++i) issue_copy(s + 1, 2 * kCopies * wave + i);
       }
+      lds_barrier();  // period 2s + 1
+      multiply();
+      __builtin_amdgcn_sched_barrier(0);  // the wait stays behind the products
+      wait_vm<0>();  // the copies of step s + 1 are in LDS before period 2s + 2
+    }
+    lds_barrier();  // period 2 steps
+  } else {
+    lds_barrier();  // period 0
+    for (int s = 0; s < steps; ++s) {
+      lds_barrier();  // period 2s + 1
+      read(s);
+      wait_vm<0>();  // (step 1's copies from before the loop)
+      lds_barrier();  // period 2s + 2
+      multiply();
     }
   }
   // Output through LDS, half a tile (128 rows x 256 columns, fp32) at a time:
