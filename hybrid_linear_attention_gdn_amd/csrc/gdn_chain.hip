@@ -25,7 +25,9 @@
 // Buffers.  Rows (K, Q, V, scales) are double-buffered and the M / P' record
 // single-buffered.  Phase A reads all of them, so at barrier Y both the
 // record buffer and row buffer c & 1 are free: the copy waves then issue
-// chunk c + 1's record (due at X of c + 1) and chunk c + 2's rows.
+// chunk c + 1's record (due at X of c + 1) and chunk c + 2's rows.  With fp8
+// rows there is room for a second record buffer: chunk c's record then sits
+// in buffer c & 1 and is copied together with its rows, a chunk ahead.
 //
 // K and Q rows sit at a 256-byte stride with their 16-byte pieces permuted
 // by row (slot = piece ^ (row & 15)), so the 16-byte fragment reads of 16
@@ -89,7 +91,12 @@ struct Rows {
   static constexpr int kVInstr = kFp8 ? 2 : 3;    // 1 KB copies of the V tile
   static constexpr int kCs = kV + kVInstr * 1024;
   static constexpr int kBytes = kCs + kCsFloats * 4;  // 45,056 / 23,552
-  static constexpr int kLds = kLdsRows + 2 * kBytes;  // 153,600 / 110,592
+  // fp8 rows leave room for a second record buffer: chunk c's record sits in
+  // buffer c & 1, so the copy of chunk c + 2's record starts a chunk earlier
+  static constexpr bool kRec2 = kFp8;
+  static constexpr int kRec1 = kLdsRows + 2 * kBytes;  // the second record buffer
+  static constexpr int kLds = kRec1 + (kRec2 ? kMBytes + kPBytes : 0);  // 153,600 / 161,792
+  static constexpr int rec_off(int c) { return kRec2 && (c & 1) ? kRec1 : kLdsMP; }
   static constexpr int kKQInstr = C * kStride / 1024;  // 20 / 10 one-KB copies per matrix
   // Copy split between the three copy waves, per chunk: waves 0 and 1 take
   // kMShare KB of M each and the K, resp. Q rows; wave 2 the rest of M, P',
@@ -225,6 +232,7 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
   for (int c = cb; c < ce; ++c) {
     const int t0 = c * C, nv = min(C, T - t0);
     const char *rb = lds + kLdsRows + (c & 1) * G::kBytes;
+    MPlds = lds + G::rec_off(c);
     const float *csl = reinterpret_cast<const float *>(rb + G::kCs);
     const char *vl = rb + G::kV;
     compute_barrier();  // X: chunk c opens (S published; its rows and record landed)
@@ -501,29 +509,56 @@ __device__ __forceinline__ void copy_role(const char *__restrict__ q, const char
     const auto rm = make_rsrc(Mws + (u * N + c) * size_t(kMBytes), kMBytes);
     constexpr int kMShare = G::kMShare;
     constexpr int m0 = L == 0 ? 0 : (L == 1 ? kMShare : 2 * kMShare), m1 = L == 2 ? kMInstr : m0 + kMShare;
+    char *rd = lds + G::rec_off(c);
 #pragma unroll
-    for (int i = m0; i < m1; ++i) copy16(rm, lds + kLdsMP + 1024 * i, 1024u * i + 16u * lane);
+    for (int i = m0; i < m1; ++i) copy16(rm, rd + 1024 * i, 1024u * i + 16u * lane);
     if constexpr (L == 2) {
       const auto rp = make_rsrc(Pws + (u * N + c) * size_t(kPBytes), kPBytes);
 #pragma unroll
-      for (int i = 0; i < kPInstr; ++i) copy16(rp, lds + kLdsMP + kMBytes + 1024 * i, 1024u * i + 16u * lane);
+      for (int i = 0; i < kPInstr; ++i) copy16(rp, rd + kMBytes + 1024 * i, 1024u * i + 16u * lane);
     }
   };
-  if (cb < ce) {
-    copy_rows(cb);
-    copy_record(cb);
-    if (cb + 1 < ce) copy_rows(cb + 1);
-  }
-  for (int c = cb; c < ce; ++c) {
-    // in flight, oldest first: rows(c), record(c), rows(c + 1) if c + 1 < ce
-    if (c + 1 < ce)
-      wait_vm<kRow>();
-    else
-      wait_vm<0>();
-    bare_barrier();  // X: chunk c opens
-    bare_barrier();  // Y: chunk c's record and rows have been read
-    if (c + 1 < ce) copy_record(c + 1);
-    if (c + 2 < ce) copy_rows(c + 2);
+  if constexpr (G::kRec2) {
+    constexpr int kRec = G::rec_share(L);
+    static_assert(2 * (kRow + kRec) < 64, "vmcnt holds 63");
+    if (cb < ce) {
+      copy_rows(cb);
+      copy_record(cb);
+      if (cb + 1 < ce) {
+        copy_rows(cb + 1);
+        copy_record(cb + 1);
+      }
+    }
+    for (int c = cb; c < ce; ++c) {
+      // in flight, oldest first: rows(c), record(c), then rows(c + 1), record(c + 1) if c + 1 < ce
+      if (c + 1 < ce)
+        wait_vm<kRow + kRec>();
+      else
+        wait_vm<0>();
+      bare_barrier();  // X: chunk c opens
+      bare_barrier();  // Y: chunk c's record and rows have been read
+      if (c + 2 < ce) {
+        copy_rows(c + 2);
+        copy_record(c + 2);
+      }
+    }
+  } else {
+    if (cb < ce) {
+      copy_rows(cb);
+      copy_record(cb);
+      if (cb + 1 < ce) copy_rows(cb + 1);
+    }
+    for (int c = cb; c < ce; ++c) {
+      // in flight, oldest first: rows(c), record(c), rows(c + 1) if c + 1 < ce
+      if (c + 1 < ce)
+        wait_vm<kRow>();
+      else
+        wait_vm<0>();
+      bare_barrier();  // X: chunk c opens
+      bare_barrier();  // Y: chunk c's record and rows have been read
+      if (c + 1 < ce) copy_record(c + 1);
+      if (c + 2 < ce) copy_rows(c + 2);
+    }
   }
   wait_vm<0>();
 }
