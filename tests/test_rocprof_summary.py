@@ -58,3 +58,24 @@ def test_source_hash_ignores_comments_and_layout():
     a = rs._code_only("int x = 1; // note\n/* block\n comment */  int  y = 2;\n")
     assert a == "int x = 1; int y = 2;"
     assert rs._code_only("a //c\nb") != rs._code_only("a b c")
+
+
+def test_counters_table(tmp_path, capsys):
+    # two counters per dispatch, two dispatches of one kernel and one of another;
+    # kernels whose counters are all zero are left out of the table
+    d = tmp_path / "c"
+    os.makedirs(d)
+    with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(HDR)
+        rows = [(1, CHAIN, "MfmaUtil", 10.0), (1, CHAIN, "LdsBankConflict", 0.5),
+                (2, CHAIN, "MfmaUtil", 20.0), (2, CHAIN, "LdsBankConflict", 0.25),
+                (3, NEG, "MfmaUtil", 0.0), (3, NEG, "LdsBankConflict", 0.0)]
+        for i, name, counter, value in rows:
+            w.writerow([i, i, "Agent 1", 1, 1, 1, 64, 1, name, 256, 0, 0, 8, 0, 8, counter, value, 0, 1])
+    rs.main(["counters", str(d), "--command", "rocprofv3 --pmc MfmaUtil LdsBankConflict -- x"])
+    out = capsys.readouterr().out
+    assert "rocprofv3 --pmc MfmaUtil LdsBankConflict -- x" in out
+    assert "| `chain_kernel<false>` | 2 | 15 | 0.375 |" in out
+    assert "neg_kernel" not in out
+    assert "MfmaUtil:" in out and "LdsBankConflict:" in out
