@@ -218,13 +218,21 @@ __device__ __forceinline__ void copy_role(const char *__restrict__ bh, const Seg
   };
   // barrier j (j = 0 .. ntiles) opens step j, which reads K tile j and V^T
   // tile j - 1; after it, K tile j + 1 and V^T tile j are issued (their
-  // buffers were last read in step j - 1)
+  // buffers were last read in step j - 1).  K tile j + 1 has landed by the
+  // mid-step turn, so the compute waves can read its first key tile during
+  // their vector half.
   issue_k(0);
   for (int j = 0; j <= ntiles; ++j) {
     wait_vm<0>();
     bare_barrier();  // step j opens
     if (j + 1 < ntiles) issue_k(j + 1);
     if (j < ntiles) issue_v(j);
+    if (j + 1 < ntiles) {  // K tile j + 1 lands by the mid-step turn (V^T tile j may stay in flight)
+      if (j < ntiles)
+        wait_vm<kVInstr>();
+      else
+        wait_vm<0>();
+    }
     bare_barrier();  // the compute waves' mid-step turn
   }
 }
@@ -272,19 +280,32 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
   f32x4 sacc[4][2];
   F32 pf[2][2];  // P^T B operands [qq][key pair] of the previous tile
   // ---- S^T = K Q^T of tile j: key tile t (16 keys), query tile qq
-  auto scores = [&](int j) {
-    const char *kb_ = lds + (j & 1) * kKTile;
+  // fragments of key tile t of K tile j
+  auto kfrag = [&](int j, int t, F32 *kf, F16 &kt) {
+    const char *rowp = lds + (j & 1) * kKTile + (16 * t + ln) * kKRow;
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) {
+      const uint4 x = *reinterpret_cast<const uint4 *>(rowp + 16 * ((4 * kb + lg) ^ ln));
+      kf[kb] = F32{{x.x, x.y, x.z, x.w}};
+    }
+    const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 16 * ((12 + (lg >> 1)) ^ ln) + 8 * (lg & 1));
+    kt = F16{{x2.x, x2.y}};
+  };
+  F32 kpf[3];  // key tile 0 of the next K tile, read in the vector half before its scores
+  F16 kpt;
+  auto scores = [&](int j, bool pre) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const char *rowp = kb_ + (16 * t + ln) * kKRow;
       F32 kf[3];
-#pragma unroll
-      for (int kb = 0; kb < 3; ++kb) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(rowp + 16 * ((4 * kb + lg) ^ ln));
-        kf[kb] = F32{{x.x, x.y, x.z, x.w}};
+      F16 kt;
+      if (t == 0 && pre) {
+        kf[0] = kpf[0];
+        kf[1] = kpf[1];
+        kf[2] = kpf[2];
+        kt = kpt;
+      } else {
+        kfrag(j, t, kf, kt);
       }
-      const uint2 x2 = *reinterpret_cast<const uint2 *>(rowp + 16 * ((12 + (lg >> 1)) ^ ln) + 8 * (lg & 1));
-      const F16 kt{{x2.x, x2.y}};
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         f32x4 acc = zero4();
@@ -382,17 +403,19 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
   // other wave's vector work.
   if (W < 4) {
     compute_barrier();
-    scores(0);
+    scores(0, false);
     compute_barrier();
     softmax(0);
+    if (1 < ntiles) kfrag(1, 0, kpf, kpt);
     for (int j = 1; j < ntiles; ++j) {
       compute_barrier();
       __builtin_amdgcn_s_setprio(2);
-      scores(j);
+      scores(j, true);
       pv(j - 1);
       __builtin_amdgcn_s_setprio(0);
       compute_barrier();
       softmax(j);
+      if (j + 1 < ntiles) kfrag(j + 1, 0, kpf, kpt);  // K tile j + 1 landed by the mid-step turn
     }
     compute_barrier();
     pv(ntiles - 1);
@@ -400,13 +423,14 @@ __device__ __forceinline__ void compute_role(int W, const uint16_t *__restrict__
   } else {
     compute_barrier();
     compute_barrier();
-    scores(0);
+    scores(0, false);
     for (int j = 1; j < ntiles; ++j) {
       compute_barrier();
       softmax(j - 1);
+      kfrag(j, 0, kpf, kpt);
       compute_barrier();
       __builtin_amdgcn_s_setprio(2);
-      scores(j);
+      scores(j, true);
       pv(j - 1);
       __builtin_amdgcn_s_setprio(0);
     }
