@@ -42,6 +42,21 @@ __device__ __forceinline__ ChunkIdx chunk_of_block(int H, int N, int T) {
   return r;
 }
 
+// Each kernel first stages the rows it multiplies in LDS (row stride d + 1
+// floats, so that threads walking rows hit distinct banks), then forms its
+// products from LDS; global loads are coalesced row copies.  The reduction
+// loops are unrolled so that their LDS reads are in flight together (the
+// solve's serial chains are otherwise bound by one LDS latency per term).
+__host__ __device__ constexpr size_t intra_lds_floats(int dk, int dv) {
+  return size_t(C) * (dk + 1) + size_t(C) * (dv + 1) + 2 * size_t(C) * (C + 1) + 4 * C + (C / 16 - 1) * 256;
+}
+__host__ __device__ constexpr size_t state_lds_floats(int dk) {
+  return 16 * size_t(dk + 1) + 2 * size_t(C) * (dk + 1) + size_t(C) * 17 + C + 1;
+}
+__host__ __device__ constexpr size_t output_lds_floats(int dk, int dv) {
+  return size_t(C) * (dk + 1) + size_t(dv > C ? dv : C) * (dk + 1) + size_t(C) * (C + 1) + C;
+}
+
 template <typename TIn>
 __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, const TIn *__restrict__ v,
                                                     const float *__restrict__ s_beta,
@@ -49,9 +64,14 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, c
                                                     const float *__restrict__ s_gcum, float *__restrict__ W,
                                                     float *__restrict__ Ut, int T, int H, int dk, int dv,
                                                     int N, bool rev) {
-  __shared__ float A[C][C + 1];
-  __shared__ float Tm[C][C + 1];
-  __shared__ float sb[C], srk[C], sG[C];
+  extern __shared__ float sm[];
+  const int ldk = dk + 1, ldv = dv + 1, ldc = C + 1;
+  float *Ks = sm;              // [C][ldk] raw k rows
+  float *Vs = Ks + C * ldk;    // [C][ldv] v rows
+  float *A = Vs + C * ldv;     // [C][ldc]
+  float *Tm = A + C * ldc;     // [C][ldc]
+  float *sb = Tm + C * ldc, *srk = sb + C, *sG = srk + C, *cw = sG + C;
+  float *X = cw + C;           // [4][16][16] off-diagonal products of the solve
   const ChunkIdx ci = chunk_of_block(H, N, T);
   const size_t sbase = (size_t(ci.b) * H + ci.h) * T + ci.t0;
   for (int r = threadIdx.x; r < C; r += blockDim.x) {
@@ -59,55 +79,83 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, c
     sb[r] = ok ? s_beta[sbase + r] : 0.f;
     srk[r] = ok ? s_rk[sbase + r] : 0.f;
     sG[r] = ok ? s_gcum[sbase + r] : 0.f;
+    cw[r] = ok ? sb[r] * expf(sG[r]) * srk[r] : 0.f;  // beta gamma rk
+  }
+  auto row = [&](int r, int d) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(d); };
+  for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
+    const int r = idx / dk, d = idx % dk;
+    Ks[r * ldk + d] = r < ci.n ? load_f32(k, row(r, dk) + d) : 0.f;
+  }
+  for (int idx = threadIdx.x; idx < C * dv; idx += blockDim.x) {
+    const int r = idx / dv, e = idx % dv;
+    Vs[r * ldv + e] = r < ci.n ? load_f32(v, row(r, dv) + e) : 0.f;
   }
   __syncthreads();
-  auto krow = [&](int r) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(dk); };
-  auto vrow = [&](int r) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(dv); };
   // A (strictly lower), padded rows/cols are zero
   for (int idx = threadIdx.x; idx < C * C; idx += blockDim.x) {
     const int r = idx / C, i = idx % C;
     float val = 0.f;
     if (i < r && r < ci.n) {
-      const size_t kr = krow(r), ki = krow(i);
       float dot = 0.f;
-      for (int d = 0; d < dk; ++d) dot = fmaf(load_f32(k, kr + d), load_f32(k, ki + d), dot);
+      #pragma unroll 8
+      for (int d = 0; d < dk; ++d) dot = fmaf(Ks[r * ldk + d], Ks[i * ldk + d], dot);
       val = sb[r] * expf(sG[r] - sG[i]) * srk[r] * srk[i] * dot;
     }
-    A[r][i] = val;
+    A[r * ldc + i] = val;
   }
   __syncthreads();
-  // Tm = (I + A)^{-1} by forward substitution, one column per thread
+  // Tm = (I + A)^{-1} by 16 x 16 blocks (A is strictly lower, so Tm is unit
+  // lower triangular): the diagonal blocks by forward substitution, one column
+  // per thread, then the blocks at distance 1 .. 4 below the diagonal,
+  // Tm_IJ = -Tm_II X_IJ with X_IJ = sum_{K=J}^{I-1} A_IK Tm_KJ, whose blocks
+  // Tm_KJ all lie closer to the diagonal.
+  constexpr int NB = C / 16;
+  for (int idx = threadIdx.x; idx < C * C; idx += blockDim.x) Tm[(idx / C) * ldc + idx % C] = 0.f;
+  __syncthreads();
   if (threadIdx.x < C) {
-    const int j = threadIdx.x;
-    for (int r = 0; r < C; ++r) {
-      float x;
-      if (r < j) {
-        x = 0.f;
-      } else if (r == j) {
-        x = 1.f;
-      } else {
-        float s = 0.f;
-        for (int i = j; i < r; ++i) s = fmaf(A[r][i], Tm[i][j], s);
-        x = -s;
-      }
-      Tm[r][j] = x;
+    const int c0 = 16 * (threadIdx.x / 16), jj = threadIdx.x % 16, j = c0 + jj;
+    for (int rr = jj; rr < 16; ++rr) {
+      const int r = c0 + rr;
+      float s = 0.f;
+#pragma unroll 8
+      for (int i = j; i < r; ++i) s = fmaf(A[r * ldc + i], Tm[i * ldc + j], s);
+      Tm[r * ldc + j] = rr == jj ? 1.f : -s;
     }
   }
   __syncthreads();
+  for (int dist = 1; dist < NB; ++dist) {
+    const int nb = NB - dist;  // blocks (J + dist, J), J = 0 .. nb - 1
+    for (int idx = threadIdx.x; idx < nb * 256; idx += blockDim.x) {
+      const int J = idx / 256, I = J + dist, r = 16 * I + (idx % 256) / 16, j = 16 * J + idx % 16;
+      float s = 0.f;
+#pragma unroll 8
+      for (int i = 16 * J; i < 16 * I; ++i) s = fmaf(A[r * ldc + i], Tm[i * ldc + j], s);
+      X[idx] = s;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nb * 256; idx += blockDim.x) {
+      const int J = idx / 256, I = J + dist, rr = (idx % 256) / 16, jj = idx % 16, r = 16 * I + rr;
+      float s = 0.f;
+#pragma unroll 8
+      for (int kk = 0; kk <= rr; ++kk) s = fmaf(Tm[r * ldc + 16 * I + kk], X[J * 256 + kk * 16 + jj], s);
+      Tm[r * ldc + 16 * J + jj] = -s;
+    }
+    __syncthreads();
+  }
   const size_t cbase = ((size_t(ci.b) * H + ci.h) * N + ci.c) * C;
-  // W = Tm diag(beta gamma rk) K_raw
+  // W = Tm diag(beta gamma rk) K_raw,  Ut = Tm diag(beta) V
   for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
     const int r = idx / dk, d = idx % dk;
     float s = 0.f;
-    for (int i = 0; i <= r && i < ci.n; ++i)
-      s = fmaf(Tm[r][i] * (sb[i] * expf(sG[i]) * srk[i]), load_f32(k, krow(i) + d), s);
+    #pragma unroll 8
+    for (int i = 0; i <= r && i < ci.n; ++i) s = fmaf(Tm[r * ldc + i] * cw[i], Ks[i * ldk + d], s);
     W[(cbase + r) * dk + d] = s;
   }
-  // Ut = Tm diag(beta) V
   for (int idx = threadIdx.x; idx < C * dv; idx += blockDim.x) {
     const int r = idx / dv, e = idx % dv;
     float s = 0.f;
-    for (int i = 0; i <= r && i < ci.n; ++i) s = fmaf(Tm[r][i] * sb[i], load_f32(v, vrow(i) + e), s);
+    #pragma unroll 8
+    for (int i = 0; i <= r && i < ci.n; ++i) s = fmaf(Tm[r * ldc + i] * sb[i], Vs[i * ldv + e], s);
     Ut[(cbase + r) * dv + e] = s;
   }
 }
@@ -121,10 +169,14 @@ __global__ __launch_bounds__(256) void state_kernel(const TIn *__restrict__ k, c
                                                     float *__restrict__ U, float *__restrict__ S0, int T, int H,
                                                     int dk, int dv, int N, bool rev) {
   constexpr int R = 16;
-  __shared__ float S[R][kMaxPortableDim + 1];
-  __shared__ float Us[C][R + 1];
-  __shared__ float coef[C];
-  __shared__ float gammaC;
+  extern __shared__ float sm[];
+  const int ldk = dk + 1;
+  float *S = sm;                // [R][ldk] this block's rows of the state
+  float *Ws = S + R * ldk;      // [C][ldk] W rows of the chunk
+  float *Ks = Ws + C * ldk;     // [C][ldk] raw k rows of the chunk
+  float *Us = Ks + C * ldk;     // [C][R + 1]
+  float *coef = Us + C * (R + 1);
+  float *gammaC = coef + C;
   const int tiles = (dv + R - 1) / R;
   const int tile = blockIdx.x % tiles;
   const int h = (blockIdx.x / tiles) % H;
@@ -134,53 +186,59 @@ __global__ __launch_bounds__(256) void state_kernel(const TIn *__restrict__ k, c
   const size_t bh = size_t(b) * H + h;
   for (int idx = threadIdx.x; idx < R * dk; idx += blockDim.x) {
     const int ii = idx / dk, d = idx % dk;
-    S[ii][d] = (ii < nrows && state_in) ? state_in[(bh * dv + i0 + ii) * dk + d] : 0.f;
+    S[ii * ldk + d] = (ii < nrows && state_in) ? state_in[(bh * dv + i0 + ii) * dk + d] : 0.f;
   }
   for (int c = 0; c < N; ++c) {
     const int t0 = c * C, n = min(C, T - t0);
-    __syncthreads();
+    __syncthreads();  // the previous chunk's update of S is complete; Ws, Ks, Us are free
     const size_t sb = bh * T + t0;
     if (threadIdx.x < C) {
       const int r = threadIdx.x;
       const float Gl = s_gcum[sb + n - 1];
       coef[r] = r < n ? s_rk[sb + r] * expf(Gl - s_gcum[sb + r]) : 0.f;
-      if (r == 0) gammaC = expf(Gl);
+      if (r == 0) gammaC[0] = expf(Gl);
     }
     // entry state of this chunk, for the output kernel
     for (int idx = threadIdx.x; idx < nrows * dk; idx += blockDim.x) {
       const int ii = idx / dk, d = idx % dk;
-      S0[((bh * N + c) * dv + i0 + ii) * dk + d] = S[ii][d];
+      S0[((bh * N + c) * dv + i0 + ii) * dk + d] = S[ii * ldk + d];
     }
-    // U = Ut - W S0^T for this tile's columns
     const size_t cb = (bh * N + c) * C;
+    for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
+      const int r = idx / dk, d = idx % dk;
+      const bool ok = r < n;
+      Ws[r * ldk + d] = ok ? W[(cb + r) * dk + d] : 0.f;
+      Ks[r * ldk + d] = ok ? load_f32(k, ((size_t(b) * T + phys_token(t0 + r, T, rev)) * H + h) * size_t(dk) + d) : 0.f;
+    }
+    __syncthreads();
+    // U = Ut - W S0^T for this tile's columns
     for (int idx = threadIdx.x; idx < C * R; idx += blockDim.x) {
       const int r = idx / R, ii = idx % R;
       float u = 0.f;
       if (r < n && ii < nrows) {
         float s = 0.f;
-        const float *wr = W + (cb + r) * dk;
-        for (int d = 0; d < dk; ++d) s = fmaf(wr[d], S[ii][d], s);
+        #pragma unroll 8
+        for (int d = 0; d < dk; ++d) s = fmaf(Ws[r * ldk + d], S[ii * ldk + d], s);
         u = Ut[(cb + r) * dv + i0 + ii] - s;
         U[(cb + r) * dv + i0 + ii] = u;
       }
-      Us[r][ii] = u;
+      Us[r * (R + 1) + ii] = u;
     }
     __syncthreads();
     // S <- gamma_n S + U^T diag(rk e^{G_n - G}) K_raw
     for (int idx = threadIdx.x; idx < R * dk; idx += blockDim.x) {
       const int ii = idx / dk, d = idx % dk;
       float s = 0.f;
-      for (int r = 0; r < n; ++r)
-        s = fmaf(Us[r][ii] * coef[r], load_f32(k, ((size_t(b) * T + phys_token(t0 + r, T, rev)) * H + h) * size_t(dk) + d),
-                 s);
-      S[ii][d] = fmaf(gammaC, S[ii][d], s);
+      #pragma unroll 8
+      for (int r = 0; r < n; ++r) s = fmaf(Us[r * (R + 1) + ii] * coef[r], Ks[r * ldk + d], s);
+      S[ii * ldk + d] = fmaf(gammaC[0], S[ii * ldk + d], s);
     }
   }
   __syncthreads();
   if (state_out)
     for (int idx = threadIdx.x; idx < nrows * dk; idx += blockDim.x) {
       const int ii = idx / dk, d = idx % dk;
-      state_out[(bh * dv + i0 + ii) * dk + d] = S[ii][d];
+      state_out[(bh * dv + i0 + ii) * dk + d] = S[ii * ldk + d];
     }
 }
 
@@ -192,41 +250,65 @@ __global__ __launch_bounds__(256) void output_kernel(const TIn *__restrict__ q, 
                                                      const float *__restrict__ U, const float *__restrict__ S0,
                                                      TOut *__restrict__ o, int T, int H, int dk, int dv, int N,
                                                      bool rev) {
-  __shared__ float P[C][C + 1];
-  __shared__ float sc[C];
+  extern __shared__ float sm[];
+  const int ldk = dk + 1, ldc = C + 1;
+  float *Qs = sm;                                // [C][ldk] raw q rows
+  float *KS = Qs + C * ldk;                      // [C][ldk] raw k rows, then [dv][ldk] the entry state
+  float *P = KS + (dv > C ? dv : C) * ldk;       // [C][ldc]
+  float *sc = P + C * ldc;
   const ChunkIdx ci = chunk_of_block(H, N, T);
   const size_t sbase = (size_t(ci.b) * H + ci.h) * T + ci.t0;
   auto row = [&](int r, int d) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(d); };
+  for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
+    const int r = idx / dk, d = idx % dk;
+    const bool ok = r < ci.n;
+    Qs[r * ldk + d] = ok ? load_f32(q, row(r, dk) + d) : 0.f;
+    KS[r * ldk + d] = ok ? load_f32(k, row(r, dk) + d) : 0.f;
+  }
+  for (int r = threadIdx.x; r < C; r += blockDim.x)
+    sc[r] = r < ci.n ? expf(s_gcum[sbase + r]) * s_rq[sbase + r] : 0.f;
+  __syncthreads();
   for (int idx = threadIdx.x; idx < C * C; idx += blockDim.x) {
     const int r = idx / C, i = idx % C;
     float val = 0.f;
     if (i <= r && r < ci.n) {
       float dot = 0.f;
-      const size_t qr = row(r, dk), ki = row(i, dk);
-      for (int d = 0; d < dk; ++d) dot = fmaf(load_f32(q, qr + d), load_f32(k, ki + d), dot);
+      #pragma unroll 8
+      for (int d = 0; d < dk; ++d) dot = fmaf(Qs[r * ldk + d], KS[i * ldk + d], dot);
       val = expf(s_gcum[sbase + r] - s_gcum[sbase + i]) * s_rq[sbase + r] * s_rk[sbase + i] * dot;
     }
-    P[r][i] = val;
+    P[r * ldc + i] = val;
   }
-  for (int r = threadIdx.x; r < C; r += blockDim.x)
-    sc[r] = r < ci.n ? expf(s_gcum[sbase + r]) * s_rq[sbase + r] : 0.f;
-  __syncthreads();
+  __syncthreads();  // the k rows are no longer read: the entry state takes their place
   const size_t bhc = (size_t(ci.b) * H + ci.h) * N + ci.c;
   const float *S0c = S0 + bhc * size_t(dv) * dk;
+  for (int idx = threadIdx.x; idx < dv * dk; idx += blockDim.x) {
+    const int e = idx / dk, d = idx % dk;
+    KS[e * ldk + d] = S0c[idx];
+  }
+  __syncthreads();
   const float *Uc = U + bhc * C * size_t(dv);
   for (int idx = threadIdx.x; idx < ci.n * dv; idx += blockDim.x) {
     const int r = idx / dv, e = idx % dv;
     float qs = 0.f;
-    const size_t qr = row(r, dk);
-    for (int d = 0; d < dk; ++d) qs = fmaf(load_f32(q, qr + d), S0c[size_t(e) * dk + d], qs);
+    #pragma unroll 8
+    for (int d = 0; d < dk; ++d) qs = fmaf(Qs[r * ldk + d], KS[e * ldk + d], qs);
     float acc = sc[r] * qs;
-    for (int i = 0; i <= r; ++i) acc = fmaf(P[r][i], Uc[size_t(i) * dv + e], acc);
+    #pragma unroll 8
+    for (int i = 0; i <= r; ++i) acc = fmaf(P[r * ldc + i], Uc[size_t(i) * dv + e], acc);
     const size_t oi = row(r, dv) + e;
     if constexpr (sizeof(TOut) == 2)
       o[oi] = f32_to_bf16(acc);
     else
       o[oi] = acc;
   }
+}
+
+// more than the default 64 KB of dynamic LDS, once per instantiation, sized for the largest head dims
+template <typename F>
+hipError_t allow_lds(F *kernel, size_t floats) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             int(floats * sizeof(float)));
 }
 
 template <typename TIn>
@@ -244,24 +326,31 @@ hipError_t launch_typed(const Plan &p, const Args &a) {
   const unsigned chunks = unsigned(p.B) * p.H * p.N;
   const bool rev = p.flags & kReverse;
   stage_begin(a, kStageIntra);
-  intra_kernel<TIn><<<dim3(chunks), dim3(256), 0, a.stream>>>(k, v, beta, rk, gc, W, Ut, p.T, p.H, p.dk, p.dv,
-                                                              p.N, rev);
+  constexpr int kD = kMaxPortableDim;
+  static const hipError_t lds_ok[4] = {
+      allow_lds(&intra_kernel<TIn>, intra_lds_floats(kD, kD)), allow_lds(&state_kernel<TIn>, state_lds_floats(kD)),
+      allow_lds(&output_kernel<TIn, uint16_t>, output_lds_floats(kD, kD)),
+      allow_lds(&output_kernel<TIn, float>, output_lds_floats(kD, kD))};
+  for (hipError_t le : lds_ok)
+    if (le != hipSuccess) return le;
+  intra_kernel<TIn><<<dim3(chunks), dim3(256), intra_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
+      k, v, beta, rk, gc, W, Ut, p.T, p.H, p.dk, p.dv, p.N, rev);
   stage_end(a, kStageIntra);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned tiles = unsigned(p.B) * p.H * ((p.dv + 15) / 16);
   stage_begin(a, kStageState);
-  state_kernel<TIn><<<dim3(tiles), dim3(256), 0, a.stream>>>(k, rk, gc, W, Ut, a.state_in, a.state_out, U, S0,
-                                                             p.T, p.H, p.dk, p.dv, p.N, rev);
+  state_kernel<TIn><<<dim3(tiles), dim3(256), state_lds_floats(p.dk) * sizeof(float), a.stream>>>(
+      k, rk, gc, W, Ut, a.state_in, a.state_out, U, S0, p.T, p.H, p.dk, p.dv, p.N, rev);
   stage_end(a, kStageState);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(a, kStageOutput);
   if (p.o_bf16)
-    output_kernel<TIn, uint16_t><<<dim3(chunks), dim3(256), 0, a.stream>>>(
+    output_kernel<TIn, uint16_t><<<dim3(chunks), dim3(256), output_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
         q, k, rq, rk, gc, U, S0, static_cast<uint16_t *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
   else
-    output_kernel<TIn, float><<<dim3(chunks), dim3(256), 0, a.stream>>>(
+    output_kernel<TIn, float><<<dim3(chunks), dim3(256), output_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
         q, k, rq, rk, gc, U, S0, static_cast<float *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
   stage_end(a, kStageOutput);
   return hipGetLastError();

@@ -27,40 +27,62 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn *__restrict__ q, co
   const int t0 = c * kChunk;
   const int n = min(kChunk, T - t0);
   const bool rev = flags & kReverse;
-  // one thread per token-head row; consecutive threads read consecutive rows
-  for (int idx = threadIdx.x; idx < n * H; idx += blockDim.x) {
+  // 16 lanes per token-head row: lane l sums d = l, l + 16, ... (coalesced 64-byte
+  // pieces), then the 16 partial sums are added by butterfly shuffles
+  const int sub = threadIdx.x & 15;
+  for (int idx = threadIdx.x >> 4; idx < n * H; idx += blockDim.x >> 4) {
     const int tt = idx / H, h = idx % H;
     const size_t th = (size_t(b) * T + phys_token(t0 + tt, T, rev)) * H + h;
     float rq = 1.f, rk = 1.f;
     if (!(flags & kQkPrenormalized)) {
       float sq = 0.f, sk = 0.f;
       const size_t row = th * size_t(dk);
-      for (int d = 0; d < dk; ++d) {
+      for (int d = sub; d < dk; d += 16) {
         const float a = load_f32(q, row + d), e = load_f32(k, row + d);
         sq = fmaf(a, a, sq);
         sk = fmaf(e, e, sk);
       }
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) {
+        sq += __shfl_xor(sq, m, 16);
+        sk += __shfl_xor(sk, m, 16);
+      }
       rq = 1.f / fmaxf(sqrtf(sq), 1e-6f);
       rk = 1.f / fmaxf(sqrtf(sk), 1e-6f);
     }
-    const float bl = beta[th];
-    const float bt = (flags & kBetaIsProb) ? bl : 1.f / (1.f + expf(-bl));
-    const size_t out = (size_t(b) * H + h) * T + t0 + tt;
-    o_beta[out] = bt;
-    o_rq[out] = rq;
-    o_rk[out] = rk;
+    if (sub == 0) {
+      const float bl = beta[th];
+      const float bt = (flags & kBetaIsProb) ? bl : 1.f / (1.f + expf(-bl));
+      const size_t out = (size_t(b) * H + h) * T + t0 + tt;
+      o_beta[out] = bt;
+      o_rq[out] = rq;
+      o_rk[out] = rk;
+    }
   }
-  // chunk-local inclusive cumsum of the floored log-decay, one thread per head.
-  // The reverse scan takes each token's decay from its successor in the
-  // original order (the same frame boundary), and none for the last token.
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    float G = 0.f;
-    const size_t out = (size_t(b) * H + h) * T + t0;
-    for (int tt = 0; tt < n; ++tt) {
-      const int tau = t0 + tt;
-      const float gv = !rev ? g[(size_t(b) * T + tau) * H + h] : (tau > 0 ? g[(size_t(b) * T + T - tau) * H + h] : 0.f);
-      G += fmaxf(gv, kLogDecayFloor);
-      o_gcum[out + tt] = G;
+  // chunk-local inclusive cumsum of the floored log-decay: the chunk's decays
+  // of up to 64 heads are staged in LDS (coalesced over heads), then one
+  // thread per head scans them.  The reverse scan takes each token's decay
+  // from its successor in the original order (the same frame boundary), and
+  // none for the last token.
+  __shared__ float gs[kChunk][65];
+  for (int h0 = 0; h0 < H; h0 += 64) {
+    const int nh = min(64, H - h0);
+    __syncthreads();  // the previous group's scan is done with gs
+    for (int idx = threadIdx.x; idx < n * nh; idx += blockDim.x) {
+      const int tt = idx / nh, hh = idx % nh, tau = t0 + tt;
+      const float gv = !rev ? g[(size_t(b) * T + tau) * H + h0 + hh]
+                            : (tau > 0 ? g[(size_t(b) * T + T - tau) * H + h0 + hh] : 0.f);
+      gs[tt][hh] = fmaxf(gv, kLogDecayFloor);
+    }
+    __syncthreads();
+    if (threadIdx.x < nh) {
+      const int h = h0 + threadIdx.x;
+      float G = 0.f;
+      const size_t out = (size_t(b) * H + h) * T + t0;
+      for (int tt = 0; tt < n; ++tt) {
+        G += gs[tt][threadIdx.x];
+        o_gcum[out + tt] = G;
+      }
     }
   }
 }

@@ -83,6 +83,19 @@ def test_portable_general_head_dims_fp32():
     _check(inp, o, st, o_ref, s_ref, TOL_F32, "dk64 dv48 fp32")
 
 
+def test_portable_largest_and_smallest_head_dims_fp32():
+    # d = 128 is the largest the portable kernels take (their LDS is sized for it); d = 1 the smallest
+    from hybrid_linear_attention_gdn_amd.inputs import Workload
+    for d, frame_tokens in ((128, 85), (1, 45)):  # T = 170 and 90: ragged last chunks
+        w = Workload(f"d{d}", 1, 2, 2, frame_tokens, "f32", 33 + d, state_std=0.1, head_dim=d)
+        T = w.seq_len
+        inp = make_inputs(w)
+        _say(f"case portable dk=dv={d} T={T}")
+        o, st = _run(inp)
+        o_ref, s_ref = oracle_for(inp)
+        _check(inp, o, st, o_ref, s_ref, TOL_F32, f"d{d} fp32")
+
+
 def test_clip_241f_full_config():
     w = WORKLOADS["clip_241f"]
     _say("case clip_241f (27,280 tokens x 20 heads)")
