@@ -256,7 +256,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the GDN forward's (batch, head) units "
+        print(json.dumps({"error": "bench.py measures one GPU only: the GDN forward's (batch, head) units "
                                    "are independent and would shard without communication; run --gpus 1"}))
         sys.exit(2)
     if args.attn:
