@@ -110,6 +110,21 @@ def test_bidir_window_2f(portable):
     np.testing.assert_array_equal(o16.float().cpu().numpy(), round_bf16(o))
 
 
+@pytest.mark.parametrize("portable", [False, True])
+def test_bidir_equals_forward_plus_reverse_bitwise(portable):
+    # o is the one fp32 sum of the two scans' outputs (the combine kernel); each
+    # scan alone is gdn_fwd with and without GDN_FLAG_REVERSE
+    w = Workload("bidir_sum", 1, 4, 3, 210, "bf16", 91)  # T = 630: seven full chunks and a ragged one
+    inp = make_inputs(w)
+    q, k, v, g, beta, _ = to_device(inp)
+    _say("case bidirectional = forward + reverse, portable=", portable)
+    o = gdn.gdn_bidir_fwd(q, k, v, g, beta, portable=portable)
+    of, _ = gdn.gdn_fwd(q, k, v, g, beta, state_out=None, portable=portable)
+    orv, _ = gdn.gdn_fwd(q, k, v, g, beta, state_out=None, portable=portable, reverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, of + orv)
+
+
 @pytest.mark.parametrize("T", [1, 81, 250])
 def test_bidir_ragged_and_fp32(T):
     w = Workload("ragged_bidir", 2, 3, 1, 10**9, "bf16", 70 + T)
