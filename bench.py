@@ -421,6 +421,11 @@ def main():
                  "steps": cold_steps, "note": "median over steps each preceded by a 512 MiB write"},
         "gdn_per_dit_forward_ms": {"x20_layers": round(20 * ms, 3), "x15_gdn_layers": round(15 * ms, 3)},
     }
+    if calls > 1:  # streaming: latency of one call (state carried in, out) and per chunk of 80 tokens
+        per_call_us = 1e3 * ms / calls
+        out["streaming"] = {"us_per_call": round(per_call_us, 2),
+                            "us_per_chunk": round(per_call_us / -(-(T // calls) // 80), 3),
+                            "tokens_per_call": T // calls}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens, args.cpu_seconds, args.bidir)
     print(json.dumps(out), flush=True)
