@@ -56,6 +56,11 @@ __host__ __device__ constexpr size_t state_lds_floats(int dk) {
 __host__ __device__ constexpr size_t output_lds_floats(int dk, int dv) {
   return size_t(C) * (dk + 1) + size_t(dv > C ? dv : C) * (dk + 1) + size_t(C) * (C + 1) + C;
 }
+static_assert(C % 16 == 0, "the blocked solve works on 16 x 16 blocks");
+static_assert(intra_lds_floats(kMaxPortableDim, kMaxPortableDim) * 4 <= 160 * 1024 &&
+                  state_lds_floats(kMaxPortableDim) * 4 <= 160 * 1024 &&
+                  output_lds_floats(kMaxPortableDim, kMaxPortableDim) * 4 <= 160 * 1024,
+              "every portable kernel fits one CU's LDS at the largest head dims");
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, const TIn *__restrict__ v,
