@@ -268,7 +268,15 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
 #pragma unroll
         for (int e = 0; e < 4; ++e) va[s][e] = v_elem(vl, 16 * tile + 4 * lg + e);
       }
-    __builtin_amdgcn_sched_barrier(0);  // the operands of Y and R first: they are on the critical path
+    const float gamma_n = csl[240];
+    f32x4 ya[2];
+    rows_times_S(fa, nA, Sh, Sl, Sth, Stl, ya);
+    // The phase-B operands (Q tiles, M and P' fragments) are read only after
+    // the Y products have issued: a wave tracks at most 15 LDS reads in
+    // flight, so reading them first held the products back until most of
+    // them had gone out.  They still land before barrier Y, which waits for
+    // them, and they are in flight while the products run.
+    __builtin_amdgcn_sched_barrier(0);
     RowFrags fb[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -303,9 +311,6 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
           for (int hl = 0; hl < 2; ++hl) Pt[s][hl] = ld16(kMBytes + p_off16(R, hl));
         cc[s] = ldf4(csl + 160 + 16 * R + 4 * lg);
       }
-    const float gamma_n = csl[240];
-    f32x4 ya[2];
-    rows_times_S(fa, nA, Sh, Sl, Sth, Stl, ya);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < ro.nY) {
