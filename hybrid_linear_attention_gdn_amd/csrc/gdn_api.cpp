@@ -279,20 +279,25 @@ gdn_status_t run_bidir(const gdn_problem_t *p, const void *q, const void *k, con
   gdn::Args a{q, k, v, g, beta, nullptr, nullptr, fwd_o, ws, st, prof};
   gdn::Plan R = P;
   R.flags |= GDN_FLAG_REVERSE;
+  // MFMA path, bf16 inputs, fp32 o: the reverse scan adds the forward scan's
+  // output (already in o) as it stores, one fp32 add per element like the
+  // combine kernel, which then does not run
+  R.o_add = P.mfma && !o_bf16 && !P.qkv_fp8;
+  float *rev_dst = R.o_add ? fwd_o : rev_o;
   hipError_t e;
   if (P.mfma && gdn::mfma_bidir_overlaps(P)) {
     gdn::Args ar = a;
-    ar.o = rev_o;
+    ar.o = rev_dst;
     ar.ws = ws + B.off_scan2;
     e = gdn::launch_mfma_bidir(P, a, R, ar);
   } else {
     e = enqueue(P, a);
     if (e == hipSuccess) {
-      a.o = rev_o;
+      a.o = rev_dst;
       e = enqueue(R, a);
     }
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !R.o_add) {
     gdn::stage_begin(a, gdn::kStageCombine);
     e = gdn::launch_combine(fwd_o, rev_o, o, o_bf16, size_t(P.B) * P.T * P.H * P.dv, st);
     gdn::stage_end(a, gdn::kStageCombine);

@@ -109,6 +109,16 @@ struct Rows {
   static_assert(rec_share(0) + 2 * row_share(0) < 64 && rec_share(2) + 2 * row_share(2) < 64, "vmcnt holds 63");
 };
 static_assert(kMBytes % 1024 == 0 && kPBytes % 1024 == 0 && kCsFloats * 4 == 1024, "whole 1 KB copies");
+// The reverse scan of the bidirectional layer (kAdd) adds the forward scan's
+// fp32 output, which o already holds, to its own: copy wave 2 brings the
+// chunk's 80 x 16 tile of o into one of two buffers after the row buffers
+// (bf16 rows only: 153,600 + 2 x 5,120 bytes is all of the CU's LDS).
+constexpr int kAddTile = C * 16 * 4;
+template <bool kFp8, bool kAdd>
+constexpr int chain_lds() { return Rows<kFp8>::kLds + (kAdd ? 2 * kAddTile : 0); }
+template <bool kFp8>
+constexpr int add_off(int c) { return Rows<kFp8>::kLds + (c & 1) * kAddTile; }
+static_assert(chain_lds<false, true>() <= 160 * 1024, "the addend tiles fit beside bf16 row buffers");
 static_assert(kLdsMP % 1024 == 0 && kLdsRows % 1024 == 0, "copy targets 1 KB aligned");
 
 struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k = d_k)
@@ -116,7 +126,7 @@ struct RowFrags {  // one lane's share of a 16-row tile of K or Q (A operand, k 
   F16 t;
 };
 
-template <int W, bool kOutBf16, bool kFp8, bool kRev>
+template <int W, bool kOutBf16, bool kFp8, bool kRev, bool kAdd>
 __device__ __forceinline__ void compute_role(const float *__restrict__ state_in, float *state_out,
                                              void *__restrict__ o, int T, int H, int cb, int ce, int b, int h,
                                              int nt, char *lds) {
@@ -297,6 +307,15 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
     F32 Pf[2][2][2];
     F16 Pt[2][2];
     f32x4 cc[2];
+    float adv[2][4];  // kAdd: o's elements of this wave's output tiles
+    if constexpr (kAdd) {
+      const float *at = reinterpret_cast<const float *>(lds + add_off<kFp8>(c));
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s < ro.nO)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) adv[s][e] = at[(16 * ro.O[s] + 4 * lg + e) * 16 + ln];
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       if (s < ro.nO) {
@@ -431,7 +450,10 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
     for (int s = 0; s < 2; ++s) {
       if (s < ro.nO) {
         const int R = ro.O[s];
-        const f32x4 acc = o0[s] + o1[s] + o2[s];
+        f32x4 acc = o0[s] + o1[s] + o2[s];
+        if constexpr (kAdd)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += adv[s][e];
         // rows past the chunk's end are aimed outside the store descriptor and dropped
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -461,13 +483,14 @@ __device__ __forceinline__ void compute_role(const float *__restrict__ state_in,
 // complete in issue order, so each wait names the number of younger copies
 // that may still be in flight (at most a record share and two row shares:
 // 57 of the 63 the counter holds).
-template <int L, bool kFp8, bool kRev>
+template <int L, bool kFp8, bool kRev, bool kAdd>
 __device__ __forceinline__ void copy_role(const char *__restrict__ q, const char *__restrict__ k,
                                           const char *__restrict__ v, const char *__restrict__ Mws,
-                                          const char *__restrict__ Pws, const float *__restrict__ CS, int T,
-                                          int H, int N, int cb, int ce, int b, int h, int nt, char *lds) {
+                                          const char *__restrict__ Pws, const float *__restrict__ CS,
+                                          const float *addend, int T, int H, int N, int cb, int ce, int b, int h,
+                                          int nt, char *lds) {
   using G = Rows<kFp8>;
-  constexpr int kRow = G::row_share(L);
+  constexpr int kRow = G::row_share(L) + (kAdd && L == 2 ? kAddTile / 1024 : 0);
   const int lane = threadIdx.x & 63;
   const size_t u = size_t(b) * H + h;
   const uint32_t row_bytes = uint32_t(H) * D * G::kElem;
@@ -477,6 +500,7 @@ __device__ __forceinline__ void copy_role(const char *__restrict__ q, const char
   // or past nv read as zero (forward: they lie past the buffer's end).
   auto row_ok = [&](int r, int nv) { return !kRev || r < nv; };
   auto row_at = [&](int r, int nv) { return uint32_t(kRev ? nv - 1 - r : r) * row_bytes; };
+  auto row_at_f32 = [&](int r, int nv) { return uint32_t(kRev ? nv - 1 - r : r) * uint32_t(H) * D * 4u; };
   // K / Q: copy i fills 1 KB of LDS rows, lane -> (row, slot lane % kSlots)
   // holding piece slot ^ (row % kSlots); slots past the row's pieces read as zero
   auto kq_off = [&](int i, int nv) {
@@ -507,6 +531,17 @@ __device__ __forceinline__ void copy_role(const char *__restrict__ q, const char
 #pragma unroll
       for (int i = 0; i < G::kVInstr; ++i) copy16(rv, rb + G::kV + 1024 * i, v_off(i, nv));
       copy16(make_rsrc(CS + (u * N + c) * kCsFloats, kCsFloats * 4), rb + G::kCs, 16u * lane);
+      if constexpr (kAdd) {  // o's 80 x 16 fp32 tile: copy i, lane l -> row 16 i + l / 4, columns 4 (l % 4) ..
+        const uint32_t orow = uint32_t(H) * D * 4u;
+        const auto ra = make_rsrc(addend + (size_t(b) * T + p0) * size_t(H) * D, uint32_t(nv) * orow);
+#pragma unroll
+        for (int i = 0; i < kAddTile / 1024; ++i) {
+          const int r = 16 * i + lane / 4;
+          const uint32_t off = row_ok(r, nv) ? row_at_f32(r, nv) + uint32_t(h * D + 16 * nt + 4 * (lane % 4)) * 4u
+                                             : kOutOfRange;
+          copy16(ra, lds + add_off<kFp8>(c) + 1024 * i, off);
+        }
+      }
     }
   };
   // waves 0, 1: kMShare KB of M each; wave 2: the rest of M and P'
@@ -629,13 +664,14 @@ __device__ __forceinline__ void warm_role(const char *__restrict__ q, const char
   if (T < 0 && sink != 0u) static_cast<uint32_t *>(o)[0] = sink;  // never taken: keeps the touches alive
 }
 
-template <bool kOutBf16, bool kFp8, bool kRev>
+template <bool kOutBf16, bool kFp8, bool kRev, bool kAdd>
 __global__ __launch_bounds__(kThreads) void chain_kernel(const char *__restrict__ q,
                                                          const char *__restrict__ k,
                                                          const char *__restrict__ v,
                                                          const char *__restrict__ Mws,
                                                          const char *__restrict__ Pws,
-                                                         const float *__restrict__ CS, const float *state_in,
+                                                         const float *__restrict__ CS, const float *addend,
+                                                         const float *state_in,
                                                          float *state_out, void *__restrict__ o, int T, int H,
                                                          int N, int cb, int ce, int units) {
   extern __shared__ __align__(16) char lds[];
@@ -647,13 +683,13 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const char *__restrict_
   const int b = u / H, h = u % H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wave) {
-    case 0: compute_role<0, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 1: compute_role<1, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 2: compute_role<2, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 3: compute_role<3, kOutBf16, kFp8, kRev>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
-    case 4: copy_role<0, kFp8, kRev>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 5: copy_role<1, kFp8, kRev>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
-    case 6: copy_role<2, kFp8, kRev>(q, k, v, Mws, Pws, CS, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 0: compute_role<0, kOutBf16, kFp8, kRev, kAdd>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 1: compute_role<1, kOutBf16, kFp8, kRev, kAdd>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 2: compute_role<2, kOutBf16, kFp8, kRev, kAdd>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 3: compute_role<3, kOutBf16, kFp8, kRev, kAdd>(state_in, state_out, o, T, H, cb, ce, b, h, nt, lds); break;
+    case 4: copy_role<0, kFp8, kRev, kAdd>(q, k, v, Mws, Pws, CS, addend, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 5: copy_role<1, kFp8, kRev, kAdd>(q, k, v, Mws, Pws, CS, addend, T, H, N, cb, ce, b, h, nt, lds); break;
+    case 6: copy_role<2, kFp8, kRev, kAdd>(q, k, v, Mws, Pws, CS, addend, T, H, N, cb, ce, b, h, nt, lds); break;
     default: warm_role<kFp8, kRev>(q, k, v, Mws, Pws, CS, o, T, H, N, cb, ce, b, h, nt); break;
   }
 }
@@ -695,20 +731,21 @@ void segment_bounds(int N, std::vector<int> &bounds) {
 }
 constexpr int kSegmentMinChunks = 64;
 
-template <bool kOutBf16, bool kFp8, bool kRev>
+template <bool kOutBf16, bool kFp8, bool kRev, bool kAdd = false>
 hipError_t launch_chain_typed(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb,
                               int ce, const float *sin, float *sout, hipStream_t st) {
   const char *q = static_cast<const char *>(a.q), *k = static_cast<const char *>(a.k),
              *v = static_cast<const char *>(a.v);
   const int units = p.B * p.H;
   const dim3 grid(8u * mfma::NT * unsigned((units + 7) / 8)), block(mfma::kThreads);
-  constexpr int lds = mfma::Rows<kFp8>::kLds;
+  constexpr int lds = mfma::chain_lds<kFp8, kAdd>();
   // more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU), once per instantiation
   static const hipError_t lds_ok = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&mfma::chain_kernel<kOutBf16, kFp8, kRev>),
+      reinterpret_cast<const void *>(&mfma::chain_kernel<kOutBf16, kFp8, kRev, kAdd>),
       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (lds_ok != hipSuccess) return lds_ok;
-  mfma::chain_kernel<kOutBf16, kFp8, kRev><<<grid, block, lds, st>>>(q, k, v, M, P, cs, sin, sout, a.o, p.T, p.H,
+  mfma::chain_kernel<kOutBf16, kFp8, kRev, kAdd><<<grid, block, lds, st>>>(
+      q, k, v, M, P, cs, kAdd ? static_cast<const float *>(a.o) : nullptr, sin, sout, a.o, p.T, p.H,
                                                                      p.N, cb, ce, units);
   return hipGetLastError();
 }
@@ -716,8 +753,11 @@ hipError_t launch_chain_typed(const Plan &p, const Args &a, const char *M, const
 template <bool kOutBf16, bool kFp8>
 hipError_t launch_chain_rev(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb,
                             int ce, const float *sin, float *sout, hipStream_t st) {
-  return (p.flags & kReverse) ? launch_chain_typed<kOutBf16, kFp8, true>(p, a, M, P, cs, cb, ce, sin, sout, st)
-                              : launch_chain_typed<kOutBf16, kFp8, false>(p, a, M, P, cs, cb, ce, sin, sout, st);
+  if (!(p.flags & kReverse)) return launch_chain_typed<kOutBf16, kFp8, false>(p, a, M, P, cs, cb, ce, sin, sout, st);
+  // the bidirectional layer's reverse scan adds o (the forward scan's fp32 output) to its own
+  if constexpr (!kOutBf16 && !kFp8)
+    if (p.o_add) return launch_chain_typed<false, false, true, true>(p, a, M, P, cs, cb, ce, sin, sout, st);
+  return launch_chain_typed<kOutBf16, kFp8, true>(p, a, M, P, cs, cb, ce, sin, sout, st);
 }
 
 hipError_t launch_chain(const Plan &p, const Args &a, const char *M, const char *P, const float *cs, int cb, int ce,

@@ -24,6 +24,9 @@ struct Plan {
   int qkv_bf16 = 0, qkv_fp8 = 0, o_bf16 = 0;
   uint32_t flags = 0;
   bool mfma = false;
+  // MFMA reverse scan, bf16 q/k/v, fp32 o: add o (the forward scan's output) to
+  // this scan's output as it is stored (the bidirectional layer's sum)
+  bool o_add = false;
   // byte offsets into the workspace
   size_t off_beta = 0, off_rq = 0, off_rk = 0, off_gcum = 0;       // fp32 [B,H,T]
   size_t off_W = 0, off_Ut = 0, off_U = 0, off_S0 = 0;              // portable path
