@@ -157,7 +157,8 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
  *
  * gdn_bidir_fwd: o [B, T, H, d_v] (fp32 or bf16) for every token; the flags
  * may not include GDN_FLAG_REVERSE.  Both scans accumulate in fp32; for bf16
- * o the sum is rounded once.  Size the workspace with
+ * o the sum is rounded once; either way each element is one fp32 add of the
+ * two scans' outputs.  Size the workspace with
  * gdn_bidir_workspace_bytes: the scan's workspace (twice with the MFMA
  * kernels, whose reverse scan prepares its operands while the forward scan's
  * state pass runs) plus one or two fp32 copies of o.  Same validation, ownership and asynchrony contract as gdn_fwd.
@@ -230,7 +231,9 @@ gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t
  * the number of calls that ran stage i into calls[i] (i < n; unused stages get
  * 0), then releases the events.  Stages: 0 "prep", 1 "intra", 2 "state"
  * (the fused state pass + output on the MFMA path), 3 "output" (portable
- * path only), 4 "combine" (gdn_bidir_fwd's sum of the two scans), 5 "in_proj", 6
+ * path only), 4 "combine" (gdn_bidir_fwd's sum of the two scans when a
+ * separate pass forms it: bf16 o, fp8 inputs or the portable kernels; otherwise
+ * the reverse scan's state pass adds the forward output as it stores), 5 "in_proj", 6
  * "out_proj" (the layer's projections).  The events are the only host resources the library creates.
  */
 gdn_status_t gdn_profile_begin(void);
