@@ -3,14 +3,20 @@
 
 A step is one gdn_fwd over the whole workload (for the streaming workload:
 the chain of gdn_chunk_step calls), inputs already resident in HBM.  Prints
-ONE JSON line: tokens/s per GDN layer, the dominant kernel against the HBM
-roofline (HIP events recorded by the library around each kernel, inside the
-timed region), and the fp64 CPU oracle timed on this host as a baseline.
+ONE JSON line: tokens/s per GDN layer, the path's kernel against the HBM
+roofline, and the fp64 CPU oracle timed on this host as a baseline.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload clip_241f]
 
-`roofline.traffic` is the dominant kernel's measured HBM bytes per launch from
-profiles/traffic_<kernel>_<workload>.json, reported only while the hash of the
+On the MFMA path one gdn_fwd is a short sequence of launches of a single
+kernel (scan_kernel: the state pass over one chunk range merged with the
+intra-chunk step of the next), and nothing else runs on the stream, so HIP
+events on that stream around the timed steps measure that kernel (the gaps
+between its launches included).  `roofline.achieved` is the algorithmic bytes
+of one step over that time.
+
+`roofline.traffic` is the kernel's measured HBM bytes per step from
+profiles/traffic_scan_<workload>.json, reported only while the hash of the
 kernel's sources stored there matches the sources of this tree.
 """
 from __future__ import annotations
@@ -27,27 +33,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
-# Algorithmic bytes per token-head that a kernel must move by the method's own
-# definition (q/k/v rows of 112 elements: 224 B each in bf16, 112 B in fp8;
-# fp32 g and beta 4 B each, o 448 B fp32 / 224 B bf16, the prep scalars 16 B),
-# and per (batch, head) for state in/out.
+# The state in and out of one (batch, head): 112 x 112 fp32.
 STATE_BYTES = 112 * 112 * 4
 
 
-def stage_algorithmic_bytes(stage: str, o_bytes: int, mfma: bool, row: int = 224) -> int:
-    """Per token-head algorithmic bytes of one kernel stage; `row` = bytes of one q/k/v row."""
-    if stage == "prep":
-        return 2 * row + 8 + 16      # reads q, k, g, beta; writes 4 scalars
-    if stage == "intra":
-        return 2 * row + 16 if mfma else 2 * row + 12  # reads q, k (+v on portable) and scalars
-    if stage == "state":
-        return (3 * row + 16 + o_bytes) if mfma else (row + 12)  # fused state pass + output on MFMA
-    if stage == "output":
-        return 2 * row + 12 + o_bytes
-    raise KeyError(stage)
-
-
 def path_algorithmic_bytes(o_bytes: int, row: int = 224) -> int:
+    """Bytes per token-head the forward must move by its definition: read the
+    q, k, v rows (`row` bytes each: 224 in bf16, 112 in fp8) and g, beta (4 B
+    each), write o (448 B fp32, 224 B bf16): 1,128 B for bf16 inputs, fp32 o."""
     return 3 * row + 8 + o_bytes
 
 
@@ -56,15 +49,29 @@ def flops_per_token_head(C: int = 80, d: int = 112) -> float:
     return 6 * d * d + 5 * C * d + C * C / 3
 
 
-def cpu_baseline(w, max_tokens: int, min_seconds: float, bidir: bool = False):
-    """fp64 oracle on a bounded sample of the same workload: all heads, the first
-    `max_tokens` tokens, repeated until `min_seconds` of wall time have passed."""
+def host_cpus():
+    """(CPUs this process may run on, the CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def _oracle_rate(w, T, threads, min_seconds, bidir):
     from hybrid_linear_attention_gdn_amd.inputs import make_inputs
     from oracle.bidirectional import bidirectional
-    from oracle.recurrence import default_threads, gdn_recurrence
-    T = min(w.seq_len, max_tokens)
+    from oracle.recurrence import gdn_recurrence
     inp = make_inputs(w, seq_len=T, frame_tokens=w.frame_tokens)
-    threads = min(default_threads(w.batch * w.heads), 16)
     runs, dt = 0, 0.0
     while runs == 0 or dt < min_seconds:
         t0 = time.perf_counter()
@@ -74,11 +81,27 @@ def cpu_baseline(w, max_tokens: int, min_seconds: float, bidir: bool = False):
             gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, nthreads=threads, want_state=True)
         dt += time.perf_counter() - t0
         runs += 1
-    return {"value": runs * w.batch * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return runs * w.batch * T / dt, runs, dt
+
+
+def cpu_baseline(w, max_tokens: int, min_seconds: float, bidir: bool = False):
+    """fp64 oracle on a bounded sample of the same workload: all (batch, head)
+    units, the first `max_tokens` tokens, repeated until `min_seconds` of wall
+    time have passed, on min(CPUs, B x H) threads (one unit per thread at a
+    time); then the same on one thread over a tenth of the tokens."""
+    nproc, model = host_cpus()
+    threads = max(1, min(nproc, w.batch * w.heads))
+    T = min(w.seq_len, max_tokens)
+    rate, runs, dt = _oracle_rate(w, T, threads, min_seconds, bidir)
+    T1 = max(80, T // 10)
+    rate1, runs1, dt1 = _oracle_rate(w, T1, 1, min_seconds / 4, bidir)
+    return {"value": round(rate, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.name}: all {w.batch}x{w.heads} (batch, head) units, first {T} of {w.seq_len} tokens, "
                       f"{runs} passes ({runs * w.batch * T * w.heads} token-heads, {dt:.1f} s wall, "
-                      f"fp64 C recurrence{', forward and reverse scans' if bidir else ''})",
-            "seconds": round(dt, 3)}
+                      f"fp64 C recurrence{', forward and reverse scans' if bidir else ''}, one thread per unit)",
+            "seconds": round(dt, 3), "nproc": nproc, "cpu_model": model,
+            "one_thread": {"value": round(rate1, 1), "unit": "tokens/s", "tokens": T1, "passes": runs1,
+                           "seconds": round(dt1, 3)}}
 
 
 def layer_bench(args):
@@ -90,7 +113,7 @@ def layer_bench(args):
     import numpy as np
     import torch
 
-    from hybrid_linear_attention_gdn_amd import gdn, layer
+    from hybrid_linear_attention_gdn_amd import layer
     from hybrid_linear_attention_gdn_amd.inputs import make_layer_inputs
 
     B, T, H, ft = 1, 27280, 20, 880
@@ -114,18 +137,35 @@ def layer_bench(args):
         step()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gdn.profile_begin()
     start.record(stream)
     for _ in range(args.steps):
         step()
     end.record(stream)
     torch.cuda.synchronize()
-    stages = gdn.profile_end()
     ms = start.elapsed_time(end) / args.steps
+
+    # each projection alone, on the same stream, timed by its own events
+    qkvbg = layer.in_proj(x, w_in, ft, stream=stream)
+    o_in = torch.zeros((B, T, HD), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t_proj = {"in_proj": timed(lambda: layer.in_proj(x, w_in, ft, stream=stream)),
+              "out_proj": timed(lambda: layer.out_proj(o_in, w_out, y_dtype=y_dtype, stream=stream))}
+    del qkvbg
     n_in = 3 * HD + 2 * H
     flops = {"in_proj": 2.0 * B * T * HD * n_in, "out_proj": 2.0 * B * T * HD * HD}
-    proj = {k: {"ms": round(stages[k][0], 5), "tflops": round(flops[k] / (stages[k][0] * 1e-3) / 1e12, 1)}
-            for k in flops if k in stages}
+    proj = {k: {"ms": round(t_proj[k], 5), "tflops": round(flops[k] / (t_proj[k] * 1e-3) / 1e12, 1)}
+            for k in flops}
     dom = "in_proj"
     achieved = proj[dom]["tflops"]
     cpu = None
@@ -138,7 +178,7 @@ def layer_bench(args):
             LY.layer(li.x[:, :Ts], li.w_in, li.w_out, H, ft, bidirectional_scan=bidir)
             runs += 1
         dt = time.perf_counter() - t0
-        cpu = {"value": round(runs * B * Ts / dt, 1), "unit": "tokens/s", "cores": os.cpu_count(),
+        cpu = {"value": round(runs * B * Ts / dt, 1), "unit": "tokens/s", "cores": host_cpus()[0],
                "kind": "oracle", "sample": f"layer: first {Ts} of {T} tokens, all {H} heads, {runs} passes, "
                                            f"{dt:.1f} s wall (numpy fp64 projections + C recurrence)"}
     out = {
@@ -155,7 +195,7 @@ def layer_bench(args):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel_ms": proj[dom]["ms"], "launches_per_step": 1.0},
         "projections": proj,
-        "stages_ms": {k: round(v[0], 5) for k, v in stages.items()},
+        "scan_ms_estimate": round(ms - sum(t_proj.values()), 5),
     }
     if cpu:
         out["cpu_baseline"] = cpu
@@ -240,7 +280,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="clip_241f")
     ap.add_argument("--o-dtype", default="fp32", choices=["fp32", "bf16"])
-    ap.add_argument("--portable", action="store_true", help="time the fp32 vector-ALU kernels instead")
+    ap.add_argument("--fp32-inputs", action="store_true",
+                    help="upload q, k, v as fp32 (the vector-ALU kernels) instead of the workload's dtype")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 30, help="tokens of the oracle's CPU sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -266,6 +307,10 @@ def main():
         layer_bench(args)
         return
 
+    gdn_bench(args)
+
+
+def gdn_bench(args):
     import numpy as np
     import torch
 
@@ -276,7 +321,9 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     inp = make_inputs(w)
-    if inp.dtype == "bf16":
+    if args.fp32_inputs:
+        q, k, v = (torch.from_numpy(np.asarray(a, np.float32)).to(dev) for a in (inp.q, inp.k, inp.v))
+    elif inp.dtype == "bf16":
         up = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
         q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
     elif inp.dtype == "fp8":  # E4M3FN codes
@@ -298,72 +345,68 @@ def main():
     Tc = T // calls
     o = torch.empty((B, T, H, d), dtype=o_dtype, device=dev)
     st = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-    p = gdn.problem(B, Tc, H, d, d, q.dtype, o_dtype, portable=args.portable)
-    ws = torch.empty(max(gdn.workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
-    mfma = bool(gdn.workspace_layout(p).mfma)
+    p = gdn.problem(B, Tc, H, d, d, q.dtype, o_dtype)
+    lay = gdn.workspace_layout(p)
+    mfma = bool(lay.mfma)
+    ws = torch.empty(max(gdn.bidir_workspace_bytes(p) if args.bidir else lay.total, 1), dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream(dev)
     if calls > 1:
         parts = [tuple(t[:, c * Tc:(c + 1) * Tc].contiguous() for t in (q, k, v, g, beta)) for c in range(calls)]
         o_parts = [torch.empty((B, Tc, H, d), dtype=o_dtype, device=dev) for _ in range(calls)]
-
-    if args.bidir:
-        ws = torch.empty(max(gdn.bidir_workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
+    # launches of the MFMA kernel per call: one per chunk range, plus one
+    N = -(-Tc // 80)
+    ranges = 0
+    if mfma and N > 0:
+        first = lay.first_range
+        ranges = 1 + -(-(N - first) // lay.range_cap) if N > first else 1
+    launches_per_call = ranges + 1 if mfma else None
 
     def step():
         if args.bidir:
-            gdn.gdn_bidir_fwd(q, k, v, g, beta, o, portable=args.portable, workspace=ws, stream=stream)
+            gdn.gdn_bidir_fwd(q, k, v, g, beta, o, workspace=ws, stream=stream)
         elif calls == 1:
-            gdn.gdn_fwd(q, k, v, g, beta, s0, st, o, portable=args.portable, workspace=ws, stream=stream)
+            gdn.gdn_fwd(q, k, v, g, beta, s0, st, o, workspace=ws, stream=stream)
         else:
             st.copy_(s0)
             for c in range(calls):
-                gdn.gdn_chunk_step(*parts[c], st, st, o_parts[c], portable=args.portable, workspace=ws,
-                                   stream=stream)
+                gdn.gdn_chunk_step(*parts[c], st, st, o_parts[c], workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: B={B} T={T} H={H} d={d} calls={calls} kernels={'mfma' if mfma else 'portable'} "
-          f"warmup done", file=sys.stderr, flush=True)
+          f"launches/call={launches_per_call} warmup done", file=sys.stderr, flush=True)
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    gdn.profile_begin()
     start.record(stream)
     for _ in range(args.steps):
         step()
     end.record(stream)
     torch.cuda.synchronize()
-    stages = gdn.profile_end()
     ms = start.elapsed_time(end) / args.steps
     token_heads = B * T * H
     tokens_per_s = B * T / (ms * 1e-3)
 
-    # dominant kernel against the HBM roofline
-    dom = max(stages, key=lambda s: stages[s][0] * stages[s][1])
-    dom_ms = stages[dom][0]
-    dom_calls_per_step = stages[dom][1] / args.steps
-    launch_th = token_heads / calls
-    # (the bidirectional layer's scans write fp32 o and carry no state in or out)
-    dom_bytes = stage_algorithmic_bytes(dom, 448 if args.bidir else o_bytes, mfma, row) * launch_th
-    if dom == "state" and not args.bidir:
-        dom_bytes += 2 * STATE_BYTES * B * H
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    # the bidirectional layer reads its inputs and writes o once (no state in or out)
-    path_bytes = path_algorithmic_bytes(o_bytes, row) * token_heads + (
+    # the path against the HBM roofline: the method's own bytes per step (the
+    # bidirectional layer reads its inputs and writes o once, no state in or out;
+    # a streaming step copies the initial state once, outside the definition)
+    step_bytes = path_algorithmic_bytes(o_bytes, row) * token_heads + (
         0 if args.bidir else 2 * STATE_BYTES * B * H * calls)
-    path_gbs = path_bytes / (ms * 1e-3) / 1e9
+    achieved = step_bytes / (ms * 1e-3) / 1e9
     tflops = flops_per_token_head() * token_heads * (2 if args.bidir else 1) / (ms * 1e-3) / 1e12
 
-    # measured HBM bytes per launch of the dominant kernel (rocprofv3 FETCH_SIZE and
-    # WRITE_SIZE, calibrated on a plain copy), valid only for the sources they were taken on
+    # measured HBM bytes per step of the kernel (rocprofv3 FETCH_SIZE and WRITE_SIZE,
+    # calibrated on a plain copy), valid only for the sources they were taken on
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
+    stage = "scan" if mfma else "portable"
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{stage}_{w.name}{'_bidir' if args.bidir else ''}.json")
     if os.path.exists(tpath):
         try:
             rec = json.load(open(tpath))
-            if rec.get("source_hash") == kernel_source_hash(dom, mfma) and rec.get("o_dtype") == args.o_dtype:
-                traffic = rec.get("bytes_per_launch")
+            if rec.get("source_hash") == kernel_source_hash(stage, mfma) and rec.get("o_dtype") == args.o_dtype:
+                traffic = rec.get("bytes_per_step")
         except (OSError, ValueError):
             traffic = None
 
@@ -393,6 +436,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    kname = "scan_kernel" if mfma else "prep + portable kernels"
     out = {
         "metric": (f"GDN {'bidirectional ' if args.bidir else ''}fwd tokens/s per layer (20h×112d, {dtype_name}) "
                    "+ % MFMA peak on 1 MI355X"),
@@ -411,12 +455,16 @@ def main():
                                                            else ""), "batch": B, "tokens": T, "heads": H, "head_dim": d,
                    "calls_per_step": calls, "o_dtype": args.o_dtype, "kernels": "mfma" if mfma else "portable",
                    "chunk": 80},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel_ms": round(dom_ms, 5), "launches_per_step": dom_calls_per_step},
-        "path_roofline": {"algorithmic_GBps": round(path_gbs, 1), "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
-                          "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
-        "stages_ms": {s: round(v[0], 5) for s, v in stages.items()},
+                     "algorithmic_bytes_per_step": step_bytes,
+                     "bytes_per_token_head": path_algorithmic_bytes(o_bytes, row),
+                     "kernel_ms": round(ms, 5), "launches_per_step": (launches_per_call * calls * (2 if args.bidir
+                                                                                                  else 1)
+                                                                     if mfma else None),
+                     "per": "step (all launches of the kernel in one step; HIP events on its stream)"},
+        "mfma": {"tflops": round(tflops, 2), "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "flops_per_token_head": flops_per_token_head()},
         "cold": {"ms_per_step": round(cold_ms, 5), "tokens_per_s": round(B * T / (cold_ms * 1e-3), 1),
                  "steps": cold_steps, "note": "median over steps each preceded by a 512 MiB write"},
         "gdn_per_dit_forward_ms": {"x20_layers": round(20 * ms, 3), "x15_gdn_layers": round(15 * ms, 3)},

@@ -9,15 +9,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsanawm_g
 
 GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP, GDN_ERR_INTERNAL = range(6)
 GDN_F32, GDN_BF16, GDN_FP8_E4M3 = 0, 1, 2
-GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_PORTABLE_KERNELS, GDN_FLAG_REVERSE = 1, 2, 4, 8
+GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_REVERSE = 1, 2, 8
 
 # every symbol include/sanawm_gdn.h declares
 EXPORTED = ("gdn_chunk_len", "gdn_workspace_bytes", "gdn_fwd", "gdn_chunk_step", "gdn_workspace_layout",
             "gdn_bidir_workspace_bytes", "gdn_bidir_fwd",
             "gdn_in_proj", "gdn_out_proj", "gdn_layer_workspace_bytes", "gdn_layer_fwd",
-            "gdn_profile_begin", "gdn_profile_end", "gdn_profile_stage_name",
             "gdn_status_string", "gdn_last_error", "gdn_version")
-NUM_STAGES = 7
 GDN_LAYER_BIDIRECTIONAL = 16
 # every symbol include/sanawm_attn.h declares
 EXPORTED_ATTN = ("attn_cache_bytes", "attn_block_fwd")
@@ -42,8 +40,9 @@ class AttnProblem(ctypes.Structure):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("beta", ctypes.c_size_t), ("rq", ctypes.c_size_t), ("rk", ctypes.c_size_t),
-                ("gcum", ctypes.c_size_t), ("mfrag", ctypes.c_size_t), ("pfrag", ctypes.c_size_t),
-                ("cscal", ctypes.c_size_t), ("total", ctypes.c_size_t), ("mfma", ctypes.c_int32)]
+                ("gcum", ctypes.c_size_t), ("rec", ctypes.c_size_t), ("rec_bytes", ctypes.c_size_t),
+                ("carry", ctypes.c_size_t), ("range_cap", ctypes.c_int32), ("first_range", ctypes.c_int32),
+                ("total", ctypes.c_size_t), ("mfma", ctypes.c_int32)]
 
 
 _lib = None
@@ -84,12 +83,6 @@ def load():
     lib.gdn_layer_workspace_bytes.argtypes = [LP, ctypes.POINTER(sz)]
     lib.gdn_layer_fwd.restype = ctypes.c_int
     lib.gdn_layer_fwd.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.gdn_profile_begin.restype = ctypes.c_int
-    lib.gdn_profile_begin.argtypes = []
-    lib.gdn_profile_end.restype = ctypes.c_int
-    lib.gdn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
-    lib.gdn_profile_stage_name.restype = ctypes.c_char_p
-    lib.gdn_profile_stage_name.argtypes = [ctypes.c_int32]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_last_error.restype = ctypes.c_char_p

@@ -6,57 +6,14 @@
 #include "sanawm_gdn.h"
 #include "sanawm_attn.h"
 
-#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <limits>
-#include <mutex>
 #include <vector>
 
 #include "gdn_internal.h"
-
-namespace {
-
-// ---- kernel-level timing (gdn_profile_begin / gdn_profile_end) ----
-struct Profiler {
-  std::mutex mu;
-  std::atomic<bool> on{false};
-  std::vector<hipEvent_t> open[gdn::kNumStages];  // begin events not yet closed, per stage
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> done[gdn::kNumStages];
-};
-Profiler &profiler() {
-  static Profiler p;
-  return p;
-}
-
-}  // namespace
-
-namespace gdn {
-
-void stage_begin(const Args &a, Stage s, hipStream_t stream) {
-  if (!a.profile) return;
-  hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, stream ? stream : a.stream);
-  Profiler &P = profiler();
-  std::lock_guard<std::mutex> lk(P.mu);
-  P.open[s].push_back(e);
-}
-
-void stage_end(const Args &a, Stage s, hipStream_t stream) {
-  if (!a.profile) return;
-  Profiler &P = profiler();
-  std::lock_guard<std::mutex> lk(P.mu);
-  if (P.open[s].empty()) return;
-  hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, stream ? stream : a.stream);
-  P.done[s].emplace_back(P.open[s].back(), e);
-  P.open[s].pop_back();
-}
-
-}  // namespace gdn
 
 namespace {
 
@@ -88,8 +45,7 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   if ((p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16 && p->qkv_dtype != GDN_FP8_E4M3) ||
       (p->o_dtype != GDN_F32 && p->o_dtype != GDN_BF16))
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown dtype (qkv=%d, o=%d)", p->qkv_dtype, p->o_dtype);
-  const uint32_t known =
-      GDN_FLAG_BETA_IS_PROB | GDN_FLAG_QK_PRENORMALIZED | GDN_FLAG_PORTABLE_KERNELS | GDN_FLAG_REVERSE;
+  const uint32_t known = GDN_FLAG_BETA_IS_PROB | GDN_FLAG_QK_PRENORMALIZED | GDN_FLAG_REVERSE;
   if (p->flags & ~known) return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags & ~known);
 
   gdn::Plan P;
@@ -103,9 +59,7 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   P.qkv_fp8 = p->qkv_dtype == GDN_FP8_E4M3;
   P.o_bf16 = p->o_dtype == GDN_BF16;
   P.flags = p->flags;
-  if (P.qkv_fp8 && (p->flags & GDN_FLAG_PORTABLE_KERNELS))
-    return fail(GDN_ERR_UNSUPPORTED, "fp8 q, k, v run on the MFMA kernels only");
-  P.mfma = gdn::kHaveMfmaPath && (P.qkv_bf16 || P.qkv_fp8) && !(p->flags & GDN_FLAG_PORTABLE_KERNELS);
+  P.mfma = gdn::kHaveMfmaPath && (P.qkv_bf16 || P.qkv_fp8);
   if (P.mfma) {
     if (P.dk != gdn::kMfmaDim || P.dv != gdn::kMfmaDim)
       return fail(GDN_ERR_UNSUPPORTED, "the MFMA kernels need d_k = d_v = %d (got %d, %d)", gdn::kMfmaDim, P.dk,
@@ -132,11 +86,10 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   if (!mul_ok(units, size_t(P.T), &bht) || !mul_ok(bht, sizeof(float), &sz))
     return fail(GDN_ERR_UNSUPPORTED, "problem too large");
   const size_t chunks = units * size_t(P.N);
-  if (P.mfma) {  // the MFMA path computes its per-token scalars inside the intra kernel
-    P.off_M = take(chunks * gdn::mfma_chunk_bytes_M());
-    P.off_P = take(chunks * gdn::mfma_chunk_bytes_P());
-    P.off_cs = take(chunks * gdn::mfma_chunk_bytes_cs());
-    P.off_Sseg = take(units * size_t(P.dv) * P.dk * sizeof(float));
+  if (P.mfma) {  // the MFMA path computes its per-token scalars inside the intra-chunk step
+    P.range_cap = std::max(1, std::min(P.N, gdn::kRangeCap));
+    P.off_rec = take(2 * size_t(P.range_cap) * units * gdn::mfma_record_bytes());
+    P.off_carry = take(units * size_t(P.dv) * P.dk * sizeof(float));
   } else {
     P.off_beta = take(sz);
     P.off_rq = take(sz);
@@ -208,21 +161,19 @@ gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const voi
               state_out,
               o,
               static_cast<char *>(workspace),
-              static_cast<hipStream_t>(hip_stream),
-              profiler().on.load(std::memory_order_relaxed)};
+              static_cast<hipStream_t>(hip_stream)};
   const hipError_t e = enqueue(P, a);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
   return GDN_OK;
 }
 
-// Workspace of the bidirectional layer: one scan's workspace, on the MFMA
-// path a second one (the reverse scan's intra kernel runs next to the forward
-// state pass and needs its own records), then the reverse scan's fp32 output
+// Workspace of the bidirectional layer: one scan's workspace (the two scans
+// run one after the other and share it), then the reverse scan's fp32 output
 // and, for bf16 o, the forward scan's fp32 output.
 struct BidirPlan {
   gdn::Plan scan;
-  size_t off_scan2 = 0, off_rev = 0, off_fwd = 0, total = 0;
+  size_t off_rev = 0, off_fwd = 0, total = 0;
 };
 
 gdn_status_t make_bidir_plan(const gdn_problem_t *p, BidirPlan *bp) {
@@ -236,8 +187,7 @@ gdn_status_t make_bidir_plan(const gdn_problem_t *p, BidirPlan *bp) {
   size_t n, bytes;
   if (!mul_ok(size_t(P.B) * size_t(P.H), size_t(P.T), &n) || !mul_ok(n, size_t(P.dv) * sizeof(float), &bytes))
     return fail(GDN_ERR_UNSUPPORTED, "problem too large");
-  B.off_scan2 = align_up(P.total);
-  B.off_rev = P.mfma ? align_up(B.off_scan2 + P.total) : B.off_scan2;
+  B.off_rev = align_up(P.total);
   B.off_fwd = align_up(B.off_rev + bytes);
   B.total = P.T == 0 ? 0 : (P.o_bf16 ? align_up(B.off_fwd + bytes) : B.off_fwd);
   *bp = B;
@@ -273,10 +223,9 @@ gdn_status_t run_bidir(const gdn_problem_t *p, const void *q, const void *k, con
   float *rev_o = reinterpret_cast<float *>(ws + B.off_rev);
   float *fwd_o = o_bf16 ? reinterpret_cast<float *>(ws + B.off_fwd) : static_cast<float *>(o);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const bool prof = profiler().on.load(std::memory_order_relaxed);
   // both scans write fp32; the combine kernel writes o in its own type
   P.o_bf16 = 0;
-  gdn::Args a{q, k, v, g, beta, nullptr, nullptr, fwd_o, ws, st, prof};
+  gdn::Args a{q, k, v, g, beta, nullptr, nullptr, fwd_o, ws, st};
   gdn::Plan R = P;
   R.flags |= GDN_FLAG_REVERSE;
   // MFMA path, bf16 inputs, fp32 o: the reverse scan adds the forward scan's
@@ -284,24 +233,12 @@ gdn_status_t run_bidir(const gdn_problem_t *p, const void *q, const void *k, con
   // combine kernel, which then does not run
   R.o_add = P.mfma && !o_bf16 && !P.qkv_fp8;
   float *rev_dst = R.o_add ? fwd_o : rev_o;
-  hipError_t e;
-  if (P.mfma && gdn::mfma_bidir_overlaps(P)) {
-    gdn::Args ar = a;
-    ar.o = rev_dst;
-    ar.ws = ws + B.off_scan2;
-    e = gdn::launch_mfma_bidir(P, a, R, ar);
-  } else {
-    e = enqueue(P, a);
-    if (e == hipSuccess) {
-      a.o = rev_dst;
-      e = enqueue(R, a);
-    }
+  hipError_t e = enqueue(P, a);
+  if (e == hipSuccess) {
+    a.o = rev_dst;
+    e = enqueue(R, a);
   }
-  if (e == hipSuccess && !R.o_add) {
-    gdn::stage_begin(a, gdn::kStageCombine);
-    e = gdn::launch_combine(fwd_o, rev_o, o, o_bf16, size_t(P.B) * P.T * P.H * P.dv, st);
-    gdn::stage_end(a, gdn::kStageCombine);
-  }
+  if (e == hipSuccess && !R.o_add) e = gdn::launch_combine(fwd_o, rev_o, o, o_bf16, size_t(P.B) * P.T * P.H * P.dv, st);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
   return GDN_OK;
@@ -333,9 +270,11 @@ gdn_status_t gdn_workspace_layout(const gdn_problem_t *p, gdn_workspace_layout_t
   layout->rq = P.mfma ? 0 : P.off_rq;
   layout->rk = P.mfma ? 0 : P.off_rk;
   layout->gcum = P.mfma ? 0 : P.off_gcum;
-  layout->mfrag = P.mfma ? P.off_M : 0;
-  layout->pfrag = P.mfma ? P.off_P : 0;
-  layout->cscal = P.mfma ? P.off_cs : 0;
+  layout->rec = P.mfma ? P.off_rec : 0;
+  layout->rec_bytes = P.mfma ? gdn::mfma_record_bytes() : 0;
+  layout->carry = P.mfma ? P.off_carry : 0;
+  layout->range_cap = P.mfma ? P.range_cap : 0;
+  layout->first_range = P.mfma ? std::min(P.N, std::min(gdn::kFirstRange, P.range_cap)) : 0;
   layout->total = P.total;
   layout->mfma = P.mfma ? 1 : 0;
   return GDN_OK;
@@ -434,12 +373,9 @@ gdn_status_t gdn_in_proj(const gdn_layer_t *L, const void *x, const void *w_in, 
   }
   gdn::Args a{};
   a.stream = static_cast<hipStream_t>(hip_stream);
-  a.profile = profiler().on.load(std::memory_order_relaxed);
-  gdn::stage_begin(a, gdn::kStageInProj);
   const hipError_t e = gdn::proj::launch_in_proj(
       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_in), P.M, P.H, L->seq_len, L->frame_tokens,
       static_cast<uint16_t *>(q), static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), beta, g, a.stream);
-  gdn::stage_end(a, gdn::kStageInProj);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
   return GDN_OK;
@@ -460,12 +396,9 @@ gdn_status_t gdn_out_proj(const gdn_layer_t *L, const void *o, const void *w_out
   }
   gdn::Args a{};
   a.stream = static_cast<hipStream_t>(hip_stream);
-  a.profile = profiler().on.load(std::memory_order_relaxed);
-  gdn::stage_begin(a, gdn::kStageOutProj);
   const hipError_t e = gdn::proj::launch_out_proj(static_cast<const uint16_t *>(o),
                                                   static_cast<const uint16_t *>(w_out), P.M, P.HD, y, P.y_bf16,
                                                   a.stream);
-  gdn::stage_end(a, gdn::kStageOutProj);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
   return GDN_OK;
@@ -537,45 +470,6 @@ const char *gdn_status_string(gdn_status_t s) {
 }
 
 const char *gdn_last_error(void) { return g_last_error; }
-
-gdn_status_t gdn_profile_begin(void) {
-  Profiler &P = profiler();
-  P.on.store(true);
-  return GDN_OK;
-}
-
-gdn_status_t gdn_profile_end(float *ms, int32_t *calls, int32_t n) {
-  Profiler &P = profiler();
-  P.on.store(false);
-  std::lock_guard<std::mutex> lk(P.mu);
-  gdn_status_t st = GDN_OK;
-  for (int s = 0; s < gdn::kNumStages; ++s) {
-    double sum = 0.0;
-    int cnt = 0;
-    for (auto &pr : P.done[s]) {
-      float t = 0.f;
-      hipError_t e = hipEventSynchronize(pr.second);
-      if (e == hipSuccess) e = hipEventElapsedTime(&t, pr.first, pr.second);
-      if (e != hipSuccess && st == GDN_OK) st = fail(GDN_ERR_HIP, "profile events: %s", hipGetErrorString(e));
-      sum += t;
-      ++cnt;
-      hipEventDestroy(pr.first);
-      hipEventDestroy(pr.second);
-    }
-    for (hipEvent_t e : P.open[s]) hipEventDestroy(e);
-    P.open[s].clear();
-    P.done[s].clear();
-    if (s < n) {
-      if (ms) ms[s] = cnt ? float(sum / cnt) : 0.f;
-      if (calls) calls[s] = cnt;
-    }
-  }
-  for (int s = gdn::kNumStages; s < n; ++s) {
-    if (ms) ms[s] = 0.f;
-    if (calls) calls[s] = 0;
-  }
-  return st;
-}
 
 // ---- streaming attention block (include/sanawm_attn.h) ----
 static gdn_status_t attn_plan(const attn_problem_t *p, gdn::AttnPlan &P) {
@@ -652,12 +546,6 @@ gdn_status_t attn_block_fwd(const attn_problem_t *p, int32_t block, const void *
   const hipError_t e = gdn::attn::launch_attn(P, block, q, k, v, cache, o, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return GDN_OK;
-}
-
-const char *gdn_profile_stage_name(int32_t stage) {
-  static const char *names[gdn::kNumStages] = {"prep",    "intra",   "state",   "output",
-                                               "combine", "in_proj", "out_proj"};
-  return (stage >= 0 && stage < gdn::kNumStages) ? names[stage] : "";
 }
 
 }  // extern "C"

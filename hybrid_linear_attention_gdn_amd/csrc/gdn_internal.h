@@ -13,9 +13,13 @@ constexpr int kChunk = 80;        // tokens per chunk (divides the 880-token lat
 constexpr int kMaxPortableDim = 128;
 constexpr int kMfmaDim = 112;     // head_dim of the SANA-WM DiT (20 heads x 112 = 2240)
 constexpr float kLogDecayFloor = -80.0f;
+// MFMA path: chunks in the first range (its intra-chunk step runs alone) and the
+// default length of the later ranges (the workspace ring holds two ranges)
+constexpr int kFirstRange = 8;
+constexpr int kRangeCap = 96;
 constexpr bool kHaveMfmaPath = true;
 
-enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kPortable = 4u, kReverse = 8u };
+enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kReverse = 8u };
 
 // Everything a launch sequence needs: the problem, the selected kernels and
 // where each intermediate lives inside the caller's workspace.
@@ -30,8 +34,11 @@ struct Plan {
   // byte offsets into the workspace
   size_t off_beta = 0, off_rq = 0, off_rk = 0, off_gcum = 0;       // fp32 [B,H,T]
   size_t off_W = 0, off_Ut = 0, off_U = 0, off_S0 = 0;              // portable path
-  size_t off_M = 0, off_P = 0, off_cs = 0;                           // MFMA path
-  size_t off_Sseg = 0;  // MFMA path: fp32 [B, H, d_v, d_k] state carried between chunk ranges
+  // MFMA path: a ring of two slots of range_cap x B*H chunk-head records
+  // (M | P' | scales, mfma_record_bytes() each) and the fp32 [B, H, d_v, d_k]
+  // state carried from one chunk range to the next
+  size_t off_rec = 0, off_carry = 0;
+  int range_cap = 0;
   size_t total = 0;
 };
 
@@ -42,35 +49,13 @@ struct Args {
   void *o;
   char *ws;
   hipStream_t stream;
-  bool profile;  // record timing events around each stage
 };
-
-// Timing stages (see gdn_profile_begin in include/sanawm_gdn.h).
-enum Stage : int {
-  kStagePrep = 0,
-  kStageIntra = 1,
-  kStageState = 2,
-  kStageOutput = 3,
-  kStageCombine = 4,
-  kStageInProj = 5,
-  kStageOutProj = 6,
-  kNumStages = 7
-};
-// timing events around a stage, on `stream` (default: the call's stream)
-void stage_begin(const Args &a, Stage s, hipStream_t stream = nullptr);
-void stage_end(const Args &a, Stage s, hipStream_t stream = nullptr);
 
 // Kernel launch sequences (each returns the first launch error, if any).
 hipError_t launch_prep(const Plan &p, const Args &a);
 hipError_t launch_portable(const Plan &p, const Args &a);
 hipError_t launch_mfma(const Plan &p, const Args &a);
 hipError_t launch_state_passthrough(const Plan &p, const Args &a);
-// The bidirectional layer on the MFMA path with the reverse scan's intra kernel
-// beside the forward state pass (on a second stream): possible when the state
-// pass leaves CUs free (one round of workgroups).  F and R use separate record
-// regions (af.ws + F.off_*, ar.ws + R.off_*).
-bool mfma_bidir_overlaps(const Plan &p);
-hipError_t launch_mfma_bidir(const Plan &F, const Args &af, const Plan &R, const Args &ar);
 // The layer's projections (proj.hip): x [M, H*112] -> q, k, v [M, H*112] bf16,
 // beta, g [M, H] fp32; o [M, HD] bf16 -> y [M, HD].  Weights are [out, in] bf16.
 namespace proj {
@@ -98,10 +83,8 @@ hipError_t launch_attn(const AttnPlan &p, int block, const void *q, const void *
                        void *o, hipStream_t stream);
 }
 
-// bytes needed by the MFMA path's own intermediates (beyond the prep scalars)
-size_t mfma_chunk_bytes_M();
-size_t mfma_chunk_bytes_P();
-size_t mfma_chunk_bytes_cs();
+// bytes of one chunk-head record of the MFMA path (M | P' | scales)
+size_t mfma_record_bytes();
 
 // ---- small device helpers shared by the kernel files ----
 // Physical token index of logical token tau: the reverse scan (kReverse)
@@ -119,6 +102,17 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+// two fp32 -> packed fp16 pair (first value in the low half), round to nearest even
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
+// The log-decay floor: g below -80 is read as -80 (a decay factor changes by at
+// most e^-80); NaN passes through unchanged, so a NaN gate propagates like any
+// other NaN input.
+__device__ __forceinline__ float floor_log_decay(float g) { return g < kLogDecayFloor ? kLogDecayFloor : g; }
 
 template <typename T> __device__ __forceinline__ float load_f32(const T *p, size_t i);
 template <> __device__ __forceinline__ float load_f32<float>(const float *p, size_t i) { return p[i]; }

@@ -1,9 +1,12 @@
-// Kernel "intra" of the MFMA family: the per-chunk operands of the state pass,
-// one workgroup (4 waves) per (b, h, chunk), fully parallel.
+// Intra-chunk work of the MFMA family: the per-chunk operands of the state
+// pass for one (b, h, chunk), run by a group of four waves (256 threads).  It
+// is a device function: the scan kernel (gdn_scan.hip) runs it in the blocks
+// that do not run the state pass.
 //
-// With raw bf16 rows K, Q of the chunk (fp8 inputs are widened to bf16 exactly on load) and fp32 scales (all derived here from
-// the raw inputs: rk = 1/||k||, rq = 1/||q||, beta = sigmoid(logit), G = the
-// chunk-local inclusive cumulative floored log-decay):
+// With raw bf16 rows K, Q of the chunk (fp8 inputs are widened to bf16 exactly
+// on load) and fp32 scales (all derived here from the raw inputs: rk = 1/||k||,
+// rq = 1/||q||, beta = sigmoid(logit), G = the chunk-local inclusive cumulative
+// floored log-decay):
 //   A_ri = beta_r rk_r rk_i e^{G_r - G_i} (k_r . k_i)   (i < r)
 //   P_ri = rq_r rk_i e^{G_r - G_i} (q_r . k_i)          (i <= r)
 //   T    = (I + A)^{-1}
@@ -19,17 +22,17 @@
 //     substitution (fp32, one column per thread), then block distance L = 1..4:
 //     T_IJ = -D_I sum_{K=J}^{I-1} A_IK T_KJ on the matrix cores with bf16 hi/lo
 //     operands and fp32 accumulation, one block per wave per level.
-//  4. M^T = T^T diag(s) K and P'^T = T^T P^T on the matrix cores, each wave
-//     owning whole token-row tiles (their hi/lo fragments are built once); the
-//     accumulators are exactly the A-operand fragments the state pass reads,
-//     split into bf16 hi/lo and stored.
+//  4. M^T = T^T diag(s) K and P'^T = T^T P^T on the matrix cores (bf16 hi/lo
+//     operands, fp32 accumulation), each wave owning whole token-row tiles;
+//     the accumulators are exactly the A-operand fragments the state pass
+//     reads.  They are rounded once to fp16 (round to nearest even) and stored.
 // T and P live in LDS as 16 x 16 fp32 blocks with 16-byte aligned rows, so
 // every operand fragment is one 128-bit LDS read.
+#pragma once
 #include "gdn_mfma_common.h"
 
 namespace gdn {
 namespace mfma {
-namespace {
 
 constexpr int kKrRow = 116;  // bf16 per K row (232 B): 8-byte reads of 16 rows hit distinct banks
 constexpr int kKtRow = 84;   // bf16 per K^T row (168 B)
@@ -70,14 +73,18 @@ __device__ __forceinline__ float lane_value(float x, int l) {
 // e^x on the hardware exp2 (relative error a few ulp for |x| up to ~100)
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 
-// q, k: bf16 or (kFp8) E4M3FN elements, addressed in bytes
+// One chunk-head: q, k bf16 or (kFp8) E4M3FN elements, addressed in bytes.
+// `lds` is this group's kLdsIntra bytes; `tid` its thread index 0..255.  Every
+// __syncthreads() here is reached by all threads of the block, whatever their
+// group: a group with valid == false (a block's spare half) runs the same
+// steps on zero rows and stores nothing.
 template <bool kFp8>
-__global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ q, const char *__restrict__ k,
-                                                       const float *__restrict__ g, const float *__restrict__ beta,
-                                                       char *__restrict__ Mout, char *__restrict__ Pout,
-                                                       float *__restrict__ CSout, int T, int H, int N,
-                                                       int c_first, int n_chunks, uint32_t flags) {
-  extern __shared__ __align__(16) char lds[];
+__device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ q, const char *__restrict__ k,
+                                            const float *__restrict__ g, const float *__restrict__ beta,
+                                            char *__restrict__ rec, int T, int H, int b, int h, int c,
+                                            uint32_t flags, int tid, bool valid) {
+  char *Mrec = rec + kRecM, *Prec = rec + kRecP;
+  float *cs = reinterpret_cast<float *>(rec + kRecCs);
   uint16_t *Kr = reinterpret_cast<uint16_t *>(lds + kLdsKr);
   uint16_t *Kt = reinterpret_cast<uint16_t *>(lds + kLdsKt);
   float *Tt = reinterpret_cast<float *>(lds + kLdsT);   // block (I, J), I >= J: [jj][m] = T[16I+m][16J+jj]
@@ -88,22 +95,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
   float *sbeta = sc, *srq = sc + 80, *srk = sc + 160, *sG = sc + 240, *ss = sc + 320;
   auto blk = [](float *base, int I, int J) { return base + tri(I, J) * kBlkF; };
 
-  // block -> (b, c, h) over chunks c_first .. c_first + n_chunks - 1, h fastest:
-  // neighbouring workgroups read neighbouring rows.  Chunks run last to
-  // first, so that the records and rows of the first chunks, which the state
-  // pass reads first, are the most recently touched when it starts (and are
-  // still in the last-level cache).
-  int x = blockIdx.x;
-  const int h = x % H;
-  x /= H;
-  const int c = c_first + (n_chunks - 1 - x % n_chunks);
-  const int b = x / n_chunks;
   const int t0 = c * C;
-  const int n = min(C, T - t0);
-  const size_t u = size_t(b) * H + h;
-  const size_t rec = u * N + c;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = valid ? min(C, T - t0) : 0;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int ln = lane & 15, lg = lane >> 4;
   const size_t rowstride = size_t(H) * D;  // elements between consecutive tokens
 
@@ -118,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
     const size_t th = (size_t(b) * T + phys_token(tau, T, rev)) * H + h;
     float gv = 0.f;
     if (ok) gv = !rev ? g[th] : (tau > 0 ? g[th + H] : 0.f);
-    gl[tid] = ok ? fmaxf(gv, kLogDecayFloor) : 0.f;
+    gl[tid] = ok ? floor_log_decay(gv) : 0.f;
     bl[tid] = ok ? beta[th] : 0.f;
   }
   // ---- (1) K and Q rows -> LDS (row-major); partial sums of squares over 14
@@ -176,7 +171,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
     const float G0_last = lane_value(G0, 63);
     const float Gl = G0_last + lane_value(G1, C - 65);  // G at the chunk's last token
     const int t = 64 * wave + lane;
-    float *cs = CSout + rec * kCsFloats;
     if (t < C) {
       const bool ok = t < n;
       float nk = 0.f, nq = 0.f;
@@ -196,13 +190,50 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
       srk[t] = rko;
       sG[t] = G;
       ss[t] = rko * fexp(Gl - G);
-      cs[t] = bo;
-      cs[80 + t] = bo * gam * rko;
-      cs[160 + t] = gam * rqo;
+      if (valid) {
+        cs[t] = bo;
+        cs[80 + t] = bo * gam;
+        cs[160 + t] = ok ? gam : 0.f;
+      }
     }
-    if (wave == 0 && lane == 0) cs[240] = fexp(Gl);
+    if (valid && wave == 0 && lane == 0) cs[240] = fexp(Gl);
   }
   __syncthreads();
+
+  // ---- (1b) the state pass's row operands, rounded to fp16, as fragment
+  // images: K~ = -diag(b) K^ and Q~ = diag(c) Q^, where K^ = diag(rk) K and
+  // Q^ = diag(rq) Q are the normalised rows and b = beta gamma, c = gamma the
+  // per-token scales (so that R = diag(a) V + K~ S^T and O = Q~ S^T + P' R come
+  // straight out of the matrix products).  Per token tile t, blocks kb = 0..2
+  // hold d_k 32 kb + 8 g .. + 7 of row 16 t + (lane & 15) (g = lane >> 4) for
+  // all 64 lanes.  Within a
+  // block the lane's eight d_k are in the "pair" order of the state's
+  // accumulator tiles: d_k 32 kb + 4 g .. + 3, then 32 kb + 16 + 4 g .. + 3; block
+  // 3 stores only d_k 96 + 4 g .. + 3 (8 bytes per lane).
+  if (valid) {
+    constexpr int kPerTile = 4 * 64;
+    for (int idx = tid; idx < 2 * CT * kPerTile; idx += 256) {
+      const int m = idx / (CT * kPerTile), w = idx % (CT * kPerTile), t = w / kPerTile, x = w % kPerTile;
+      const int kb = x / 64, l = x % 64, lg4 = l >> 4;
+      const int row = 16 * t + (l & 15);
+      const uint16_t *src = (m ? Qr : Kr) + row * kKrRow + 32 * kb + 4 * lg4;
+      const float gam = fexp(sG[row]);
+      const float sc = m ? gam * srq[row] : -(sbeta[row] * gam) * srk[row];
+      // d_k 32 kb + 4 g .. + 3 and, below d_k 112, 32 kb + 16 + 4 g .. + 3
+      const uint2 lo = *reinterpret_cast<const uint2 *>(src);
+      const uint2 hi = kb < 3 ? *reinterpret_cast<const uint2 *>(src + 16) : make_uint2(0u, 0u);
+      const uint32_t wd[4] = {lo.x, lo.y, hi.x, hi.y};
+      uint32_t pk[4];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2)
+        pk[i2] = pack_f16x2(sc * __uint_as_float(wd[i2] << 16), sc * __uint_as_float(wd[i2] & 0xffff0000u));
+      char *dst = rec + (m ? kRecQ : kRecK) + kq_off(t, kb);
+      if (kb < 3)
+        *reinterpret_cast<uint4 *>(dst + 16 * l) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      else
+        *reinterpret_cast<uint2 *>(dst + 8 * l) = make_uint2(pk[0], pk[1]);
+    }
+  }
 
   // ---- (2) K K^T (transposed A blocks of this wave's block-row) and K Q^T
   // K fragments over d in "pair" k-order: one tile = 3 x 32-deep + 1 x 16-deep
@@ -394,8 +425,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
   // Row r of T^T over columns i = 16p + 4lg .. +3 (p >= r / 16): one 128-bit read.
   auto tt4 = [&](int r, int p) { return ld4(blk(Tt, p, r >> 4) + (r & 15) * kBs + 4 * lg); };
   auto pair = [](const F16 &a, const F16 &b) { return F32{{a.w[0], a.w[1], b.w[0], b.w[1]}}; };
-  char *Mrec = Mout + rec * size_t(kMBytes);
-  char *Prec = Pout + rec * size_t(kPBytes);
   auto m_rows = [&](int Rt) {
     const int r = 16 * Rt + ln;
     F16 uh[CT], ul[CT];  // (T^T diag(s)) rows r over token tile p, hi/lo
@@ -431,15 +460,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
         }
       }
       // accumulator: column d = 16Dt + ln, rows r = 16Rt + 4lg + e -> M[d][r], the state pass's A-operand order
-      uint32_t hi[2], lo[2];
-      split4(acc, hi, lo);
-      if (Rt < 4) {
-        const int kb = Rt >> 1, half = Rt & 1;
-        *reinterpret_cast<uint2 *>(Mrec + m_off32(Dt, kb, 0) + lane * 16 + half * 8) = make_uint2(hi[0], hi[1]);
-        *reinterpret_cast<uint2 *>(Mrec + m_off32(Dt, kb, 1) + lane * 16 + half * 8) = make_uint2(lo[0], lo[1]);
-      } else {
-        *reinterpret_cast<uint2 *>(Mrec + m_off16(Dt, 0) + lane * 8) = make_uint2(hi[0], hi[1]);
-        *reinterpret_cast<uint2 *>(Mrec + m_off16(Dt, 1) + lane * 8) = make_uint2(lo[0], lo[1]);
+      if (valid) {
+        const uint2 w = pack_f16x4(acc);
+        if (Rt < 4)
+          *reinterpret_cast<uint2 *>(Mrec + m_off32(Dt, Rt >> 1) + lane * 16 + (Rt & 1) * 8) = w;
+        else
+          *reinterpret_cast<uint2 *>(Mrec + m_off16(Dt) + lane * 8) = w;
       }
     }
   };
@@ -481,15 +507,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
         }
       }
       // accumulator: column r = 16Rt + ln, rows i = 16It + 4lg + e -> P'[r][i], the state pass's A-operand order
-      uint32_t hi[2], lo[2];
-      split4(acc, hi, lo);
-      if (It == Rt && !(Rt & 1)) {
-        *reinterpret_cast<uint2 *>(Prec + p_off16(Rt, 0) + lane * 8) = make_uint2(hi[0], hi[1]);
-        *reinterpret_cast<uint2 *>(Prec + p_off16(Rt, 1) + lane * 8) = make_uint2(lo[0], lo[1]);
-      } else {
-        const int kb = It >> 1, half = It & 1;
-        *reinterpret_cast<uint2 *>(Prec + p_off32(Rt, kb, 0) + lane * 16 + half * 8) = make_uint2(hi[0], hi[1]);
-        *reinterpret_cast<uint2 *>(Prec + p_off32(Rt, kb, 1) + lane * 16 + half * 8) = make_uint2(lo[0], lo[1]);
+      if (valid) {
+        const uint2 w = pack_f16x4(acc);
+        if (It == Rt && !(Rt & 1))
+          *reinterpret_cast<uint2 *>(Prec + p_off16(Rt) + lane * 8) = w;
+        else
+          *reinterpret_cast<uint2 *>(Prec + p_off32(Rt, It >> 1) + lane * 16 + (It & 1) * 8) = w;
       }
     }
   };
@@ -499,30 +522,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(const char *__restrict__ 
     case 2: m_rows(2); p_rows(1); break;
     default: m_rows(3); m_rows(4); p_rows(0); break;
   }
-}
-
-}  // namespace
-
-hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs, int c_first, int c_end,
-                        hipStream_t stream) {
-  const char *q = static_cast<const char *>(a.q), *k = static_cast<const char *>(a.k);
-  const int n_chunks = c_end - c_first;
-  const unsigned blocks = unsigned(p.B) * p.H * unsigned(n_chunks);
-  // more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU)
-  static const hipError_t lds_bf16 = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel<false>),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsIntra);
-  static const hipError_t lds_fp8 = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel<true>),
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsIntra);
-  if (lds_bf16 != hipSuccess) return lds_bf16;
-  if (lds_fp8 != hipSuccess) return lds_fp8;
-  if (n_chunks <= 0) return hipSuccess;
-  if (p.qkv_fp8)
-    intra_kernel<true><<<dim3(blocks), dim3(256), kLdsIntra, stream>>>(q, k, a.g, a.beta, M, P, cs, p.T, p.H, p.N,
-                                                                      c_first, n_chunks, p.flags);
-  else
-    intra_kernel<false><<<dim3(blocks), dim3(256), kLdsIntra, stream>>>(q, k, a.g, a.beta, M, P, cs, p.T, p.H, p.N,
-                                                                       c_first, n_chunks, p.flags);
-  return hipGetLastError();
 }
 
 }  // namespace mfma

@@ -12,22 +12,34 @@
 //            P_ri = rq_r rk_i e^{G_r - G_i} (q_r . k_i)   (i <= r)
 //   S^T   <- gamma_n S^T + M R                        M  = K^T diag(s) T,
 //            s_i = rk_i e^{G_n - G_i}
+// The state pass takes the normalised rows K^ = diag(rk) K, Q^ = diag(rq) Q
+// with its scales folded in: K~ = -diag(beta gamma) K^ and Q~ = diag(gamma) Q^,
+// so that R = diag(beta) V + K~ S^T and O = Q~ S^T + P' R.
 // (derivation: the chunked WY form U = T R, O = diag(gamma) Q^ S^T + P U,
 // S_next = gamma_n S + U^T diag(e^{G_n - G}) K^, with the scales folded in).
 //
-// Kernel "intra" (one workgroup per (b, h, chunk), fully parallel) forms A and
-// P from K K^T and K Q^T on the matrix cores, solves T in LDS (fp32), and then
-// M and P' on the matrix cores.  It stores M and P' already split into bf16
-// hi + lo pairs in the exact register order the state pass consumes, and the
-// per-token scales.  Kernel "chain" (one workgroup per (b, h, 16 columns of
-// d_v), sequential over chunks) keeps its 16 x 112 slice of the fp32 state in
-// registers and runs the four products above per chunk.
+// The intra-chunk step (gdn_intra.h, one group of four waves per (b, h,
+// chunk), fully parallel) forms A and P from K K^T and K Q^T on the matrix
+// cores, solves T in LDS (fp32), and then M and P' on the matrix cores.  It
+// stores M and P' as fp16 in the exact register order the state pass
+// consumes, and the per-token scales.  The state pass (gdn_scan.hip, one
+// workgroup per (b, h, pair of 16-column tiles of d_v), sequential over
+// chunks) keeps its 112 x 16 slices of the fp32 state in registers and runs
+// the four products above per chunk.
 //
-// Precision: q, k, v enter the matrix cores as the exact bf16 inputs; every
-// derived operand (S, R, M, P', T) is split x = hi + lo with hi = bf16(x),
-// lo = bf16(x - hi) and multiplied as hi*hi + hi*lo + lo*hi (or hi*raw +
-// lo*raw), accumulating in fp32 -- a relative error near 2^-16 per operand
-// instead of bf16's unit roundoff 2^-8.
+// Precision.  The intra-chunk step works from the exact bf16 rows: K K^T and
+// K Q^T on bf16 matrix instructions, T by fp32 substitution and bf16 hi/lo
+// block products (x = hi + lo, hi = bf16(x), lo = bf16(x - hi): about 16
+// bits), M and P' from hi/lo operands, all accumulating in fp32.  The state
+// pass then takes every operand as fp16 (11 significant bits, round to
+// nearest even): the normalised rows K~, Q~ (|x| <= 1), M and P' from the
+// intra step, and S and R from its own fp32 registers.  S and R are scaled by
+// a power of two per 112 x 16 / 80 x 16 tile whenever the tile's largest
+// magnitude leaves [2^-6, 2^15), which keeps fp16's range out of the way;
+// the scale is undone exactly on the fp32 results.  Every product accumulates
+// in fp32 and the state stays fp32.  An fp64 emulation of exactly these
+// roundings gives 2.5e-3 to 3.1e-3 of rms(o) on the 241-frame and minute-scale
+// clips, against 2e-2 if the same operands were plain bf16.
 //
 // MFMA lane layouts (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16, lane l,
 // g = l >> 4): A row l & 15 and B column l & 15 hold k = 8g..8g+7 (4g..4g+3
@@ -50,12 +62,20 @@ constexpr int C = kChunk;    // 80
 constexpr int NT = D / 16;   // 7 column tiles of d_v (and row tiles of d_k)
 constexpr int CT = C / 16;   // 5 token tiles per chunk
 
-// bytes per chunk-head of the precomputed operands
-constexpr int kMBytes = NT * 5120;  // 7 d_k tiles x (2 K32 blocks + 1 K16 block) x hi/lo
-constexpr int kPBytes = 15360;      // lower-triangular token blocks of P', hi/lo
-constexpr int kCsFloats = 256;      // a[80], b[80], c[80], gamma_n, pad
+// One chunk-head record of fp16 fragment images (the state pass's operands)
+// and fp32 scales, in the order the state pass copies it: part A (K~, Q~, P',
+// scales: read before its mid-chunk barrier) then part B (M: read after it).
+// The scales are a = beta, b = beta gamma, c = gamma (per token) and gamma_n.
+constexpr int kKQBytes = CT * 3584;  // K~ or Q~: per token tile 3 K32 blocks of 1 KB + 1 of 512 B
+constexpr int kPBytes = 7680;        // lower-triangular token blocks of P'
+constexpr int kCsFloats = 256;       // a[80], b[80], c[80], gamma_n, pad
+constexpr int kMBytes = NT * 2560;   // 7 d_k tiles x (2 K32 blocks of 1 KB + 1 K16 block of 512 B)
+constexpr int kRecK = 0, kRecQ = kKQBytes, kRecP = 2 * kKQBytes, kRecCs = kRecP + kPBytes;
+constexpr int kRecM = kRecCs + kCsFloats * 4;     // 44,544: the end of part A
+constexpr int kRecBytes = kRecM + kMBytes;        // 62,464
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 struct F32 {  // 8 bf16 = one lane of a 32-deep operand
@@ -79,6 +99,16 @@ __device__ __forceinline__ f32x4 mma(const F16 &a, const F16 &b, f32x4 c) {
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// fp16 operands (eight per lane, packed in pairs) on the 16x16x32 fp16 instruction
+__device__ __forceinline__ f32x4 mma_h(const F32 &a, const F32 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
+// four fp32 -> four fp16 (round to nearest even), element order kept
+__device__ __forceinline__ uint2 pack_f16x4(const f32x4 &v) {
+  return make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
+}
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), both round-to-nearest-even;
 // four consecutive k-slots -> two packed words of hi and two of lo
@@ -133,18 +163,23 @@ __device__ __forceinline__ uint4 elems8_bf16(const Elems8<kFp8> &x) {
 }
 
 // ---------------------------------------------------------------------------
-// Byte offsets of the fragment-ordered operands inside one chunk-head record.
+// Byte offsets of the fragment-ordered fp16 operands inside their record parts.
+// K~, Q~: token tile t, block kb (d_k 32kb .. 32kb + 31 in the "pair" order of
+//    the state's accumulator tiles, 16 B per lane; block 3 holds only its slots
+//    0..3, d_k 96 + 4g .. + 3, 8 B per lane: d_k 112.. do not exist).
+__device__ __forceinline__ constexpr int kq_off(int t, int kb) { return t * 3584 + kb * 1024; }
 // M: tile mt (d_k rows 16mt..), blocks kb 0,1 (tokens 32kb.. paired, 16 B per
-//    lane) and the 16-deep block of tokens 64..79 (8 B per lane); hi then lo.
-__device__ __forceinline__ int m_off32(int mt, int kb, int hl) { return mt * 5120 + kb * 2048 + hl * 1024; }
-__device__ __forceinline__ int m_off16(int mt, int hl) { return mt * 5120 + 4096 + hl * 512; }
+//    lane) and the 16-deep block of tokens 64..79 (8 B per lane).
+__device__ __forceinline__ constexpr int m_off32(int mt, int kb) { return mt * 2560 + kb * 1024; }
+__device__ __forceinline__ constexpr int m_off16(int mt) { return mt * 2560 + 2048; }
 // P': row tile R (tokens 16R..) uses 32-deep blocks over token tiles (0,1),
 // (2,3) below its diagonal and, for even R, the 16-deep block of tile R.
-__device__ __forceinline__ int p_base(int R) {
-  return R == 0 ? 0 : R == 1 ? 1024 : R == 2 ? 3072 : R == 3 ? 6144 : 10240;
+__device__ __forceinline__ constexpr int p_base(int R) {
+  return R == 0 ? 0 : R == 1 ? 512 : R == 2 ? 1536 : R == 3 ? 3072 : 5120;
 }
-__device__ __forceinline__ int p_off32(int R, int kb, int hl) { return p_base(R) + kb * 2048 + hl * 1024; }
-__device__ __forceinline__ int p_off16(int R, int hl) { return p_base(R) + (R / 2) * 2048 + hl * 512; }
+__device__ __forceinline__ constexpr int p_off32(int R, int kb) { return p_base(R) + kb * 1024; }
+__device__ __forceinline__ constexpr int p_off16(int R) { return p_base(R) + (R / 2) * 1024; }
+static_assert(p_base(4) + 2560 == kPBytes, "P' record layout");
 
 // Raw buffer access (gfx9 descriptor, stride 0): an offset at or past
 // `bytes` reads zero and drops a store.
@@ -182,11 +217,6 @@ __device__ __forceinline__ void bare_barrier() {
 
 // lower-triangular 16x16 block index (I >= J)
 __device__ __forceinline__ constexpr int tri(int I, int J) { return I * (I + 1) / 2 + J; }
-
-// Launches the intra kernel writing M, P' and the chunk scales of chunks
-// c_first .. c_end - 1 of every (b, h) on `stream` (gdn_intra.hip).
-hipError_t launch_intra(const Plan &p, const Args &a, char *M, char *P, float *cs, int c_first, int c_end,
-                        hipStream_t stream);
 
 }  // namespace mfma
 }  // namespace gdn

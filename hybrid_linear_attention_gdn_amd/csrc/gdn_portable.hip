@@ -330,7 +330,6 @@ hipError_t launch_typed(const Plan &p, const Args &a) {
   float *S0 = reinterpret_cast<float *>(a.ws + p.off_S0);
   const unsigned chunks = unsigned(p.B) * p.H * p.N;
   const bool rev = p.flags & kReverse;
-  stage_begin(a, kStageIntra);
   constexpr int kD = kMaxPortableDim;
   static const hipError_t lds_ok[4] = {
       allow_lds(&intra_kernel<TIn>, intra_lds_floats(kD, kD)), allow_lds(&state_kernel<TIn>, state_lds_floats(kD)),
@@ -340,24 +339,19 @@ hipError_t launch_typed(const Plan &p, const Args &a) {
     if (le != hipSuccess) return le;
   intra_kernel<TIn><<<dim3(chunks), dim3(256), intra_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
       k, v, beta, rk, gc, W, Ut, p.T, p.H, p.dk, p.dv, p.N, rev);
-  stage_end(a, kStageIntra);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned tiles = unsigned(p.B) * p.H * ((p.dv + 15) / 16);
-  stage_begin(a, kStageState);
   state_kernel<TIn><<<dim3(tiles), dim3(256), state_lds_floats(p.dk) * sizeof(float), a.stream>>>(
       k, rk, gc, W, Ut, a.state_in, a.state_out, U, S0, p.T, p.H, p.dk, p.dv, p.N, rev);
-  stage_end(a, kStageState);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  stage_begin(a, kStageOutput);
   if (p.o_bf16)
     output_kernel<TIn, uint16_t><<<dim3(chunks), dim3(256), output_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
         q, k, rq, rk, gc, U, S0, static_cast<uint16_t *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
   else
     output_kernel<TIn, float><<<dim3(chunks), dim3(256), output_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
         q, k, rq, rk, gc, U, S0, static_cast<float *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
-  stage_end(a, kStageOutput);
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn *__restrict__ q, co
       const int tt = idx / nh, hh = idx % nh, tau = t0 + tt;
       const float gv = !rev ? g[(size_t(b) * T + tau) * H + h0 + hh]
                             : (tau > 0 ? g[(size_t(b) * T + T - tau) * H + h0 + hh] : 0.f);
-      gs[tt][hh] = fmaxf(gv, kLogDecayFloor);
+      gs[tt][hh] = floor_log_decay(gv);
     }
     __syncthreads();
     if (threadIdx.x < nh) {
@@ -126,7 +126,6 @@ hipError_t launch_prep(const Plan &p, const Args &a) {
   float *rk = reinterpret_cast<float *>(a.ws + p.off_rk);
   float *gc = reinterpret_cast<float *>(a.ws + p.off_gcum);
   dim3 grid(unsigned(p.B) * unsigned(p.N)), block(256);
-  stage_begin(a, kStagePrep);
   if (p.qkv_bf16)
     prep_kernel<uint16_t><<<grid, block, 0, a.stream>>>(static_cast<const uint16_t *>(a.q),
                                                         static_cast<const uint16_t *>(a.k), a.g, a.beta, beta,
@@ -135,7 +134,6 @@ hipError_t launch_prep(const Plan &p, const Args &a) {
     prep_kernel<float><<<grid, block, 0, a.stream>>>(static_cast<const float *>(a.q),
                                                      static_cast<const float *>(a.k), a.g, a.beta, beta, rq,
                                                      rk, gc, p.T, p.H, p.dk, p.N, p.flags);
-  stage_end(a, kStagePrep);
   return hipGetLastError();
 }
 

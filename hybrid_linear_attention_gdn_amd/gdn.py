@@ -32,10 +32,9 @@ def _dtype_code(t: torch.dtype) -> int:
 
 
 def problem(B, T, H, dk, dv, qkv_dtype, o_dtype, *, beta_is_prob=False, qk_prenormalized=False,
-            portable=False, reverse=False) -> L.Problem:
+            reverse=False) -> L.Problem:
     flags = ((L.GDN_FLAG_BETA_IS_PROB if beta_is_prob else 0) |
              (L.GDN_FLAG_QK_PRENORMALIZED if qk_prenormalized else 0) |
-             (L.GDN_FLAG_PORTABLE_KERNELS if portable else 0) |
              (L.GDN_FLAG_REVERSE if reverse else 0))
     return L.Problem(B, T, H, dk, dv, _dtype_code(qkv_dtype), _dtype_code(o_dtype), flags)
 
@@ -67,26 +66,12 @@ def chunk_len() -> int:
     return L.load().gdn_chunk_len()
 
 
-def profile_begin():
-    """Start recording HIP events around every kernel stage (see gdn_profile_begin)."""
-    _check(L.load().gdn_profile_begin())
-
-
-def profile_end():
-    """Stop recording; returns {stage name: (mean ms per call, calls)} for the stages that ran."""
-    lib = L.load()
-    ms = (ctypes.c_float * L.NUM_STAGES)()
-    calls = (ctypes.c_int32 * L.NUM_STAGES)()
-    _check(lib.gdn_profile_end(ms, calls, L.NUM_STAGES))
-    return {lib.gdn_profile_stage_name(i).decode(): (ms[i], calls[i]) for i in range(L.NUM_STAGES) if calls[i]}
-
-
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
 def _call(entry, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob, qk_prenormalized,
-          portable, workspace, stream, reverse=False, bidir=False):
+          workspace, stream, reverse=False, bidir=False):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, d_k]")
     B, T, H, dk = q.shape
@@ -111,7 +96,7 @@ def _call(entry, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob
     elif tuple(o.shape) != (B, T, H, dv) or not o.is_contiguous() or o.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("o must be a contiguous float32/bfloat16 tensor of shape [B, T, H, d_v]")
     p = problem(B, T, H, dk, dv, q.dtype, o.dtype, beta_is_prob=beta_is_prob,
-                qk_prenormalized=qk_prenormalized, portable=portable, reverse=reverse)
+                qk_prenormalized=qk_prenormalized, reverse=reverse)
     need = bidir_workspace_bytes(p) if bidir else workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -126,8 +111,7 @@ def _call(entry, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob
 
 
 def gdn_fwd(q, k, v, g, beta, state_in=None, state_out="new", o=None, *, o_dtype=torch.float32,
-            beta_is_prob=False, qk_prenormalized=False, portable=False, reverse=False, workspace=None,
-            stream=None):
+            beta_is_prob=False, qk_prenormalized=False, reverse=False, workspace=None, stream=None):
     """Frame-wise GDN forward over q, k [B,T,H,d_k], v [B,T,H,d_v] (bf16, fp8 E4M3FN or
     fp32), g (log-decay), beta (logits) [B,T,H] fp32.  ``state_out``: "new" allocates the
     final state, None skips it, a tensor receives it (may be ``state_in``).
@@ -136,25 +120,24 @@ def gdn_fwd(q, k, v, g, beta, state_in=None, state_out="new", o=None, *, o_dtype
         B, _, H, dk = q.shape
         state_out = torch.empty((B, H, v.shape[-1], dk), dtype=torch.float32, device=q.device)
     return _call(L.load().gdn_fwd, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob,
-                 qk_prenormalized, portable, workspace, stream, reverse=reverse)
+                 qk_prenormalized, workspace, stream, reverse=reverse)
 
 
 def gdn_bidir_fwd(q, k, v, g, beta, o=None, *, o_dtype=torch.float32, beta_is_prob=False,
-                  qk_prenormalized=False, portable=False, workspace=None, stream=None):
+                  qk_prenormalized=False, workspace=None, stream=None):
     """Bidirectional layer (gdn_bidir_fwd): the forward scan plus the reverse scan,
     both from a zero state.  Returns o."""
     o, _ = _call(L.load().gdn_bidir_fwd, q, k, v, g, beta, None, None, o, o_dtype, beta_is_prob,
-                 qk_prenormalized, portable, workspace, stream, bidir=True)
+                 qk_prenormalized, workspace, stream, bidir=True)
     return o
 
 
 def gdn_chunk_step(q, k, v, g, beta, state_in, state_out="new", o=None, *, o_dtype=torch.float32,
-                   beta_is_prob=False, qk_prenormalized=False, portable=False, reverse=False, workspace=None,
-                   stream=None):
+                   beta_is_prob=False, qk_prenormalized=False, reverse=False, workspace=None, stream=None):
     """One streaming call: like gdn_fwd with state_in required and T a multiple of
     the chunk length (80), which makes a rollout bitwise equal to one pass."""
     if isinstance(state_out, str):
         B, _, H, dk = q.shape
         state_out = torch.empty((B, H, v.shape[-1], dk), dtype=torch.float32, device=q.device)
     return _call(L.load().gdn_chunk_step, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob,
-                 qk_prenormalized, portable, workspace, stream, reverse=reverse)
+                 qk_prenormalized, workspace, stream, reverse=reverse)

@@ -13,12 +13,14 @@ Per-kernel means of a ``rocprofv3 --pmc`` run of rocprofv3's derived metrics
 
 HBM bytes of one kernel from two ``rocprofv3 --pmc`` runs (FETCH_SIZE, then
 WRITE_SIZE), each scaled by what the same counter reads for the elementwise
-copy of known size that ``bench.py --copy-mib N`` runs in the same process::
+copy of known size that ``bench.py --copy-mib N`` runs in the same process,
+per launch and per step (``--launches-per-step``: the kernel's launches in one
+bench step, which repeat identically from step to step)::
 
     python -m hybrid_linear_attention_gdn_amd.rocprof_summary traffic --fetch DIR --write DIR \\
-        --copy-mib N --kernel chain_kernel --stage state --workload clip_241f --o-dtype fp32 \\
-        --fetch-command "..." --write-command "..." --json profiles/traffic_state_clip_241f.json \\
-        --md profiles/chain_clip_241f_traffic.md
+        --copy-mib N --kernel scan_kernel --stage scan --workload clip_241f --o-dtype fp32 \\
+        --launches-per-step 6 --fetch-command "..." --write-command "..." \\
+        --json profiles/traffic_scan_clip_241f.json --md profiles/scan_clip_241f_traffic.md
 
 The JSON carries a hash of the kernel's sources (see ``kernel_source_hash``);
 ``bench.py`` reports the stored bytes only while the hash still matches.
@@ -39,8 +41,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 # Source files of the kernels a profiling stage runs.
 _STAGE_SOURCES = {
-    (True, "intra"): ["gdn_intra.hip"],
-    (True, "state"): ["gdn_chain.hip"],
+    (True, "scan"): ["gdn_scan.hip", "gdn_intra.h"],
+    (False, "portable"): [],
 }
 _COMMON = {True: ["gdn_mfma_common.h", "gdn_internal.h"], False: ["gdn_prep.hip", "gdn_portable.hip",
                                                                     "gdn_internal.h"]}
@@ -113,12 +115,11 @@ def stats(args) -> str:
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
     if args.bench_log:
         b = _bench_json(args.bench_log)
-        if b and "stages_ms" in b:
-            rl = b.get("roofline", {})
-            out += ["", f"bench.py's own HIP-event timing in the same run (per launch): "
-                        f"{rl.get('kernel', '?')} {1e3 * rl.get('kernel_ms', 0.0):.1f} us; "
-                        f"stages {', '.join(f'{k} {1e3 * v:.1f} us' for k, v in b.get('stages_ms', {}).items())}; "
-                        f"step {1e3 * b.get('ms_per_step', 0.0):.1f} us."]
+        rl = (b or {}).get("roofline", {})
+        if b and rl.get("launches_per_step"):
+            out += ["", f"bench.py's own HIP-event timing in the same run: {1e3 * b.get('ms_per_step', 0.0):.1f} us "
+                        f"per step of {rl['launches_per_step']} launches of {rl.get('kernel', '?')} "
+                        f"({b.get('value')} {b.get('unit')}; {rl.get('achieved')} GB/s algorithmic)."]
         elif b:
             out += ["", f"bench.py's own HIP-event timing in the same run: {1e3 * b.get('ms_per_step', 0.0):.1f} us "
                         f"per step ({b.get('value')} {b.get('unit')})."]
@@ -195,14 +196,17 @@ def traffic(args):
     kw = [v for n in _match(write, args.kernel) for v in write[n]]
     fetch_b = statistics.mean(kf) * 1024.0 * f_factor
     write_b = statistics.mean(kw) * 1024.0 * w_factor
+    L = args.launches_per_step
     rec = {
         "kernel": args.kernel, "stage": args.stage, "workload": args.workload, "o_dtype": args.o_dtype,
         "bytes_per_launch": round(fetch_b + write_b),
         "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+        "launches_per_step": L, "bytes_per_step": round(L * (fetch_b + write_b)),
+        "fetch_bytes_per_step": round(L * fetch_b), "write_bytes_per_step": round(L * write_b),
         "fetch_kib_raw": statistics.mean(kf), "write_kib_raw": statistics.mean(kw), "dispatches": [len(kf), len(kw)],
         "calibration": {"copy_mib": args.copy_mib, "fetch_kib_raw": statistics.mean(cal_f),
                         "write_kib_raw": statistics.mean(cal_w), "fetch_factor": f_factor, "write_factor": w_factor},
-        "source_hash": kernel_source_hash(args.stage, True),
+        "source_hash": kernel_source_hash(args.stage, args.stage != "portable"),
         "commands": [args.fetch_command, args.write_command],
     }
     md = ["# HBM traffic of `" + args.kernel + "` on " + args.workload, "",
@@ -211,10 +215,11 @@ def traffic(args):
           f"Calibration: the elementwise copy of {args.copy_mib} MiB that the same process runs reads "
           f"FETCH_SIZE {statistics.mean(cal_f):.0f} KiB and WRITE_SIZE {statistics.mean(cal_w):.0f} KiB for "
           f"{known_kib:.0f} KiB moved each way: factors {f_factor:.3f} (fetch) and {w_factor:.3f} (write).", "",
-          "| per launch | raw counter (KiB) | scaled bytes |", "|---|---:|---:|",
-          f"| fetched | {statistics.mean(kf):.0f} | {fetch_b:.4g} |",
-          f"| written | {statistics.mean(kw):.0f} | {write_b:.4g} |",
-          f"| total | | {fetch_b + write_b:.4g} |", "",
+          "| mean per launch | raw counter (KiB) | scaled bytes | per step (x " + str(L) + ") |",
+          "|---|---:|---:|---:|",
+          f"| fetched | {statistics.mean(kf):.0f} | {fetch_b:.4g} | {L * fetch_b:.4g} |",
+          f"| written | {statistics.mean(kw):.0f} | {write_b:.4g} | {L * write_b:.4g} |",
+          f"| total | | {fetch_b + write_b:.4g} | {L * (fetch_b + write_b):.4g} |", "",
           f"Kernel sources hash {rec['source_hash']}; dispatches averaged: {len(kf)} (fetch run), {len(kw)} "
           f"(write run)."]
     with open(args.json, "w") as fh:
@@ -222,7 +227,7 @@ def traffic(args):
         fh.write("\n")
     with open(args.md, "w") as fh:
         fh.write("\n".join(md) + "\n")
-    print(json.dumps({k: rec[k] for k in ("bytes_per_launch", "fetch_bytes_per_launch", "write_bytes_per_launch")}))
+    print(json.dumps({k: rec[k] for k in ("bytes_per_step", "fetch_bytes_per_step", "write_bytes_per_step")}))
 
 
 def main(argv=None):
@@ -241,6 +246,7 @@ def main(argv=None):
         t.add_argument(a, required=True)
     t.add_argument("--o-dtype", default="fp32")
     t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--launches-per-step", type=int, default=1)
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         sys.stdout.write(stats(args))

@@ -13,8 +13,12 @@ TOL_BF16 = 1e-2
 TOL_F32 = 1e-4
 
 
-def to_device(inp: Inputs, dev="cuda"):
-    if inp.dtype == "bf16":
+def to_device(inp: Inputs, dev="cuda", fp32=False):
+    """Upload the inputs.  ``fp32``: q, k, v as fp32 tensors of the same values
+    (a bf16 workload then runs on the fp32 vector-ALU kernels)."""
+    if fp32:
+        q, k, v = (torch.from_numpy(np.asarray(a, np.float32)).to(dev) for a in (inp.q, inp.k, inp.v))
+    elif inp.dtype == "bf16":
         up = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
         q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
     elif inp.dtype == "fp8":  # E4M3FN codes

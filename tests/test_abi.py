@@ -59,9 +59,17 @@ def test_workspace_bytes(lib):
     assert stp == L.GDN_OK and np_ > 0
     lay = L.WorkspaceLayout()
     assert lib.gdn_workspace_layout(ctypes.byref(_p()), ctypes.byref(lay)) == L.GDN_OK
-    assert lay.total == n and lay.mfma == 1 and lay.mfrag < lay.pfrag < lay.cscal < lay.total
+    # MFMA path: a ring of two chunk ranges of records per head, then the carried state
+    assert lay.total == n and lay.mfma == 1 and lay.rec < lay.carry < lay.total
+    assert lay.range_cap == 2 and lay.first_range == 2  # T = 160: two chunks
+    assert lay.carry - lay.rec >= 2 * lay.range_cap * 20 * lay.rec_bytes
+    assert lay.total - lay.carry >= 20 * 112 * 112 * 4
+    lay_l = L.WorkspaceLayout()
+    assert lib.gdn_workspace_layout(ctypes.byref(_p(seq_len=80 * 500)), ctypes.byref(lay_l)) == 0
+    assert lay_l.range_cap == 96 and lay_l.first_range == 8
+    assert lay_l.total < 2 * 96 * 20 * lay.rec_bytes + 20 * 112 * 112 * 4 + 4096  # bounded in T
     lay_p = L.WorkspaceLayout()
-    assert lib.gdn_workspace_layout(ctypes.byref(_p(flags=L.GDN_FLAG_PORTABLE_KERNELS)), ctypes.byref(lay_p)) == 0
+    assert lib.gdn_workspace_layout(ctypes.byref(_p(qkv_dtype=L.GDN_F32)), ctypes.byref(lay_p)) == 0
     assert lay_p.mfma == 0 and lay_p.beta < lay_p.rq < lay_p.rk < lay_p.gcum < lay_p.total
 
 
@@ -74,7 +82,8 @@ def test_workspace_bytes(lib):
     (dict(o_dtype=-1), L.GDN_ERR_INVALID_ARGUMENT),
     (dict(flags=64), L.GDN_ERR_INVALID_ARGUMENT),
     (dict(qkv_dtype=L.GDN_F32, head_dim_k=129), L.GDN_ERR_UNSUPPORTED),
-    (dict(flags=L.GDN_FLAG_PORTABLE_KERNELS, head_dim_v=200), L.GDN_ERR_UNSUPPORTED),
+    (dict(qkv_dtype=L.GDN_F32, head_dim_v=200), L.GDN_ERR_UNSUPPORTED),
+    (dict(flags=4), L.GDN_ERR_INVALID_ARGUMENT),  # the retired portable-kernel bit
     (dict(batch=1 << 20, num_heads=1 << 10), L.GDN_ERR_UNSUPPORTED),
 ])
 def test_bad_problems(lib, kw, status):
@@ -133,8 +142,6 @@ def test_fp8_problems(lib):
     lay = L.WorkspaceLayout()
     assert lib.gdn_workspace_layout(ctypes.byref(_p(qkv_dtype=L.GDN_FP8_E4M3)), ctypes.byref(lay)) == L.GDN_OK
     assert lay.mfma == 1
-    assert _ws(lib, _p(qkv_dtype=L.GDN_FP8_E4M3, flags=L.GDN_FLAG_PORTABLE_KERNELS))[0] == L.GDN_ERR_UNSUPPORTED
-    assert b"fp8" in lib.gdn_last_error()
     assert _ws(lib, _p(qkv_dtype=L.GDN_FP8_E4M3, head_dim_k=64, head_dim_v=64))[0] == L.GDN_ERR_UNSUPPORTED
     assert _ws(lib, _p(qkv_dtype=3))[0] == L.GDN_ERR_INVALID_ARGUMENT
 
@@ -145,18 +152,17 @@ def test_reverse_flag_and_bidirectional_host_checks(lib):
     assert _ws(lib, rev) == _ws(lib, _p())
     assert _call(lib, "gdn_chunk_step", rev) == L.GDN_ERR_INVALID_ARGUMENT
     assert b"REVERSE" in lib.gdn_last_error()
-    # the bidirectional layer: the scan's workspace (twice on the MFMA path) +
-    # the reverse scan's fp32 o (+ the forward scan's for bf16 o), each
-    # 256-byte aligned
+    # the bidirectional layer: one scan's workspace (the two scans run one
+    # after the other) + the reverse scan's fp32 o (+ the forward scan's for
+    # bf16 o), each 256-byte aligned
     o_bytes = 1 * 160 * 20 * 112 * 4
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     n = ctypes.c_size_t(0)
-    for o_dtype, flags, scans, copies in ((L.GDN_F32, 0, 2, 1), (L.GDN_BF16, 0, 2, 2),
-                                          (L.GDN_F32, L.GDN_FLAG_PORTABLE_KERNELS, 1, 1),
-                                          (L.GDN_BF16, L.GDN_FLAG_PORTABLE_KERNELS, 1, 2)):
-        p = _p(o_dtype=o_dtype, flags=flags)
+    for o_dtype, qkv, copies in ((L.GDN_F32, L.GDN_BF16, 1), (L.GDN_BF16, L.GDN_BF16, 2),
+                                 (L.GDN_F32, L.GDN_F32, 1), (L.GDN_BF16, L.GDN_F32, 2)):
+        p = _p(o_dtype=o_dtype, qkv_dtype=qkv)
         assert lib.gdn_bidir_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == L.GDN_OK
-        assert n.value == scans * up(_ws(lib, p)[1]) + copies * up(o_bytes)
+        assert n.value == up(_ws(lib, p)[1]) + copies * up(o_bytes)
     assert lib.gdn_bidir_workspace_bytes(ctypes.byref(rev), ctypes.byref(n)) == L.GDN_ERR_INVALID_ARGUMENT
     assert lib.gdn_bidir_workspace_bytes(ctypes.byref(_p(seq_len=0)), ctypes.byref(n)) == L.GDN_OK and n.value == 0
     vp = lambda x: ctypes.c_void_p(x)  # noqa: E731
@@ -172,7 +178,6 @@ def test_reverse_flag_and_bidirectional_host_checks(lib):
     assert bidir(o=0x80008) == L.GDN_ERR_INVALID_ARGUMENT
     assert bidir(bytes=n.value - 1) == L.GDN_ERR_WORKSPACE
     assert bidir(ws=None) == L.GDN_ERR_WORKSPACE
-    assert lib.gdn_profile_stage_name(4) == b"combine"
 
 
 def test_unsupported_head_dim_on_mfma_path(lib):

@@ -38,14 +38,14 @@ def _sel(inp, heads=None, t_end=None):
     return arrs
 
 
-@pytest.mark.parametrize("portable", [False, True])
-def test_reverse_scan_window_2f(portable):
+@pytest.mark.parametrize("fp32", [False, True])
+def test_reverse_scan_window_2f(fp32):
     w = WORKLOADS["window_2f"]
     inp = make_inputs(w)
     s_in = (0.02 * np.random.default_rng(21).standard_normal((1, 20, 112, 112))).astype(np.float32)
-    _say("case reverse scan window_2f portable=", portable)
-    q, k, v, g, beta, _ = to_device(inp)
-    o, st = gdn.gdn_fwd(q, k, v, g, beta, torch.from_numpy(s_in).cuda(), reverse=True, portable=portable)
+    _say("case reverse scan window_2f fp32 inputs=", fp32)
+    q, k, v, g, beta, _ = to_device(inp, fp32=fp32)
+    o, st = gdn.gdn_fwd(q, k, v, g, beta, torch.from_numpy(s_in).cuda(), reverse=True)
     torch.cuda.synchronize()
     o_ref, s_ref = BD.reverse_scan(*_sel(inp), s_in)
     _check(o.cpu().numpy(), o_ref, TOL_BF16, "reverse window_2f", st.cpu().numpy(), s_ref)
@@ -56,12 +56,12 @@ def test_reverse_scan_ragged(T, B, H):
     w = Workload("ragged_rev", B, H, 1, 10**9, "bf16", 60 + T, state_std=0.05)
     inp = make_inputs(w, seq_len=T, frame_tokens=97)
     _say("case reverse ragged", T, B, H)
-    q, k, v, g, beta, s0 = to_device(inp)
     o_ref, s_ref = BD.reverse_scan(*_sel(inp), inp.state0)
-    for portable in (False, True):
-        o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=True, portable=portable)
+    for fp32 in (False, True):
+        q, k, v, g, beta, s0 = to_device(inp, fp32=fp32)
+        o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=True)
         torch.cuda.synchronize()
-        _check(o.cpu().numpy(), o_ref, TOL_BF16, f"reverse T={T} portable={portable}", st.cpu().numpy(), s_ref)
+        _check(o.cpu().numpy(), o_ref, TOL_BF16, f"reverse T={T} fp32 inputs={fp32}", st.cpu().numpy(), s_ref)
 
 
 def test_reverse_scan_fp32_portable():
@@ -75,15 +75,15 @@ def test_reverse_scan_fp32_portable():
     _check(o.cpu().numpy(), o_ref, TOL_F32, "reverse fp32", st.cpu().numpy(), s_ref)
 
 
-def test_reverse_chunk_ranges_on_two_streams_equal_one_launch():
-    """B = 2 x 20 heads: the state pass runs in chunk ranges beside the intra
-    kernel on a second stream; batch 0 must equal the B = 1 result bit for bit."""
+def test_reverse_batch_copies_equal_single_batch():
+    """B = 2 x 20 heads (another split of the merged launches than B = 1): both
+    batches must equal the B = 1 result bit for bit."""
     w = WORKLOADS["clip_241f"]
     inp = make_inputs(w, seq_len=5063)
     s_in = (0.02 * np.random.default_rng(22).standard_normal((1, 20, 112, 112))).astype(np.float32)
     q, k, v, g, beta, _ = to_device(inp)
     s0 = torch.from_numpy(s_in).cuda()
-    _say("case reverse, two streams: B=2 vs B=1, T=5063")
+    _say("case reverse, batch copies: B=2 vs B=1, T=5063")
     o1, st1 = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=True)
     cat = lambda t: torch.cat([t, t], 0).contiguous()  # noqa: E731
     o2, st2 = gdn.gdn_fwd(cat(q), cat(k), cat(v), cat(g), cat(beta), cat(s0), reverse=True)
@@ -91,18 +91,18 @@ def test_reverse_chunk_ranges_on_two_streams_equal_one_launch():
     assert torch.equal(o2[:1], o1) and torch.equal(o2[1:], o1)
     assert torch.equal(st2[:1], st1) and torch.equal(st2[1:], st1)
     o_ref, s_ref = BD.reverse_scan(*_sel(inp, heads=[0, 19]), s_in[:, [0, 19]])
-    _check(o1.cpu().numpy()[:, :, [0, 19]], o_ref, TOL_BF16, "reverse two streams, heads 0 and 19",
+    _check(o1.cpu().numpy()[:, :, [0, 19]], o_ref, TOL_BF16, "reverse batch copies, heads 0 and 19",
            st1.cpu().numpy()[:, [0, 19]], s_ref)
 
 
-@pytest.mark.parametrize("portable", [False, True])
-def test_bidir_window_2f(portable):
+@pytest.mark.parametrize("fp32", [False, True])
+def test_bidir_window_2f(fp32):
     w = WORKLOADS["window_2f"]
     inp = make_inputs(w)
-    _say("case bidirectional window_2f portable=", portable)
-    q, k, v, g, beta, _ = to_device(inp)
-    o = gdn.gdn_bidir_fwd(q, k, v, g, beta, portable=portable)
-    o16 = gdn.gdn_bidir_fwd(q, k, v, g, beta, o_dtype=torch.bfloat16, portable=portable)
+    _say("case bidirectional window_2f fp32 inputs=", fp32)
+    q, k, v, g, beta, _ = to_device(inp, fp32=fp32)
+    o = gdn.gdn_bidir_fwd(q, k, v, g, beta)
+    o16 = gdn.gdn_bidir_fwd(q, k, v, g, beta, o_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     o = o.cpu().numpy()
     _check(o, BD.bidirectional(*_sel(inp)), TOL_BF16, "bidirectional window_2f")
@@ -110,19 +110,36 @@ def test_bidir_window_2f(portable):
     np.testing.assert_array_equal(o16.float().cpu().numpy(), round_bf16(o))
 
 
-@pytest.mark.parametrize("portable", [False, True])
-def test_bidir_equals_forward_plus_reverse_bitwise(portable):
-    # o is the one fp32 sum of the two scans' outputs (the combine kernel); each
-    # scan alone is gdn_fwd with and without GDN_FLAG_REVERSE
+@pytest.mark.parametrize("fp32", [False, True])
+def test_bidir_equals_forward_plus_reverse_bitwise(fp32):
+    # o is the one fp32 sum of the two scans' outputs (formed as the reverse
+    # scan stores, or by the combine kernel); each scan alone is gdn_fwd with
+    # and without GDN_FLAG_REVERSE
     w = Workload("bidir_sum", 1, 4, 3, 210, "bf16", 91)  # T = 630: seven full chunks and a ragged one
     inp = make_inputs(w)
-    q, k, v, g, beta, _ = to_device(inp)
-    _say("case bidirectional = forward + reverse, portable=", portable)
-    o = gdn.gdn_bidir_fwd(q, k, v, g, beta, portable=portable)
-    of, _ = gdn.gdn_fwd(q, k, v, g, beta, state_out=None, portable=portable)
-    orv, _ = gdn.gdn_fwd(q, k, v, g, beta, state_out=None, portable=portable, reverse=True)
+    q, k, v, g, beta, _ = to_device(inp, fp32=fp32)
+    _say("case bidirectional = forward + reverse, fp32 inputs=", fp32)
+    o = gdn.gdn_bidir_fwd(q, k, v, g, beta)
+    of, _ = gdn.gdn_fwd(q, k, v, g, beta, state_out=None)
+    orv, _ = gdn.gdn_fwd(q, k, v, g, beta, state_out=None, reverse=True)
     torch.cuda.synchronize()
     assert torch.equal(o, of + orv)
+
+
+def test_bidir_batch_copies_equal_single_batch():
+    """The bidirectional layer at B = 2 x 20 heads with batch 1 a copy of batch
+    0: both batches equal the B = 1 layer bit for bit (ragged T = 5,063)."""
+    w = WORKLOADS["clip_241f"]
+    inp = make_inputs(w, seq_len=5063)
+    q, k, v, g, beta, _ = to_device(inp)
+    _say("case bidirectional, batch copies: B=2 vs B=1, T=5063")
+    o1 = gdn.gdn_bidir_fwd(q, k, v, g, beta)
+    cat = lambda t: torch.cat([t, t], 0).contiguous()  # noqa: E731
+    o2 = gdn.gdn_bidir_fwd(cat(q), cat(k), cat(v), cat(g), cat(beta))
+    torch.cuda.synchronize()
+    assert torch.equal(o2[:1], o1) and torch.equal(o2[1:], o1)
+    o_ref = BD.bidirectional(*_sel(inp, heads=[0, 19]))
+    _check(o1.cpu().numpy()[:, :, [0, 19]], o_ref, TOL_BF16, "bidirectional batch copies, heads 0 and 19")
 
 
 @pytest.mark.parametrize("T", [1, 81, 250])

@@ -36,17 +36,17 @@ def test_flags_match_oracle(beta_is_prob, qk_pre, reverse):
     inp = _flagged_inputs(421, 90 + 2 * beta_is_prob + qk_pre + 4 * reverse)
     if not beta_is_prob:  # logits again for this case
         inp.beta = np.log(inp.beta / (1 - inp.beta)).astype(np.float32)
-    q, k, v, g, beta, s0 = to_device(inp)
     kw = dict(beta_is_prob=beta_is_prob, qk_prenormalized=qk_pre)
     if reverse:
         o_ref, s_ref = BD.reverse_scan(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, **kw)
     else:
         o_ref, s_ref = gdn_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0, **kw)
-    for portable in (False, True):
-        o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=reverse, portable=portable, **kw)
+    for fp32 in (False, True):
+        q, k, v, g, beta, s0 = to_device(inp, fp32=fp32)
+        o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=reverse, **kw)
         torch.cuda.synchronize()
         eo, es = rel_max_err(o.cpu().numpy(), o_ref), rel_max_err(st.cpu().numpy(), s_ref)
-        print(f"flags prob={beta_is_prob} pre={qk_pre} reverse={reverse} portable={portable}: "
+        print(f"flags prob={beta_is_prob} pre={qk_pre} reverse={reverse} fp32 inputs={fp32}: "
               f"o {eo:.3e} state {es:.3e}", flush=True)
         assert eo <= TOL_BF16 and es <= TOL_BF16
 

@@ -118,8 +118,9 @@ def test_clip_241f_fp8_sampled_heads():
     _check(o[:, :, heads], st[:, heads], o_ref, s_ref, "clip_241f_fp8 heads 0, 9, 19")
 
 
-def test_fp8_rejects_portable_kernels():
-    q = torch.zeros(1, 80, 2, 112, dtype=torch.float8_e4m3fn, device="cuda")
+def test_fp8_rejects_other_head_dims():
+    # fp8 inputs run on the MFMA kernels only, which take d_k = d_v = 112
+    q = torch.zeros(1, 80, 2, 64, dtype=torch.float8_e4m3fn, device="cuda")
     g = torch.zeros(1, 80, 2, device="cuda")
     with pytest.raises(gdn.GdnError):
-        gdn.gdn_fwd(q, q, q, g, g, portable=True)
+        gdn.gdn_fwd(q, q, q, g, g)

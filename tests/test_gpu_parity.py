@@ -23,9 +23,10 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _run(inp, *, portable=False, o_dtype=torch.float32, state=True):
-    q, k, v, g, beta, s0 = to_device(inp)
-    o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, "new" if state else None, o_dtype=o_dtype, portable=portable)
+def _run(inp, *, fp32=False, o_dtype=torch.float32, state=True):
+    """fp32: upload q, k, v as fp32 (the vector-ALU kernels) instead of bf16 (the MFMA kernels)."""
+    q, k, v, g, beta, s0 = to_device(inp, fp32=fp32)
+    o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, "new" if state else None, o_dtype=o_dtype)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), (st.cpu().numpy() if st is not None else None)
 
@@ -39,22 +40,21 @@ def _check(inp, o, st, o_ref, s_ref, tol, label):
     assert es <= tol, es
 
 
-@pytest.mark.parametrize("portable", [False, True])
-def test_tiny_fp32_config(portable):
+def test_tiny_fp32_config():
     w = WORKLOADS["tiny_fp32"]
     _say("case tiny_fp32", w)
     inp = make_inputs(w)
-    o, st = _run(inp, portable=portable)
+    o, st = _run(inp)
     o_ref, s_ref = oracle_for(inp)
     _check(inp, o, st, o_ref, s_ref, TOL_F32, "tiny_fp32")
 
 
-@pytest.mark.parametrize("portable", [False, True])
-def test_window_2f_config(portable):
+@pytest.mark.parametrize("fp32", [False, True])
+def test_window_2f_config(fp32):
     w = WORKLOADS["window_2f"]
-    _say("case window_2f portable=", portable)
+    _say("case window_2f fp32 inputs=", fp32)
     inp = make_inputs(w)
-    o, st = _run(inp, portable=portable)
+    o, st = _run(inp, fp32=fp32)
     o_ref, s_ref = oracle_for(inp)
     _check(inp, o, st, o_ref, s_ref, TOL_BF16, "window_2f")
 
@@ -65,10 +65,10 @@ def test_ragged_and_small(T, B, H):
     w = Workload("ragged", B, H, 1, 10**9, "bf16", 7 + T, state_std=0.05)
     inp = make_inputs(w, seq_len=T, frame_tokens=97)
     _say("case ragged", T, B, H)
-    for portable in (False, True):
-        o, st = _run(inp, portable=portable)
+    for fp32 in (False, True):
+        o, st = _run(inp, fp32=fp32)
         o_ref, s_ref = oracle_for(inp)
-        _check(inp, o, st, o_ref, s_ref, TOL_BF16, f"ragged T={T} portable={portable}")
+        _check(inp, o, st, o_ref, s_ref, TOL_BF16, f"ragged T={T} fp32 inputs={fp32}")
 
 
 def test_portable_general_head_dims_fp32():
@@ -139,17 +139,16 @@ def test_minute_cfg_sampled_heads():
     assert np.isfinite(o).all()
 
 
-def test_chunk_ranges_on_two_streams_equal_one_launch():
-    """B = 2 x 20 heads needs 280 state-pass workgroups, more than the 256 CUs:
-    the library then runs the state pass in chunk ranges, overlapped with the
-    intra kernel on a second stream, carrying the state through the workspace.
-    With batch 1 a copy of batch 0, batch 0 must equal the single-launch B = 1
-    result bit for bit (a ragged 5,063-token sequence with an initial state)."""
+def test_batch_copies_equal_single_batch():
+    """B = 2 x 20 heads: twice the state-pass workgroups of B = 1, so a
+    different split of the merged launches between state pass and intra-chunk
+    work.  With batch 1 a copy of batch 0, both must equal the B = 1 result
+    bit for bit (a ragged 5,063-token sequence with an initial state)."""
     w = WORKLOADS["clip_241f"]
     inp = make_inputs(w, seq_len=5063)
     inp.state0 = (0.02 * np.random.default_rng(7).standard_normal((1, 20, 112, 112))).astype(np.float32)
     q, k, v, g, beta, s0 = to_device(inp)
-    _say("case two streams: B=2 (chunk ranges) vs B=1, T=5063")
+    _say("case batch copies: B=2 vs B=1, T=5063")
     o1, st1 = gdn.gdn_fwd(q, k, v, g, beta, s0)
     cat = lambda t: torch.cat([t, t], 0).contiguous()  # noqa: E731
     o2, st2 = gdn.gdn_fwd(cat(q), cat(k), cat(v), cat(g), cat(beta), cat(s0))
@@ -158,7 +157,7 @@ def test_chunk_ranges_on_two_streams_equal_one_launch():
     assert torch.equal(st2[:1], st1) and torch.equal(st2[1:], st1)
     o_ref, s_ref = oracle_for(inp, heads=[0, 19], batches=[0])
     _check(inp, o1.cpu().numpy()[:, :, [0, 19]], st1.cpu().numpy()[:, [0, 19]], o_ref, s_ref, TOL_BF16,
-           "two streams, heads 0 and 19")
+           "batch copies, heads 0 and 19")
 
 
 def test_closed_forms_on_gpu():
@@ -167,8 +166,8 @@ def test_closed_forms_on_gpu():
     inp = make_inputs(w)
     # beta = 0 (logit -inf), zero state: nothing is written, o = 0 exactly
     inp.beta[:] = -np.inf
-    for portable in (False, True):
-        o, st = _run(inp, portable=portable)
+    for fp32 in (False, True):
+        o, st = _run(inp, fp32=fp32)
         assert not o.any() and not st.any()
     # alpha = 1, beta = 1, distinct standard-basis keys, every query = key 0: o_t = v_0 for all t
     T = 112
@@ -182,22 +181,22 @@ def test_closed_forms_on_gpu():
     inp2.beta[:] = np.inf
     from hybrid_linear_attention_gdn_amd.inputs import round_bf16_bits
     inp2.q_bits, inp2.k_bits = round_bf16_bits(inp2.q), round_bf16_bits(inp2.k)
-    for portable in (False, True):
-        o, st = _run(inp2, portable=portable)
+    for fp32 in (False, True):
+        o, st = _run(inp2, fp32=fp32)
         np.testing.assert_allclose(o[0, :, 0], np.repeat(inp2.v[0, :1, 0], T, 0), rtol=0, atol=1e-5)
         np.testing.assert_allclose(st[0, 0] @ inp2.k[0, :, 0].T, inp2.v[0, :, 0].T, rtol=0, atol=1e-5)
 
 
 def test_prep_scalars_match_definitions():
-    """Standalone prep kernel outputs (portable path, read from the workspace) against their
-    definitions in fp64; the MFMA path's fused copies are checked in test_gpu_kernels."""
+    """Standalone prep kernel outputs (fp32 path, read from the workspace) against their
+    definitions in fp64; the MFMA path's per-chunk scalars are checked in test_gpu_kernels."""
     w = WORKLOADS["window_2f"]
     inp = make_inputs(w, seq_len=250)
-    q, k, v, g, beta, _ = to_device(inp)
-    p = gdn.problem(1, 250, 20, 112, 112, torch.bfloat16, torch.float32, portable=True)
+    q, k, v, g, beta, _ = to_device(inp, fp32=True)
+    p = gdn.problem(1, 250, 20, 112, 112, torch.float32, torch.float32)
     lay = gdn.workspace_layout(p)
     ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
-    gdn.gdn_fwd(q, k, v, g, beta, workspace=ws, portable=True)
+    gdn.gdn_fwd(q, k, v, g, beta, workspace=ws)
     torch.cuda.synchronize()
     f = lambda off: ws[off:off + 4 * 20 * 250].view(torch.float32).view(1, 20, 250).cpu().numpy()  # noqa: E731
     bt, rq, rk, gc = f(lay.beta), f(lay.rq), f(lay.rk), f(lay.gcum)

@@ -10,13 +10,14 @@ from hybrid_linear_attention_gdn_amd import rocprof_summary as rs
 HDR = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size", "Kernel_Id",
        "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count",
        "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
-CHAIN = "void gdn::mfma::(anonymous namespace)::chain_kernel<false>(unsigned short const*, float const*, int)"
+CHAIN = ("void gdn::mfma::(anonymous namespace)::scan_kernel<false, false, false, false>"
+         "(gdn::mfma::(anonymous namespace)::ScanArgs)")
 NEG = ("void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)"
        "::{lambda()#2}, std::array<char*, 2ul> >(int, at::native::neg_kernel_cuda)")
 
 
 def test_short_name():
-    assert rs.short_name(CHAIN) == "chain_kernel<false>"
+    assert rs.short_name(CHAIN) == "scan_kernel<false, false, false, false>"
     assert rs.short_name("gdn::mfma::(anonymous namespace)::intra_kernel(unsigned short const*)") == "intra_kernel"
     assert rs.short_name(NEG).startswith("vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda")
 
@@ -36,22 +37,23 @@ def test_traffic_calibration(tmp_path):
     _counters(str(tmp_path / "w"), "WRITE_SIZE", [(CHAIN, 50.0), (CHAIN, 50.0), (NEG, 4096.0)])
     out_json, out_md = str(tmp_path / "t.json"), str(tmp_path / "t.md")
     rs.main(["traffic", "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"), "--copy-mib", "4",
-             "--kernel", "chain_kernel", "--stage", "state", "--workload", "w", "--fetch-command", "cf",
-             "--write-command", "cw", "--json", out_json, "--md", out_md])
+             "--kernel", "scan_kernel", "--stage", "scan", "--workload", "w", "--fetch-command", "cf",
+             "--write-command", "cw", "--json", out_json, "--md", out_md, "--launches-per-step", "3"])
     rec = json.load(open(out_json))
     assert rec["calibration"]["fetch_factor"] == 2.0 and rec["calibration"]["write_factor"] == 1.0
     assert rec["fetch_bytes_per_launch"] == 200 * 1024 * 2       # mean 200 KiB, doubled
     assert rec["write_bytes_per_launch"] == 50 * 1024
     assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
-    assert rec["source_hash"] == rs.kernel_source_hash("state", True)
+    assert rec["bytes_per_step"] == 3 * rec["bytes_per_launch"]
+    assert rec["source_hash"] == rs.kernel_source_hash("scan", True)
     assert "cf" in open(out_md).read()
 
 
 def test_source_hash_tracks_the_kernel_files():
-    a = rs.kernel_source_hash("state", True)
-    b = rs.kernel_source_hash("intra", True)
+    a = rs.kernel_source_hash("scan", True)
+    b = rs.kernel_source_hash("portable", False)
     assert a != b and len(a) == 16
-    assert rs.kernel_source_hash("state", True) == a
+    assert rs.kernel_source_hash("scan", True) == a
 
 
 def test_source_hash_ignores_comments_and_layout():
@@ -76,6 +78,6 @@ def test_counters_table(tmp_path, capsys):
     rs.main(["counters", str(d), "--command", "rocprofv3 --pmc MfmaUtil LdsBankConflict -- x"])
     out = capsys.readouterr().out
     assert "rocprofv3 --pmc MfmaUtil LdsBankConflict -- x" in out
-    assert "| `chain_kernel<false>` | 2 | 15 | 0.375 |" in out
+    assert "| `scan_kernel<false, false, false, false>` | 2 | 15 | 0.375 |" in out
     assert "neg_kernel" not in out
     assert "MfmaUtil:" in out and "LdsBankConflict:" in out
