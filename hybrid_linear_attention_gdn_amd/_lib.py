@@ -13,10 +13,12 @@ GDN_FLAG_BETA_IS_PROB, GDN_FLAG_QK_PRENORMALIZED, GDN_FLAG_REVERSE = 1, 2, 8
 
 # every symbol include/sanawm_gdn.h declares
 EXPORTED = ("gdn_chunk_len", "gdn_workspace_bytes", "gdn_fwd", "gdn_chunk_step", "gdn_workspace_layout",
+            "gdn_fwd_no_alloc",
             "gdn_bidir_workspace_bytes", "gdn_bidir_fwd",
             "gdn_in_proj", "gdn_out_proj", "gdn_layer_workspace_bytes", "gdn_layer_fwd",
             "gdn_status_string", "gdn_last_error", "gdn_version")
 GDN_LAYER_BIDIRECTIONAL = 16
+GDN_NO_ALLOC_SCRATCH_BYTES = 64 << 20
 # every symbol include/sanawm_attn.h declares
 EXPORTED_ATTN = ("attn_cache_bytes", "attn_block_fwd")
 
@@ -70,6 +72,8 @@ def load():
     for fn in (lib.gdn_fwd, lib.gdn_chunk_step):
         fn.restype = ctypes.c_int
         fn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_fwd_no_alloc.restype = ctypes.c_int
+    lib.gdn_fwd_no_alloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_bidir_workspace_bytes.restype = ctypes.c_int
     lib.gdn_bidir_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
     lib.gdn_bidir_fwd.restype = ctypes.c_int

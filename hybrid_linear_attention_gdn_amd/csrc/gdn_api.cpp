@@ -11,6 +11,7 @@
 #include <cstring>
 #include <algorithm>
 #include <limits>
+#include <mutex>
 #include <vector>
 
 #include "gdn_internal.h"
@@ -36,8 +37,10 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
   return true;
 }
 
-// Validates the problem descriptor and lays out the workspace.
-gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
+// Validates the problem descriptor and lays out the workspace.  `ws_limit`:
+// the most workspace the caller can offer (the MFMA path then shortens its
+// chunk ranges to fit; every other path needs its full size).
+gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl, size_t ws_limit = SIZE_MAX) {
   if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem descriptor is NULL");
   if (p->batch < 1 || p->num_heads < 1 || p->seq_len < 0 || p->head_dim_k < 1 || p->head_dim_v < 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "bad shape: batch=%d seq_len=%d heads=%d d_k=%d d_v=%d", p->batch,
@@ -88,6 +91,15 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
   const size_t chunks = units * size_t(P.N);
   if (P.mfma) {  // the MFMA path computes its per-token scalars inside the intra-chunk step
     P.range_cap = std::max(1, std::min(P.N, gdn::kRangeCap));
+    if (ws_limit != SIZE_MAX) {  // two record slots of range_cap chunks per unit, then the carried state
+      const size_t carry = align_up(units * size_t(P.dv) * P.dk * sizeof(float));
+      const size_t per_chunk = 2 * units * gdn::mfma_record_bytes();
+      const size_t fit = ws_limit > carry ? (ws_limit - carry) / per_chunk : 0;
+      if (fit < 1)
+        return fail(GDN_ERR_WORKSPACE, "B*H = %zu needs at least %zu bytes of workspace, more than the %zu "
+                    "available", units, carry + per_chunk, ws_limit);
+      P.range_cap = int(std::min<size_t>(size_t(P.range_cap), fit));
+    }
     P.off_rec = take(2 * size_t(P.range_cap) * units * gdn::mfma_record_bytes());
     P.off_carry = take(units * size_t(P.dv) * P.dk * sizeof(float));
   } else {
@@ -103,6 +115,9 @@ gdn_status_t make_plan(const gdn_problem_t *p, gdn::Plan *pl) {
     P.off_S0 = take(chunks * size_t(P.dv) * P.dk * sizeof(float));
   }
   P.total = P.T == 0 ? 0 : off;
+  if (P.total > ws_limit)
+    return fail(GDN_ERR_WORKSPACE, "the problem needs %zu bytes of workspace, more than the %zu available", P.total,
+                ws_limit);
   *pl = P;
   return GDN_OK;
 }
@@ -120,9 +135,9 @@ hipError_t enqueue(const gdn::Plan &P, const gdn::Args &a) {
 
 gdn_status_t run(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *state_in, float *state_out, void *o, void *workspace,
-                 size_t workspace_bytes, void *hip_stream, bool chunk_step) {
+                 size_t workspace_bytes, void *hip_stream, bool chunk_step, size_t ws_limit = SIZE_MAX) {
   gdn::Plan P;
-  gdn_status_t s = make_plan(p, &P);
+  gdn_status_t s = make_plan(p, &P, ws_limit);
   if (s != GDN_OK) return s;
   if (chunk_step) {
     if (P.flags & GDN_FLAG_REVERSE)
@@ -244,6 +259,46 @@ gdn_status_t run_bidir(const gdn_problem_t *p, const void *q, const void *k, con
   return GDN_OK;
 }
 
+// ---- the workspace of gdn_fwd_no_alloc ----
+// One fixed array per device in the library's code object, allocated when the
+// code object is loaded on that device and held until the process ends.  Its
+// device address comes from hipGetSymbolAddress, once per device: the name
+// `scratch` in host code is only a host-side stand-in.  Nothing in it needs to
+// start at zero (every kernel writes what it later reads), and calls that
+// overlap on one device race on it.
+static __device__ __align__(256) unsigned char scratch[GDN_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, which must be the device
+// of `hip_stream`.
+gdn_status_t scratch_address(void *hip_stream, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  if (hip_stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(hip_stream), &sdev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (int(sdev) != dev)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "the stream belongs to device %d, the current device is %d", int(sdev),
+                  dev);
+  }
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,6 +345,19 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
                             const float *beta, const float *state_in, float *state_out, void *o,
                             void *workspace, size_t workspace_bytes, void *hip_stream) {
   return run(p, q, k, v, g, beta, state_in, state_out, o, workspace, workspace_bytes, hip_stream, true);
+}
+
+gdn_status_t gdn_fwd_no_alloc(const gdn_problem_t *p, const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *state_in, float *state_out, void *o,
+                              void *hip_stream) {
+  constexpr size_t kBytes = GDN_NO_ALLOC_SCRATCH_BYTES;
+  gdn::Plan P;
+  gdn_status_t s = make_plan(p, &P, kBytes);  // size checks before any HIP call
+  if (s != GDN_OK) return s;
+  void *ws = nullptr;
+  s = scratch_address(hip_stream, &ws);
+  if (s != GDN_OK) return s;
+  return run(p, q, k, v, g, beta, state_in, state_out, o, ws, kBytes, hip_stream, false, kBytes);
 }
 
 // ---- the layer around the scan ----

@@ -71,7 +71,7 @@ def _ptr(t):
 
 
 def _call(entry, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob, qk_prenormalized,
-          workspace, stream, reverse=False, bidir=False):
+          workspace, stream, reverse=False, bidir=False, no_alloc=False):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, d_k]")
     B, T, H, dk = q.shape
@@ -97,15 +97,18 @@ def _call(entry, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob
         raise ValueError("o must be a contiguous float32/bfloat16 tensor of shape [B, T, H, d_v]")
     p = problem(B, T, H, dk, dv, q.dtype, o.dtype, beta_is_prob=beta_is_prob,
                 qk_prenormalized=qk_prenormalized, reverse=reverse)
-    need = bidir_workspace_bytes(p) if bidir else workspace_bytes(p)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     states = () if bidir else (_ptr(state_in), _ptr(state_out))
+    if no_alloc:  # the library's own fixed workspace
+        ws_args = ()
+    else:
+        need = bidir_workspace_bytes(p) if bidir else workspace_bytes(p)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_args = (_ptr(workspace), ctypes.c_size_t(workspace.numel()))
     status = entry(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), *states,
-                   _ptr(o), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                   ctypes.c_void_p(stream.cuda_stream))
+                   _ptr(o), *ws_args, ctypes.c_void_p(stream.cuda_stream))
     _check(status)
     return o, state_out
 
@@ -121,6 +124,14 @@ def gdn_fwd(q, k, v, g, beta, state_in=None, state_out="new", o=None, *, o_dtype
         state_out = torch.empty((B, H, v.shape[-1], dk), dtype=torch.float32, device=q.device)
     return _call(L.load().gdn_fwd, q, k, v, g, beta, state_in, state_out, o, o_dtype, beta_is_prob,
                  qk_prenormalized, workspace, stream, reverse=reverse)
+
+
+def gdn_fwd_no_alloc(q, k, v, g, beta, state_in, state_out, o, *, beta_is_prob=False, qk_prenormalized=False,
+                     reverse=False, stream=None):
+    """gdn_fwd on the library's fixed per-device workspace (gdn_fwd_no_alloc):
+    o and state_out (or None) are caller tensors; nothing is allocated."""
+    return _call(L.load().gdn_fwd_no_alloc, q, k, v, g, beta, state_in, state_out, o, o.dtype, beta_is_prob,
+                 qk_prenormalized, None, stream, reverse=reverse, no_alloc=True)
 
 
 def gdn_bidir_fwd(q, k, v, g, beta, o=None, *, o_dtype=torch.float32, beta_is_prob=False,

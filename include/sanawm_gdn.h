@@ -139,6 +139,26 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
                             void *hip_stream);
 
 /*
+ * gdn_fwd_no_alloc: gdn_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same problem, arguments, flags and results as gdn_fwd (the
+ * outputs equal gdn_fwd's bit for bit), but no workspace argument: the
+ * workspace is a fixed array of GDN_NO_ALLOC_SCRATCH_BYTES inside the library,
+ * one per device, allocated when the library's code is loaded on that device
+ * and held until the process ends.  The call allocates and frees nothing.
+ * Limit: on the bf16/fp8 kernels the chunk ranges shrink to fit (B*H up to
+ * 383 at 64 MiB); the fp32 kernels need their whole gdn_workspace_bytes.  A
+ * problem that does not fit returns GDN_ERR_WORKSPACE before any HIP call.
+ * The current device must be the stream's device (else
+ * GDN_ERR_INVALID_ARGUMENT).  Calls that overlap on one device (two streams,
+ * two threads) share the array and race: serialise them.
+ */
+#define GDN_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status_t gdn_fwd_no_alloc(const gdn_problem_t *p, const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, const float *state_in,
+                              float *state_out, void *o, void *hip_stream);
+
+/*
  * The reverse scan (GDN_FLAG_REVERSE, gdn_fwd only).  The same recurrence run
  * over the tokens from last to first: S'_t = alpha'_t S'_{t+1} (I - beta_t k_t
  * k_t^T) + beta_t v_t k_t^T, o_t = S'_t q_t, where alpha'_t = exp(g[t + 1])
