@@ -11,6 +11,8 @@
 //   P_ri = rq_r rk_i e^{G_r - G_i} (q_r . k_i)          (i <= r)
 //   T    = (I + A)^{-1}
 //   M    = K^T diag(s) T,  s_i = rk_i e^{G_n - G_i};     P' = P T
+//   P''  = P' diag(beta),  Q' = Q~ + P' K~  (K~ = -diag(beta gamma rk) K,
+//                                             Q~ = diag(gamma rq) Q)
 // (the algebra behind these is written out in gdn_mfma_common.h).
 //
 // Steps:
@@ -25,8 +27,14 @@
 //  4. M^T = T^T diag(s) K and P'^T = T^T P^T on the matrix cores (bf16 hi/lo
 //     operands, fp32 accumulation), each wave owning whole token-row tiles;
 //     the accumulators are exactly the A-operand fragments the state pass
-//     reads.  They are rounded once to fp16 (round to nearest even) and stored.
-// T and P live in LDS as 16 x 16 fp32 blocks with 16-byte aligned rows, so
+//     reads.  M is rounded once to fp16 (round to nearest even) and stored;
+//     P'' = P' diag(beta) is stored as a bf16 hi/lo pair, and P' itself
+//     (fp32) goes to LDS for step 5.
+//  5. Q'^T = Q~^T + K^T (P' diag(w))^T, w = -beta gamma rk, on the matrix cores
+//     (exact bf16 K^T against hi/lo P' diag(w)), accumulating onto Q~^T; the
+//     accumulators are again the state pass's A-operand fragments of Q', rounded
+//     to fp16 and stored.
+// T, P and P' live in LDS as 16 x 16 fp32 blocks with 16-byte aligned rows, so
 // every operand fragment is one 128-bit LDS read.
 #pragma once
 #include "gdn_mfma_common.h"
@@ -45,8 +53,9 @@ constexpr int kLdsQr = kLdsKt;
 constexpr int kLdsP = kLdsKt + 112 * kKtRow * 2;      // +18,816
 constexpr int kLdsAd = kLdsP + 15 * kBlkF * 4;        // +19,200: diagonal blocks of A
 constexpr int kLdsD = kLdsAd + 5 * kBlkF * 4;         // +6,400: diagonal blocks of T, row-major
-constexpr int kLdsSc = kLdsD + 5 * kBlkF * 4;         // +6,400
-constexpr int kLdsIntra = kLdsSc + 8 * 80 * 4;        // +2,560 = 72,576: two workgroups per CU
+constexpr int kLdsPp = kLdsAd;                        // step 4 on: 15 blocks of P', over the dead A and D blocks
+constexpr int kLdsSc = kLdsPp + 15 * kBlkF * 4;       // +19,200
+constexpr int kLdsIntra = kLdsSc + 8 * 80 * 4;        // +2,560 = 78,976: two workgroups per CU
 static_assert(80 * kKrRow * 2 <= kLdsKt, "K rows fit under the T blocks");
 static_assert(2 * 80 * 14 * 4 <= 15 * kBlkF * 4, "norm partial sums fit in the P region");
 
@@ -83,7 +92,7 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
                                             const float *__restrict__ g, const float *__restrict__ beta,
                                             char *__restrict__ rec, int T, int H, int b, int h, int c,
                                             uint32_t flags, int tid, bool valid) {
-  char *Mrec = rec + kRecM, *Prec = rec + kRecP;
+  char *Mrec = rec + kRecM, *Prec = rec + kRecP, *Plrec = rec + kRecPl;
   float *cs = reinterpret_cast<float *>(rec + kRecCs);
   uint16_t *Kr = reinterpret_cast<uint16_t *>(lds + kLdsKr);
   uint16_t *Kt = reinterpret_cast<uint16_t *>(lds + kLdsKt);
@@ -91,8 +100,9 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
   float *Pb = reinterpret_cast<float *>(lds + kLdsP);   // block (R, K), R >= K: [rr][kk] = P[16R+rr][16K+kk]
   float *Ad = reinterpret_cast<float *>(lds + kLdsAd);  // block I: [ii][kk] = A[16I+ii][16I+kk]
   float *Dm = reinterpret_cast<float *>(lds + kLdsD);   // block I: [ii][jj] = T[16I+ii][16I+jj]
+  float *Pp = reinterpret_cast<float *>(lds + kLdsPp);  // block (R, I), R >= I: [rr][ii] = P'[16R+rr][16I+ii]
   float *sc = reinterpret_cast<float *>(lds + kLdsSc);
-  float *sbeta = sc, *srq = sc + 80, *srk = sc + 160, *sG = sc + 240, *ss = sc + 320;
+  float *sbeta = sc, *srq = sc + 80, *srk = sc + 160, *sG = sc + 240, *ss = sc + 320, *sw = sc + 400;
   auto blk = [](float *base, int I, int J) { return base + tri(I, J) * kBlkF; };
 
   const int t0 = c * C;
@@ -184,41 +194,34 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
       const float bt = (flags & kBetaIsProb) ? bl[t] : __builtin_amdgcn_rcpf(1.f + fexp(-bl[t]));
       const float G = wave == 0 ? G0 : G0_last + G1;
       const float bo = ok ? bt : 0.f, rko = ok ? rk : 0.f, rqo = ok ? rq : 0.f;
-      const float gam = fexp(G);
       sbeta[t] = bo;
       srq[t] = rqo;
       srk[t] = rko;
       sG[t] = G;
       ss[t] = rko * fexp(Gl - G);
-      if (valid) {
-        cs[t] = bo;
-        cs[80 + t] = bo * gam;
-        cs[160 + t] = ok ? gam : 0.f;
-      }
+      sw[t] = -(bo * fexp(G)) * rko;  // K~ = diag(w) K
+      if (valid) cs[t] = bo;
     }
-    if (valid && wave == 0 && lane == 0) cs[240] = fexp(Gl);
+    if (valid && wave == 0 && lane == 0) cs[kCsGammaN] = fexp(Gl);
   }
   __syncthreads();
 
-  // ---- (1b) the state pass's row operands, rounded to fp16, as fragment
-  // images: K~ = -diag(b) K^ and Q~ = diag(c) Q^, where K^ = diag(rk) K and
-  // Q^ = diag(rq) Q are the normalised rows and b = beta gamma, c = gamma the
-  // per-token scales (so that R = diag(a) V + K~ S^T and O = Q~ S^T + P' R come
-  // straight out of the matrix products).  Per token tile t, blocks kb = 0..2
-  // hold d_k 32 kb + 8 g .. + 7 of row 16 t + (lane & 15) (g = lane >> 4) for
-  // all 64 lanes.  Within a
+  // ---- (1b) the state pass's key operand, rounded to fp16, as a fragment
+  // image: K~ = -diag(beta gamma) K^, where K^ = diag(rk) K are the normalised
+  // rows (so that R = diag(beta) V + K~ S^T comes straight out of the matrix
+  // product).  Per token tile t, blocks kb = 0..2 hold d_k 32 kb + 8 g .. + 7
+  // of row 16 t + (lane & 15) (g = lane >> 4) for all 64 lanes.  Within a
   // block the lane's eight d_k are in the "pair" order of the state's
   // accumulator tiles: d_k 32 kb + 4 g .. + 3, then 32 kb + 16 + 4 g .. + 3; block
   // 3 stores only d_k 96 + 4 g .. + 3 (8 bytes per lane).
   if (valid) {
     constexpr int kPerTile = 4 * 64;
-    for (int idx = tid; idx < 2 * CT * kPerTile; idx += 256) {
-      const int m = idx / (CT * kPerTile), w = idx % (CT * kPerTile), t = w / kPerTile, x = w % kPerTile;
+    for (int idx = tid; idx < CT * kPerTile; idx += 256) {
+      const int t = idx / kPerTile, x = idx % kPerTile;
       const int kb = x / 64, l = x % 64, lg4 = l >> 4;
       const int row = 16 * t + (l & 15);
-      const uint16_t *src = (m ? Qr : Kr) + row * kKrRow + 32 * kb + 4 * lg4;
-      const float gam = fexp(sG[row]);
-      const float sc = m ? gam * srq[row] : -(sbeta[row] * gam) * srk[row];
+      const uint16_t *src = Kr + row * kKrRow + 32 * kb + 4 * lg4;
+      const float sc = sw[row];
       // d_k 32 kb + 4 g .. + 3 and, below d_k 112, 32 kb + 16 + 4 g .. + 3
       const uint2 lo = *reinterpret_cast<const uint2 *>(src);
       const uint2 hi = kb < 3 ? *reinterpret_cast<const uint2 *>(src + 16) : make_uint2(0u, 0u);
@@ -227,7 +230,7 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2)
         pk[i2] = pack_f16x2(sc * __uint_as_float(wd[i2] << 16), sc * __uint_as_float(wd[i2] & 0xffff0000u));
-      char *dst = rec + (m ? kRecQ : kRecK) + kq_off(t, kb);
+      char *dst = rec + kRecK + kq_off(t, kb);
       if (kb < 3)
         *reinterpret_cast<uint4 *>(dst + 16 * l) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       else
@@ -506,14 +509,18 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
           }
         }
       }
-      // accumulator: column r = 16Rt + ln, rows i = 16It + 4lg + e -> P'[r][i], the state pass's A-operand order
+      // accumulator: column r = 16Rt + ln, rows i = 16It + 4lg + e -> P'[r][i], the state pass's
+      // A-operand order.  P'' = P' diag(beta) goes out as a bf16 hi/lo pair, P' to LDS.
       if (valid) {
-        const uint2 w = pack_f16x4(acc);
-        if (It == Rt && !(Rt & 1))
-          *reinterpret_cast<uint2 *>(Prec + p_off16(Rt) + lane * 8) = w;
-        else
-          *reinterpret_cast<uint2 *>(Prec + p_off32(Rt, It >> 1) + lane * 16 + (It & 1) * 8) = w;
+        const f32x4 b4 = ld4(sbeta + 16 * It + 4 * lg);
+        const float v[4] = {acc[0] * b4[0], acc[1] * b4[1], acc[2] * b4[2], acc[3] * b4[3]};
+        uint32_t hi[2], lo[2];
+        split4(v, hi, lo);
+        const int off = (It == Rt && !(Rt & 1)) ? p_off16(Rt) + lane * 8 : p_off32(Rt, It >> 1) + lane * 16 + (It & 1) * 8;
+        *reinterpret_cast<uint2 *>(Prec + off) = make_uint2(hi[0], hi[1]);
+        *reinterpret_cast<uint2 *>(Plrec + off) = make_uint2(lo[0], lo[1]);
       }
+      *reinterpret_cast<float4 *>(blk(Pp, Rt, It) + ln * kBs + 4 * lg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   };
   switch (wave) {
@@ -521,6 +528,79 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
     case 1: m_rows(1); p_rows(2); p_rows(3); break;
     case 2: m_rows(2); p_rows(1); break;
     default: m_rows(3); m_rows(4); p_rows(0); break;
+  }
+  __syncthreads();  // P' complete in LDS
+
+  // ---- (5) Q'^T = Q~^T + K^T (P' diag(w))^T, w = -beta gamma rk: A rows d = 16Dt + ln from
+  // K^T (exact bf16), B columns r = 16Rt + ln over tokens i <= r from P' diag(w) (bf16 hi/lo),
+  // accumulating onto Q~^T[d][r] = gamma_r rq_r q_r[d].  The accumulator of (Dt, Rt) holds
+  // Q'[r][16Dt + 4lg + e] for column r: the state pass's A-operand fragment of Q' (pair order
+  // over d_k, like K~).  Wave w takes the d_k tiles w and w + 4.
+  {
+    F16 bh[CT][CT], bl[CT][CT];  // [Rt][p], p <= Rt: tokens 16p + 4lg .. + 3 of column r = 16Rt + ln
+#pragma unroll
+    for (int Rt = 0; Rt < CT; ++Rt)
+#pragma unroll
+      for (int p = 0; p <= Rt; ++p) {
+        const f32x4 x = ld4(blk(Pp, Rt, p) + ln * kBs + 4 * lg), w4 = ld4(sw + 16 * p + 4 * lg);
+        const float v[4] = {x[0] * w4[0], x[1] * w4[1], x[2] * w4[2], x[3] * w4[3]};
+        uint32_t hi[2], lo[2];
+        split4(v, hi, lo);
+        bh[Rt][p] = f16_of(hi);
+        bl[Rt][p] = f16_of(lo);
+      }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int Dt = wave + 4 * pass;
+      if (Dt < NT) {
+        // Q~^T of the five tiles: q_r[16Dt + 4lg .. + 3] (L2-resident: step 1 read these rows)
+        f32x4 acc[CT];
+#pragma unroll
+        for (int Rt = 0; Rt < CT; ++Rt) {
+          const int r = 16 * Rt + ln;
+          const float f = fexp(sG[r]) * srq[r];  // 0 past the chunk's end
+          float x[4] = {0.f, 0.f, 0.f, 0.f};
+          if (r < n) {
+            const char *src = qbase + (size_t(phys_token(t0 + r, T, rev)) * rowstride + 16 * Dt + 4 * lg) * kElem;
+            if constexpr (kFp8) {
+              const uint32_t w = *reinterpret_cast<const uint32_t *>(src);
+              const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+              x[0] = lo2[0], x[1] = lo2[1], x[2] = hi2[0], x[3] = hi2[1];
+            } else {
+              const uint2 w = *reinterpret_cast<const uint2 *>(src);
+              x[0] = __uint_as_float(w.x << 16), x[1] = __uint_as_float(w.x & 0xffff0000u);
+              x[2] = __uint_as_float(w.y << 16), x[3] = __uint_as_float(w.y & 0xffff0000u);
+            }
+          }
+          acc[Rt] = f32x4{f * x[0], f * x[1], f * x[2], f * x[3]};
+        }
+        const uint16_t *kt = Kt + (16 * Dt + ln) * kKtRow + 4 * lg;
+#pragma unroll
+        for (int Rt = 0; Rt < CT; ++Rt) {
+#pragma unroll
+          for (int p = 0; p <= Rt; p += 2) {
+            if (p + 1 <= Rt) {  // 32-deep block over token tiles p, p + 1
+              const uint2 k0 = *reinterpret_cast<const uint2 *>(kt + 16 * p), k1 = *reinterpret_cast<const uint2 *>(kt + 16 * p + 16);
+              const F32 ak{{k0.x, k0.y, k1.x, k1.y}};
+              acc[Rt] = mma(ak, pair(bh[Rt][p], bh[Rt][p + 1]), acc[Rt]);
+              acc[Rt] = mma(ak, pair(bl[Rt][p], bl[Rt][p + 1]), acc[Rt]);
+            } else {  // 16-deep block over tile p
+              const uint2 k0 = *reinterpret_cast<const uint2 *>(kt + 16 * p);
+              const F16 ak{{k0.x, k0.y}};
+              acc[Rt] = mma(ak, bh[Rt][p], acc[Rt]);
+              acc[Rt] = mma(ak, bl[Rt][p], acc[Rt]);
+            }
+          }
+          if (valid) {
+            const uint2 w = pack_f16x4(acc[Rt]);
+            if (Dt < 6)
+              *reinterpret_cast<uint2 *>(rec + kRecQ + kq_off(Rt, Dt >> 1) + lane * 16 + (Dt & 1) * 8) = w;
+            else
+              *reinterpret_cast<uint2 *>(rec + kRecQ + kq_off(Rt, 3) + lane * 8) = w;
+          }
+        }
+      }
+    }
   }
 }
 

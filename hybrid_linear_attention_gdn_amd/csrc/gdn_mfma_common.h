@@ -12,34 +12,38 @@
 //            P_ri = rq_r rk_i e^{G_r - G_i} (q_r . k_i)   (i <= r)
 //   S^T   <- gamma_n S^T + M R                        M  = K^T diag(s) T,
 //            s_i = rk_i e^{G_n - G_i}
-// The state pass takes the normalised rows K^ = diag(rk) K, Q^ = diag(rq) Q
-// with its scales folded in: K~ = -diag(beta gamma) K^ and Q~ = diag(gamma) Q^,
-// so that R = diag(beta) V + K~ S^T and O = Q~ S^T + P' R.
 // (derivation: the chunked WY form U = T R, O = diag(gamma) Q^ S^T + P U,
 // S_next = gamma_n S + U^T diag(e^{G_n - G}) K^, with the scales folded in).
+// The state pass takes the normalised rows K^ = diag(rk) K, Q^ = diag(rq) Q
+// with their scales folded in, K~ = -diag(beta gamma) K^ and Q~ = diag(gamma) Q^,
+// so that R = diag(beta) V + K~ S^T.  Substituting R into O gives the form
+// the output uses, in which R does not appear:
+//   O = Q' S^T + P'' V,      Q' = Q~ + P' K~,      P'' = P' diag(beta).
 //
 // The intra-chunk step (gdn_intra.h, one group of four waves per (b, h,
 // chunk), fully parallel) forms A and P from K K^T and K Q^T on the matrix
-// cores, solves T in LDS (fp32), and then M and P' on the matrix cores.  It
-// stores M and P' as fp16 in the exact register order the state pass
-// consumes, and the per-token scales.  The state pass (gdn_scan.hip, one
-// workgroup per (b, h, pair of 16-column tiles of d_v), sequential over
-// chunks) keeps its 112 x 16 slices of the fp32 state in registers and runs
-// the four products above per chunk.
+// cores, solves T in LDS (fp32), then M, P', P'' and Q' on the matrix cores.
+// It stores them in the exact register order the state pass consumes, with
+// the per-token scales.  The state pass (gdn_scan.hip, one workgroup per
+// (b, h, pair of 16-column tiles of d_v), sequential over chunks) keeps its
+// 112 x 16 slices of the fp32 state in registers and runs R = diag(beta) V +
+// K~ S^T and the update per chunk, and the output O = Q' S^T + P'' V.
 //
 // Precision.  The intra-chunk step works from the exact bf16 rows: K K^T and
 // K Q^T on bf16 matrix instructions, T by fp32 substitution and bf16 hi/lo
 // block products (x = hi + lo, hi = bf16(x), lo = bf16(x - hi): about 16
-// bits), M and P' from hi/lo operands, all accumulating in fp32.  The state
-// pass then takes every operand as fp16 (11 significant bits, round to
-// nearest even): the normalised rows K~, Q~ (|x| <= 1), M and P' from the
-// intra step, and S and R from its own fp32 registers.  S and R are scaled by
-// a power of two per 112 x 16 / 80 x 16 tile whenever the tile's largest
-// magnitude leaves [2^-6, 2^15), which keeps fp16's range out of the way;
-// the scale is undone exactly on the fp32 results.  Every product accumulates
-// in fp32 and the state stays fp32.  An fp64 emulation of exactly these
-// roundings gives 2.5e-3 to 3.1e-3 of rms(o) on the 241-frame and minute-scale
-// clips, against 2e-2 if the same operands were plain bf16.
+// bits), M, P' and P' K~ from hi/lo operands, all accumulating in fp32.  The
+// state pass then takes K~, Q', M and its own S and R as fp16 (11 significant
+// bits, round to nearest even; |K~| <= 1) and P'' as a bf16 hi/lo pair against
+// the exact bf16 rows of V.  S and R are scaled by a power of two per 112 x 16
+// / 80 x 16 tile whenever the tile's largest magnitude leaves [2^-6, 2^15),
+// which keeps fp16's range out of the way; the scale is undone exactly on the
+// fp32 results.  Every product accumulates in fp32 and the state stays fp32.
+// The intra-chunk term P'' V, which dominates o when the gates decay within a
+// chunk, so carries no fp16 rounding of its own; an fp64 emulation of exactly
+// these roundings gives 2.2e-3 to 2.5e-3 of rms(o) on the 241-frame clip and
+// 0.7e-3 to 1.3e-3 with a gate on every token (against 7e-3 to 9e-3 if R
+// entered the output as fp16).
 //
 // MFMA lane layouts (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16, lane l,
 // g = l >> 4): A row l & 15 and B column l & 15 hold k = 8g..8g+7 (4g..4g+3
@@ -62,17 +66,18 @@ constexpr int C = kChunk;    // 80
 constexpr int NT = D / 16;   // 7 column tiles of d_v (and row tiles of d_k)
 constexpr int CT = C / 16;   // 5 token tiles per chunk
 
-// One chunk-head record of fp16 fragment images (the state pass's operands)
-// and fp32 scales, in the order the state pass copies it: part A (K~, Q~, P',
-// scales: read before its mid-chunk barrier) then part B (M: read after it).
-// The scales are a = beta, b = beta gamma, c = gamma (per token) and gamma_n.
-constexpr int kKQBytes = CT * 3584;  // K~ or Q~: per token tile 3 K32 blocks of 1 KB + 1 of 512 B
-constexpr int kPBytes = 7680;        // lower-triangular token blocks of P'
-constexpr int kCsFloats = 256;       // a[80], b[80], c[80], gamma_n, pad
+// One chunk-head record: the state pass's operands as fragment images (K~,
+// Q', M in fp16; P'' as bf16 hi and lo) and fp32 scales a = beta (per token)
+// and gamma_n.
+constexpr int kKQBytes = CT * 3584;  // K~ or Q': per token tile 3 K32 blocks of 1 KB + 1 of 512 B
+constexpr int kPBytes = 7680;        // lower-triangular token blocks of P'' (hi or lo)
+constexpr int kCsFloats = 128;       // a[80], gamma_n, pad
 constexpr int kMBytes = NT * 2560;   // 7 d_k tiles x (2 K32 blocks of 1 KB + 1 K16 block of 512 B)
-constexpr int kRecK = 0, kRecQ = kKQBytes, kRecP = 2 * kKQBytes, kRecCs = kRecP + kPBytes;
-constexpr int kRecM = kRecCs + kCsFloats * 4;     // 44,544: the end of part A
-constexpr int kRecBytes = kRecM + kMBytes;        // 62,464
+constexpr int kRecK = 0, kRecQ = kKQBytes, kRecP = 2 * kKQBytes, kRecPl = kRecP + kPBytes;
+constexpr int kRecCs = kRecPl + kPBytes;
+constexpr int kRecM = kRecCs + kCsFloats * 4;  // 51,712
+constexpr int kRecBytes = kRecM + kMBytes;     // 69,632
+constexpr int kCsGammaN = 80;                  // index of gamma_n among the scales
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
@@ -164,7 +169,7 @@ __device__ __forceinline__ uint4 elems8_bf16(const Elems8<kFp8> &x) {
 
 // ---------------------------------------------------------------------------
 // Byte offsets of the fragment-ordered fp16 operands inside their record parts.
-// K~, Q~: token tile t, block kb (d_k 32kb .. 32kb + 31 in the "pair" order of
+// K~, Q': token tile t, block kb (d_k 32kb .. 32kb + 31 in the "pair" order of
 //    the state's accumulator tiles, 16 B per lane; block 3 holds only its slots
 //    0..3, d_k 96 + 4g .. + 3, 8 B per lane: d_k 112.. do not exist).
 __device__ __forceinline__ constexpr int kq_off(int t, int kb) { return t * 3584 + kb * 1024; }
@@ -172,7 +177,7 @@ __device__ __forceinline__ constexpr int kq_off(int t, int kb) { return t * 3584
 //    lane) and the 16-deep block of tokens 64..79 (8 B per lane).
 __device__ __forceinline__ constexpr int m_off32(int mt, int kb) { return mt * 2560 + kb * 1024; }
 __device__ __forceinline__ constexpr int m_off16(int mt) { return mt * 2560 + 2048; }
-// P': row tile R (tokens 16R..) uses 32-deep blocks over token tiles (0,1),
+// P'' (hi and lo alike): row tile R (tokens 16R..) uses 32-deep blocks over token tiles (0,1),
 // (2,3) below its diagonal and, for even R, the 16-deep block of tile R.
 __device__ __forceinline__ constexpr int p_base(int R) {
   return R == 0 ? 0 : R == 1 ? 512 : R == 2 ? 1536 : R == 3 ? 3072 : 5120;

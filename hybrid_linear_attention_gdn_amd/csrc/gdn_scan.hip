@@ -14,31 +14,31 @@
 // the next in the workspace.
 //
 // State pass, per chunk (the algebra is in gdn_mfma_common.h), with the
-// scaled normalised rows K~, Q~ of the chunk's record:
-//   R = diag(a) V + K~ S^T,   O = Q~ S^T + P' R,   S^T <- gamma_n S^T + M R.
-// Each product accumulates onto the term before it (a V, gamma_n S^T, Q~ S^T).
+// chunk's record (K~, Q', P'', M, a = beta, gamma_n):
+//   R = diag(a) V + K~ S^T,   S^T <- gamma_n S^T + M R,   O = Q' S^T + P'' V.
+// Each product accumulates onto the term before it (a V, gamma_n S^T, Q' S^T).
+// The output needs S of the chunk's start and the chunk's own rows only, not R.
 // One workgroup per (b, h, pair of 16-column tiles of d_v): 4 workgroups per
 // head (tiles 0-1, 2-3, 4-5, 6).  Eight waves:
 //   0, 2  "state" wave of local tile 0, 1: holds the tile's 112 x 16 fp32 slice
 //         of S^T in registers (7 accumulator tiles of 16 x 16), computes R and
-//         the update M R; publishes S and R as fp16 operand images in LDS for
-//         the output wave.
-//   1, 3  "output" wave of local tile 0, 1: Q~ S^T + P' R, the output rows.
+//         the update M R; publishes S as an fp16 operand image in LDS for the
+//         output wave.
+//   1, 3  "output" wave of local tile 0, 1: Q' S^T + P'' V, the output rows.
 //   4-7   copy waves: buffer-to-LDS loads (16 bytes per lane, no register
 //         round trip) of the chunk's record and of this workgroup's V columns.
 // Two barriers per chunk: X opens chunk c (its record and V rows landed; S
-// of chunk c published), Y follows R's publication.
+// of chunk c published); by Y every wave has read what it needs of chunk c's
+// buffer and of the S image into registers.
 //
-// Buffers: records and V rows are double-buffered.  Every read of chunk c's
-// buffer happens before barrier Y(c) (M is read into registers while the
-// first products run), so chunk c + 2's record and rows are copied from Y(c)
-// on.
+// Buffers: records and V rows are double-buffered, so chunk c + 2's record
+// and rows are copied from Y(c) on; the S image is rewritten after Y(c).
 //
 // Operand orders.  All products use the "pair" k-order, in which two 16-row
 // accumulator tiles (rows 4g .. 4g + 3 of each in lane group g) already are
 // one 32-deep operand: S and R go from the accumulators to the next product
-// without moving between lanes, and the record stores K~, Q~, M and P' in that
-// order.
+// without moving between lanes, and the record stores K~, Q', M and P'' in
+// that order.
 #include <algorithm>
 #include <vector>
 
@@ -51,7 +51,7 @@ namespace {
 constexpr int kTPW = 2;                          // 16-column tiles of d_v per state-pass workgroup
 constexpr int kGroups = (NT + kTPW - 1) / kTPW;  // workgroups per (b, h)
 constexpr int kThreads = 512;
-constexpr int kRecInstr = kRecBytes / 1024;  // 1 KB copies of one record (61)
+constexpr int kRecInstr = kRecBytes / 1024;  // 1 KB copies of one record (68)
 static_assert(kRecBytes % 1024 == 0, "whole 1 KB record copies");
 constexpr int kCopyWaves = 4;
 
@@ -64,13 +64,11 @@ struct Buf {
   static constexpr int kVInstr = (kVSlots + 63) / 64;
   static constexpr int kRec = 0;                  // the record (parts A and B)
   static constexpr int kV = kRecBytes;
-  static constexpr int kBytes = kV + C * kVRow;   // 67,584 / 65,024
-  // after the two buffers: per local tile the S images (4 x 1 KB) and the R
-  // images (2 x 1 KB + 512 B), their scale exponents and the landing area of
-  // the copy waves' L2 touches
+  static constexpr int kBytes = kV + C * kVRow;   // 74,752 / 72,192
+  // after the two buffers: per local tile the S image (4 x 1 KB) and its scale
+  // exponent, and the landing area of the copy waves' L2 touches
   static constexpr int kSImg = 2 * kBytes;
-  static constexpr int kRImg = kSImg + kTPW * 4096;
-  static constexpr int kExp = kRImg + kTPW * 2560;  // per tile: S exponent, R exponent
+  static constexpr int kExp = kSImg + kTPW * 4096;  // per tile: S exponent
   static constexpr int kTouch = kExp + 32;  // landing area of the L2 touches (never read)
   static constexpr int kLds = kTouch + 256;
   static_assert(kV % 16 == 0 && kBytes % 16 == 0 && kRecBytes % 16 == 0, "16-byte aligned copy targets");
@@ -174,8 +172,7 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const size_t u = size_t(b) * a.H + h;
   char *Simg = lds + G::kSImg + jl * 4096;
-  char *Rimg = lds + G::kRImg + jl * 2560;
-  int *exps = reinterpret_cast<int *>(lds + G::kExp) + 2 * jl;
+  int *exps = reinterpret_cast<int *>(lds + G::kExp) + jl;
 
   // S^T tile i: accumulator rows d_k = 16 i + 4 lg + e, column d_v = 16 j + ln
   f32x4 St[NT];
@@ -255,7 +252,7 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
     }
     // the update accumulates onto gamma_n S^T in place (gamma_n is 1 on every
     // chunk without a frame's first token)
-    const float gamma_n = cs[240];
+    const float gamma_n = cs[kCsGammaN];
     GDN_RARELY(gamma_n != 1.f) {
 #pragma unroll
       for (int i = 0; i < NT; ++i) St[i] = St[i] * gamma_n;
@@ -292,11 +289,7 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
     const F32 Rb0 = f32_of(rw[0].x, rw[0].y, rw[1].x, rw[1].y);
     const F32 Rb1 = f32_of(rw[2].x, rw[2].y, rw[3].x, rw[3].y);
     const F32 Rb2 = f32_of(rw[4].x, rw[4].y, 0u, 0u);
-    *reinterpret_cast<uint4 *>(Rimg + lane * 16) = make_uint4(Rb0.w[0], Rb0.w[1], Rb0.w[2], Rb0.w[3]);
-    *reinterpret_cast<uint4 *>(Rimg + 1024 + lane * 16) = make_uint4(Rb1.w[0], Rb1.w[1], Rb1.w[2], Rb1.w[3]);
-    *reinterpret_cast<uint2 *>(Rimg + 2048 + lane * 8) = rw[4];
-    if (lane == 0) exps[1] = sR;
-    compute_barrier();  // Y(c): R published; chunk c's record and V are no longer read
+    compute_barrier();  // Y(c): chunk c's record and V are no longer read
     // ---- S^T <- gamma_n S^T + 2^sR M R': seven chains of three products
     GDN_RARELY(sR) {
       f32x4 U[NT];
@@ -328,14 +321,13 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
 }
 
 // ---------------------------------------------------------------------------
-// Output wave of local tile jl.
+// Output wave of local tile jl: O = Q' S^T + P'' V.
 template <bool kOutBf16, bool kFp8, bool kRev, bool kAdd>
 __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int j, int jl, char *lds) {
   using G = Buf<kFp8>;
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const char *Simg = lds + G::kSImg + jl * 4096;
-  const char *Rimg = lds + G::kRImg + jl * 2560;
-  const int *exps = reinterpret_cast<const int *>(lds + G::kExp) + 2 * jl;
+  const int *exps = reinterpret_cast<const int *>(lds + G::kExp) + jl;
   const size_t rowstride = size_t(a.H) * D;
   auto ld128 = [](const char *p) {
     const uint4 x = *reinterpret_cast<const uint4 *>(p);
@@ -349,7 +341,6 @@ __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int
     const int t0 = c * C, nv = min(C, a.T - t0);
     const int p0 = kRev ? a.T - t0 - nv : t0;  // first physical row of the chunk
     const char *buf = lds + (c & 1) * G::kBytes;
-    const float *cs = reinterpret_cast<const float *>(buf + kRecCs);
     // kAdd: the forward scan's output at this tile's rows, read early
     float add[CT][4];
     if constexpr (kAdd) {
@@ -367,54 +358,60 @@ __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Sop[kb] = ld128(Simg + kb * 1024 + lane * 16);
     const int sS = exps[0];
-    // ---- Q~ S'^T (Q~ S^T = 2^sS of it)
+    // P'' fragments (hi and lo) and this tile's V columns as bf16 B operands in
+    // pair order: token tiles (0, 1), (2, 3) and 4 alone; rows past the chunk's
+    // end hold zeros
+    const char *Ph = buf + kRecP, *Pl = buf + kRecPl;
+    F32 ph[9], pl[9];
+    {
+      const int off[9] = {p_off16(0), p_off32(1, 0), p_off32(2, 0), p_off16(2), p_off32(3, 0),
+                          p_off32(3, 1), p_off32(4, 0), p_off32(4, 1), p_off16(4)};
+      const bool wide[9] = {false, true, true, false, true, true, true, true, false};
+#pragma unroll
+      for (int x = 0; x < 9; ++x) {
+        ph[x] = wide[x] ? ld128(Ph + off[x] + lane * 16) : ld64(Ph + off[x] + lane * 8);
+        pl[x] = wide[x] ? ld128(Pl + off[x] + lane * 16) : ld64(Pl + off[x] + lane * 8);
+      }
+    }
+    uint32_t vw[CT][2];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      float vv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * t + 4 * lg + e;
+        if constexpr (kFp8)
+          vv[e] = __builtin_amdgcn_cvt_pk_f32_fp8(uint32_t(reinterpret_cast<const uint8_t *>(buf + G::kV)[r * G::kVRow + 16 * jl + ln]), false)[0];
+        else
+          vv[e] = bf16_to_f32(reinterpret_cast<const uint16_t *>(buf + G::kV)[r * (G::kVRow / 2) + 16 * jl + ln]);
+      }
+      // exact: every value here is a bf16 (or an E4M3 code, exact in bf16)
+      vw[t][0] = (__float_as_uint(vv[0]) >> 16) | (__float_as_uint(vv[1]) & 0xffff0000u);
+      vw[t][1] = (__float_as_uint(vv[2]) >> 16) | (__float_as_uint(vv[3]) & 0xffff0000u);
+    }
+    const F32 Vb0 = f32_of(vw[0][0], vw[0][1], vw[1][0], vw[1][1]);
+    const F32 Vb1 = f32_of(vw[2][0], vw[2][1], vw[3][0], vw[3][1]);
+    const F32 Vh0 = f32_of(vw[0][0], vw[0][1], 0u, 0u), Vh2 = f32_of(vw[2][0], vw[2][1], 0u, 0u);
+    const F32 Vh4 = f32_of(vw[4][0], vw[4][1], 0u, 0u);
+    // ---- Q' S'^T (Q' S^T = 2^sS of it)
     f32x4 O[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) O[t] = zero4();
     rows_times_S(buf + kRecQ, lane, Sop, O);
-    // P' fragments of this chunk (part A of the record: valid until Y(c))
-    const char *Pr = buf + kRecP;
-    const F32 P00 = ld64(Pr + p_off16(0) + lane * 8);
-    const F32 P10 = ld128(Pr + p_off32(1, 0) + lane * 16);
-    const F32 P20 = ld128(Pr + p_off32(2, 0) + lane * 16);
-    const F32 P22 = ld64(Pr + p_off16(2) + lane * 8);
-    const F32 P30 = ld128(Pr + p_off32(3, 0) + lane * 16);
-    const F32 P31 = ld128(Pr + p_off32(3, 1) + lane * 16);
-    const F32 P40 = ld128(Pr + p_off32(4, 0) + lane * 16);
-    const F32 P41 = ld128(Pr + p_off32(4, 1) + lane * 16);
-    const F32 P44 = ld64(Pr + p_off16(4) + lane * 8);
-    compute_barrier();  // Y(c)
-    const F32 Rb0 = ld128(Rimg + lane * 16), Rb1 = ld128(Rimg + 1024 + lane * 16);
-    const uint2 r4 = *reinterpret_cast<const uint2 *>(Rimg + 2048 + lane * 8);
-    const int sR = exps[1];
-    // 16-deep halves: token tile 0, 2 or 4 alone, the other slots zero
-    const F32 Rh0 = f32_of(Rb0.w[0], Rb0.w[1], 0u, 0u), Rh2 = f32_of(Rb1.w[0], Rb1.w[1], 0u, 0u);
-    const F32 Rh4 = f32_of(r4.x, r4.y, 0u, 0u);
-    // O = 2^sS Q~ S'^T + 2^sR P' R': with both scales 0 the products add onto
-    // the first term
-    auto p_times_r = [&](f32x4 *acc) {
-      acc[0] = mma_h(P00, Rh0, acc[0]);
-      acc[1] = mma_h(P10, Rb0, acc[1]);
-      acc[2] = mma_h(P20, Rb0, acc[2]);
-      acc[3] = mma_h(P30, Rb0, acc[3]);
-      acc[4] = mma_h(P40, Rb0, acc[4]);
-      acc[2] = mma_h(P22, Rh2, acc[2]);
-      acc[3] = mma_h(P31, Rb1, acc[3]);
-      acc[4] = mma_h(P41, Rb1, acc[4]);
-      acc[4] = mma_h(P44, Rh4, acc[4]);
-    };
-    GDN_RARELY(sS | sR) {
-      f32x4 PR[CT];
-#pragma unroll
-      for (int t = 0; t < CT; ++t) PR[t] = zero4();
-      p_times_r(PR);
+    GDN_RARELY(sS) {
 #pragma unroll
       for (int t = 0; t < CT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[t][e] = __builtin_ldexpf(O[t][e], sS) + __builtin_ldexpf(PR[t][e], sR);
-    } else {
-      p_times_r(O);
+        for (int e = 0; e < 4; ++e) O[t][e] = __builtin_ldexpf(O[t][e], sS);
     }
+    compute_barrier();  // Y(c): chunk c's buffer and the S image are no longer read
+    // ---- + P'' V (bf16 hi and lo against the exact rows)
+    const F32 *vb[9] = {&Vh0, &Vb0, &Vb0, &Vh2, &Vb0, &Vb1, &Vb0, &Vb1, &Vh4};
+    const int row_tile[9] = {0, 1, 2, 2, 3, 3, 4, 4, 4};
+#pragma unroll
+    for (int x = 0; x < 9; ++x) O[row_tile[x]] = mma(ph[x], *vb[x], O[row_tile[x]]);
+#pragma unroll
+    for (int x = 0; x < 9; ++x) O[row_tile[x]] = mma(pl[x], *vb[x], O[row_tile[x]]);
     // the chunk's rows of o: logical row r at physical row p0 + r (p0 + nv - 1 - r
     // reversed).  All values first, then the stores, each from its own register
     // (a store that reuses a register holds the next value back until it is sent).

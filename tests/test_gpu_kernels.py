@@ -1,29 +1,32 @@
 """Per-kernel parity of the MFMA path (needs an MI355X).
 
-The intra-chunk step's outputs -- the fp16 operand images K~, Q~, M, P' and
-the per-token scales of each chunk-head record -- are decoded from the
-workspace and compared with the same quantities built in fp64 from the chunked
-form of the gated delta rule (oracle.chunked).  The state pass is then
-replayed in fp64 from the decoded operands with its own roundings (S and R
-to fp16 under a per-tile power-of-two scale) to separate the two steps: the
-GPU's o must match that replay far more closely than the oracle.
+The intra-chunk step's outputs -- the fp16 operand images K~, Q' = Q~ + P' K~
+and M, the bf16 hi/lo pair of P'' = P' diag(beta), and the scales of each
+chunk-head record -- are decoded from the workspace and compared with the same
+quantities built in fp64 from the chunked form of the gated delta rule
+(oracle.chunked).  The state pass is then replayed in fp64 from the decoded
+operands with its own roundings (S and R to fp16 under a per-tile power-of-two
+scale) to separate the two steps: the GPU's o must match that replay far more
+closely than the oracle.
 """
 import numpy as np
 import pytest
 import torch
 
 from hybrid_linear_attention_gdn_amd import gdn
-from hybrid_linear_attention_gdn_amd.inputs import Workload, make_inputs, round_bf16_bits
+from hybrid_linear_attention_gdn_amd.inputs import Workload, bf16_bits_to_f32, make_inputs, round_bf16_bits
 from tests.helpers import oracle_for, rel_max_err, to_device
 
 pytestmark = pytest.mark.gpu
 
 C, D = 80, 112
-# record layout (bytes): K~, Q~ (5 token tiles x 3,584), P' (7,680), scales (256 fp32), M (7 x 2,560)
-KQ_BYTES, P_BYTES, CS_FLOATS = 5 * 3584, 7680, 256
+# record layout (bytes): K~, Q' (5 token tiles x 3,584), P'' hi, lo (7,680 each), scales (128 fp32:
+# beta[80], gamma_n), M (7 x 2,560)
+KQ_BYTES, P_BYTES, CS_FLOATS = 5 * 3584, 7680, 128
 REC_K, REC_Q = 0, KQ_BYTES
 REC_P = 2 * KQ_BYTES
-REC_CS = REC_P + P_BYTES
+REC_PL = REC_P + P_BYTES
+REC_CS = REC_PL + P_BYTES
 REC_M = REC_CS + 4 * CS_FLOATS
 REC_BYTES = REC_M + 7 * 2560
 P_BASE = {0: 0, 1: 512, 2: 1536, 3: 3072, 4: 5120}
@@ -45,6 +48,10 @@ def _tile16(tile):
 
 def _f16(rec, off, n):
     return rec[off:off + 2 * n].view(np.float16).astype(np.float64)
+
+
+def _bf16(rec, off, n):
+    return bf16_bits_to_f32(np.ascontiguousarray(rec[off:off + 2 * n]).view(np.uint16)).astype(np.float64)
 
 
 def decode_kq(rec, base):
@@ -69,25 +76,27 @@ def decode_m(rec):
     return M
 
 
-def decode_p(rec):
-    """P' (80 x 80), lower triangle"""
+def decode_p(rec, base):
+    """P'' hi or lo (80 x 80), lower triangle"""
     P = np.zeros((C, C))
     for R in range(5):
         rows = np.broadcast_to((16 * R + (np.arange(64) & 15))[:, None], (64, 8))
         for kb in range((R + 1) // 2):
-            P[rows, _pair32(kb)] = _f16(rec, REC_P + P_BASE[R] + kb * 1024, 512).reshape(64, 8)
+            P[rows, _pair32(kb)] = _bf16(rec, base + P_BASE[R] + kb * 1024, 512).reshape(64, 8)
         if R % 2 == 0:
-            P[rows[:, :4], _tile16(R)] = _f16(rec, REC_P + P_BASE[R] + (R // 2) * 1024, 256).reshape(64, 4)
+            P[rows[:, :4], _tile16(R)] = _bf16(rec, base + P_BASE[R] + (R // 2) * 1024, 256).reshape(64, 4)
     return P
 
 
 def decode(rec):
+    """K~, Q', P'' (hi + lo), M, scales"""
     cs = rec[REC_CS:REC_CS + 4 * CS_FLOATS].view(np.float32).astype(np.float64)
-    return decode_kq(rec, REC_K), decode_kq(rec, REC_Q), decode_p(rec), decode_m(rec), cs
+    return (decode_kq(rec, REC_K), decode_kq(rec, REC_Q), decode_p(rec, REC_P) + decode_p(rec, REC_PL),
+            decode_m(rec), cs)
 
 
 def expected_chunk(inp, b, h, c):
-    """fp64 K~, Q~, P', M and scales of one chunk from the chunked form."""
+    """fp64 K~, Q' = Q~ + P' K~, P'' = P' diag(beta), M and scales of one chunk from the chunked form."""
     from oracle.chunked import chunk_tensors
     T = inp.q.shape[1]
     sl = slice(c * C, min((c + 1) * C, T))
@@ -105,9 +114,12 @@ def expected_chunk(inp, b, h, c):
     M[:, :n] = K.T @ np.diag(rk * np.exp(G[-1] - G)) @ Tm
     Pp = np.zeros((C, C))
     Pp[:n, :n] = ct["Pm"] @ Tm  # Pm = L o Gamma o Q^ K^T
-    cs = np.zeros(241)
-    cs[:n], cs[80:80 + n], cs[160:160 + n], cs[240] = bt, bt * gam, gam, np.exp(G[-1])
-    return Kt, Qt, Pp, M, cs
+    Qh = Qt + Pp @ Kt
+    P2 = Pp.copy()
+    P2[:, :n] *= bt[None, :]
+    cs = np.zeros(81)
+    cs[:n], cs[80] = bt, np.exp(G[-1])
+    return Kt, Qh, P2, M, cs
 
 
 def _run_with_ws(inp):
@@ -145,14 +157,14 @@ def test_intra_operands_match_chunked_form():
     for h in range(3):
         for c in range(3):
             Kg, Qg, Pg, Mg, csg = decode(_record(ws, lay, 3, h, c))
-            Kt, Qt, Pp, M, cs = expected_chunk(inp, 0, h, c)
+            Kt, Qh, P2, M, cs = expected_chunk(inp, 0, h, c)
             eK = _close(Kg, Kt, f16, "K~")
-            eQ = _close(Qg, Qt, f16, "Q~")
-            eP = _close(Pg, Pp, f16, "P'")
+            eQ = _close(Qg, Qh, f16, "Q'")
+            eP = _close(Pg, P2, 2.0 ** -15, "P''")  # a bf16 hi/lo pair: 16 significant bits
             eM = _close(Mg, M, f16, "M")
-            print(f"h={h} c={c}: max err / max  K~ {eK:.1e}  Q~ {eQ:.1e}  P' {eP:.1e}  M {eM:.1e}  "
-                  f"scales {np.abs(csg[:241] - cs).max():.1e}", flush=True)
-            np.testing.assert_allclose(csg[:241], cs, rtol=1e-5, atol=1e-7)
+            print(f"h={h} c={c}: max err / max  K~ {eK:.1e}  Q' {eQ:.1e}  P'' {eP:.1e}  M {eM:.1e}  "
+                  f"scales {np.abs(csg[:81] - cs).max():.1e}", flush=True)
+            np.testing.assert_allclose(csg[:81], cs, rtol=1e-5, atol=1e-7)
 
 
 def _round_tiles(X):
@@ -177,12 +189,12 @@ def _replay(inp, ws, lay, h, T):
     for c in range(N):
         sl = slice(c * C, min((c + 1) * C, T))
         n = sl.stop - sl.start
-        Kt, Qt, Pp, M, cs = decode(_record(ws, lay, inp.q.shape[2], h, c))
+        Kt, Qh, P2, M, cs = decode(_record(ws, lay, inp.q.shape[2], h, c))
         V = inp.v[0, sl, h].astype(np.float64)
         S16 = _round_tiles(St)
         R16 = _round_tiles(cs[:n, None] * V + Kt[:n] @ S16)
-        O[sl] = Qt[:n] @ S16 + Pp[:n, :n] @ R16
-        St = cs[240] * St + M[:, :n] @ R16
+        O[sl] = Qh[:n] @ S16 + P2[:n, :n] @ V
+        St = cs[80] * St + M[:, :n] @ R16
     return O, St
 
 
