@@ -170,6 +170,17 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
     }
   }
   __syncthreads();
+  // step 5's operand: q_r[16 Dt + 4 lg .. + 3] for this wave's d_k tiles Dt = wave, wave + 4 and
+  // rows r = 16 Rt + ln (four bf16 per tile), kept in registers from here: the Q rows' LDS is
+  // reused after step 2
+  uint2 q5[2][CT];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+    for (int Rt = 0; Rt < CT; ++Rt) {
+      const int Dt = min(wave + 4 * pass, NT - 1);
+      q5[pass][Rt] = *reinterpret_cast<const uint2 *>(Qr + (16 * Rt + ln) * kKrRow + 16 * Dt + 4 * lg);
+    }
   // per-token scalars: beta, 1/||k||, 1/||q||, G; chunk scalars for the state pass.
   // Waves 0 and 1 take tokens 64 w + lane; G, the inclusive prefix sum of the
   // floored log-decays over the chunk, comes from wave scans of its two parts.
@@ -553,25 +564,15 @@ __device__ __forceinline__ void intra_chunk(char *lds, const char *__restrict__ 
     for (int pass = 0; pass < 2; ++pass) {
       const int Dt = wave + 4 * pass;
       if (Dt < NT) {
-        // Q~^T of the five tiles: q_r[16Dt + 4lg .. + 3] (L2-resident: step 1 read these rows)
+        // Q~^T of the five tiles from the q elements kept since step 1
         f32x4 acc[CT];
 #pragma unroll
         for (int Rt = 0; Rt < CT; ++Rt) {
           const int r = 16 * Rt + ln;
           const float f = fexp(sG[r]) * srq[r];  // 0 past the chunk's end
-          float x[4] = {0.f, 0.f, 0.f, 0.f};
-          if (r < n) {
-            const char *src = qbase + (size_t(phys_token(t0 + r, T, rev)) * rowstride + 16 * Dt + 4 * lg) * kElem;
-            if constexpr (kFp8) {
-              const uint32_t w = *reinterpret_cast<const uint32_t *>(src);
-              const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-              x[0] = lo2[0], x[1] = lo2[1], x[2] = hi2[0], x[3] = hi2[1];
-            } else {
-              const uint2 w = *reinterpret_cast<const uint2 *>(src);
-              x[0] = __uint_as_float(w.x << 16), x[1] = __uint_as_float(w.x & 0xffff0000u);
-              x[2] = __uint_as_float(w.y << 16), x[3] = __uint_as_float(w.y & 0xffff0000u);
-            }
-          }
+          const uint2 w = q5[pass][Rt];  // rows past the chunk's end are zero in LDS
+          const float x[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
           acc[Rt] = f32x4{f * x[0], f * x[1], f * x[2], f * x[3]};
         }
         const uint16_t *kt = Kt + (16 * Dt + ln) * kKtRow + 4 * lg;

@@ -449,13 +449,17 @@ __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int
 // ---------------------------------------------------------------------------
 // Copy wave L (0..3): the chunk record's 1 KB pieces i with i % 4 == L and
 // (L == 3) this workgroup's V columns.  Every read of chunk c's buffer happens
-// before barrier Y(c), so chunk c + 2's copies are issued at Y(c) and wait
-// before X(c + 2).  Each wave also touches its share of chunk c + 4's lines
+// before barrier Y(c), so chunk c + 2's copies may be issued from Y(c) on and
+// must land before X(c + 2).  The copies of a chunk take about as long to
+// issue as a chunk takes to compute (the memory pipeline accepts a load only
+// as fast as earlier ones drain), so they are issued in two parts: part A of
+// chunk c + 2 after Y(c), part B after X(c + 1); no barrier waits for a whole
+// chunk's issue.  Each wave also touches its share of chunk c + 4's lines
 // (one dword per 128-byte line, into an LDS area nothing reads): the record
 // (the 16 copy waves of a head's four workgroups, which share an XCD and its
-// L2, split its 488 lines) and, for L == 3, one line per V row; so chunk
-// c + 2's copies hit L2.  Loads complete in issue order, so each wait names
-// the younger loads that may stay in flight.
+// L2, split its lines) and, for L == 3, one line per V row; so chunk c + 2's
+// copies hit L2.  Loads complete in issue order, so each wait names the
+// younger loads that may stay in flight.
 template <int L, bool kFp8, bool kRev>
 __device__ __forceinline__ void copy_role(const ScanArgs &a, int b, int h, int gi, int tile0, int ntiles, char *lds) {
   using G = Buf<kFp8>;
@@ -464,18 +468,26 @@ __device__ __forceinline__ void copy_role(const ScanArgs &a, int b, int h, int g
   const uint32_t row_bytes = uint32_t(a.H) * D * G::kElem;
   const uint32_t head_off = uint32_t(h) * D * G::kElem;
   constexpr int kLast = kCopyWaves - 1;
-  // copy instructions this wave issues per chunk, and touch instructions
-  constexpr int cN = (kRecInstr - L + kCopyWaves - 1) / kCopyWaves + (L == kLast ? G::kVInstr : 0);
+  // record pieces of this wave per chunk, the first kA of them in part A;
+  // part B holds the rest and (L == 3) the V rows.  Touch instructions: nT.
+  constexpr int kPieces = (kRecInstr - L + kCopyWaves - 1) / kCopyWaves;
+  constexpr int kA = (kPieces + (L == kLast ? G::kVInstr : 0)) / 2;
+  constexpr int cN = kPieces + (L == kLast ? G::kVInstr : 0);
   constexpr int nT = L == kLast ? 3 : 1;
   constexpr int kLines = kRecBytes / 128, kPerWave = (kLines + kGroups * kCopyWaves - 1) / (kGroups * kCopyWaves);
-  static_assert(kPerWave <= 64 && 2 * (cN + nT) < 64, "one touch instruction per wave; vmcnt holds 63");
+  static_assert(kPerWave <= 64 && cN + kA + 2 * nT < 64, "one touch instruction per wave; vmcnt holds 63");
   const int c_last = a.ce - 1;
-  auto copy_chunk = [&](int c) {
+  // part A (kPart 0) or B (kPart 1) of chunk c's copies
+  auto copy_part = [&](int c, auto part) {
+    constexpr int kPart = decltype(part)::value;
     const auto rr = make_rsrc(a.rec + (size_t(c - a.cb) * a.units + u) * kRecBytes, kRecBytes);
     char *dst = lds + (c & 1) * G::kBytes + G::kRec;
 #pragma unroll
-    for (int i = L; i < kRecInstr; i += kCopyWaves) copy16(rr, dst + 1024 * i, 1024u * i + 16u * lane);
-    if constexpr (L == kLast) {
+    for (int x = 0; x < kPieces; ++x) {
+      const int i = L + kCopyWaves * x;
+      if ((x < kA) == (kPart == 0)) copy16(rr, dst + 1024 * i, 1024u * i + 16u * lane);
+    }
+    if constexpr (L == kLast && kPart == 1) {
       // this workgroup's columns of each row; a missing second tile reads as zero
       const int t0 = c * C, nv = min(C, a.T - t0);
       const int p0 = kRev ? a.T - t0 - nv : t0;
@@ -510,23 +522,28 @@ __device__ __forceinline__ void copy_role(const ScanArgs &a, int b, int h, int g
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, scratch, 4, int(64 + lane < nv ? uint32_t(64 + lane) * row_bytes : kOutOfRange), 0, 0, 0);
     }
   };
+  constexpr auto kPartA = std::integral_constant<int, 0>{};
+  constexpr auto kPartB = std::integral_constant<int, 1>{};
   const int cb = a.cb, ce = a.ce;
   if (cb < ce) {
-    copy_chunk(cb);
+    copy_part(cb, kPartA);
+    copy_part(cb, kPartB);
     touch(cb + 2);
-    if (cb + 1 < ce) copy_chunk(cb + 1);
+    if (cb + 1 < ce) copy_part(cb + 1, kPartA);
     touch(cb + 3);
   }
   for (int c = cb; c < ce; ++c) {
-    // in flight, oldest first: copies of c, touches of c + 2, copies of c + 1
-    // (if c + 1 < ce), touches of c + 3
+    // issued after chunk c's last copy: part A of c + 1 (if c + 1 < ce) and
+    // the touches since (one, two before the first chunk: the wait then also
+    // covers the older one)
     if (c + 1 < ce)
-      wait_vm<cN + 2 * nT>();
+      wait_vm<kA + nT>();
     else
-      wait_vm<2 * nT>();
+      wait_vm<nT>();
     bare_barrier();  // X(c)
+    if (c + 1 < ce) copy_part(c + 1, kPartB);
     bare_barrier();  // Y(c)
-    if (c + 2 < ce) copy_chunk(c + 2);
+    if (c + 2 < ce) copy_part(c + 2, kPartA);
     touch(c + 4);
   }
   wait_vm<0>();
