@@ -15,8 +15,8 @@ constexpr int kMfmaDim = 112;     // head_dim of the SANA-WM DiT (20 heads x 112
 constexpr float kLogDecayFloor = -80.0f;
 // MFMA path: chunks in the first range (its intra-chunk step runs alone) and the
 // default length of the later ranges (the workspace ring holds two ranges)
-constexpr int kFirstRange = 8;
-constexpr int kRangeCap = 96;
+constexpr int kFirstRange = 16;
+constexpr int kRangeCap = 48;
 constexpr bool kHaveMfmaPath = true;
 
 enum : uint32_t { kBetaIsProb = 1u, kQkPrenormalized = 2u, kReverse = 8u };

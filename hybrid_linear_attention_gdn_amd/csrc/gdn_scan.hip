@@ -239,17 +239,6 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
         Racc[t][e] = xa[e] * vv;
       }
     }
-    const char *Mr = buf + kRecM;
-    F32 mf[3][NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const uint4 x0 = *reinterpret_cast<const uint4 *>(Mr + m_off32(i, 0) + lane * 16);
-      const uint4 x1 = *reinterpret_cast<const uint4 *>(Mr + m_off32(i, 1) + lane * 16);
-      const uint2 x2 = *reinterpret_cast<const uint2 *>(Mr + m_off16(i) + lane * 8);
-      mf[0][i] = f32_of(x0.x, x0.y, x0.z, x0.w);
-      mf[1][i] = f32_of(x1.x, x1.y, x1.z, x1.w);
-      mf[2][i] = f32_of(x2.x, x2.y, 0u, 0u);
-    }
     // the update accumulates onto gamma_n S^T in place (gamma_n is 1 on every
     // chunk without a frame's first token)
     const float gamma_n = cs[kCsGammaN];
@@ -269,6 +258,20 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
         for (int e = 0; e < 4; ++e) Racc[t][e] += __builtin_ldexpf(Y[t][e], sS);
     } else {
       rows_times_S(buf + kRecK, lane, Sop, Racc);
+    }
+    // M's fragments only now (before Y(c)): read earlier, they would queue in
+    // front of K~'s in LDS and hold 84 more registers across the products
+    __builtin_amdgcn_sched_barrier(0);
+    const char *Mr = buf + kRecM;
+    F32 mf[3][NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const uint4 x0 = *reinterpret_cast<const uint4 *>(Mr + m_off32(i, 0) + lane * 16);
+      const uint4 x1 = *reinterpret_cast<const uint4 *>(Mr + m_off32(i, 1) + lane * 16);
+      const uint2 x2 = *reinterpret_cast<const uint2 *>(Mr + m_off16(i) + lane * 8);
+      mf[0][i] = f32_of(x0.x, x0.y, x0.z, x0.w);
+      mf[1][i] = f32_of(x1.x, x1.y, x1.z, x1.w);
+      mf[2][i] = f32_of(x2.x, x2.y, 0u, 0u);
     }
     // ---- R scaled by 2^-sR into fp16 pair-order operand blocks
     float mx = 0.f;
