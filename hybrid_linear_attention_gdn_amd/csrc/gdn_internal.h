@@ -35,7 +35,7 @@ struct Plan {
   size_t off_beta = 0, off_rq = 0, off_rk = 0, off_gcum = 0;       // fp32 [B,H,T]
   size_t off_W = 0, off_Ut = 0, off_U = 0, off_S0 = 0;              // portable path
   // MFMA path: a ring of two slots of range_cap x B*H chunk-head records
-  // (M | P' | scales, mfma_record_bytes() each) and the fp32 [B, H, d_v, d_k]
+  // (K~ | Q' | P'' hi | P'' lo | scales | M, mfma_record_bytes() each) and the fp32 [B, H, d_v, d_k]
   // state carried from one chunk range to the next
   size_t off_rec = 0, off_carry = 0;
   int range_cap = 0;
@@ -83,7 +83,7 @@ hipError_t launch_attn(const AttnPlan &p, int block, const void *q, const void *
                        void *o, hipStream_t stream);
 }
 
-// bytes of one chunk-head record of the MFMA path (M | P' | scales)
+// bytes of one chunk-head record of the MFMA path (K~ | Q' | P'' hi, lo | scales | M)
 size_t mfma_record_bytes();
 
 // ---- small device helpers shared by the kernel files ----

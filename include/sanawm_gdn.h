@@ -147,7 +147,7 @@ gdn_status_t gdn_chunk_step(const gdn_problem_t *p, const void *q, const void *k
  * one per device, allocated when the library's code is loaded on that device
  * and held until the process ends.  The call allocates and frees nothing.
  * Limit: on the bf16/fp8 kernels the chunk ranges shrink to fit (B*H up to
- * 383 at 64 MiB); the fp32 kernels need their whole gdn_workspace_bytes.  A
+ * 354 at 64 MiB); the fp32 kernels need their whole gdn_workspace_bytes.  A
  * problem that does not fit returns GDN_ERR_WORKSPACE before any HIP call.
  * The current device must be the stream's device (else
  * GDN_ERR_INVALID_ARGUMENT).  Calls that overlap on one device (two streams,
@@ -238,14 +238,17 @@ typedef struct {
     size_t beta, rq, rk, gcum; /* fp32 kernels: fp32 [B, H, T] each: sigmoid(beta), 1/||q||,
                                   1/||k||, chunk-local inclusive cumsum of the floored g */
     size_t rec;                /* MFMA kernels: a ring of two slots, each range_cap x B*H
-                                  chunk-head records of rec_bytes: M = K^T diag(s) T (17,920 B)
-                                  and P' = P T (7,680 B) as fp16 operand fragments, then 256
-                                  fp32 chunk scalars.  The chunks run in ranges of first_range,
-                                  then range_cap chunks; range j's records sit in slot j % 2,
-                                  record (chunk c, unit b*H + h) at index
+                                  chunk-head records of rec_bytes, in the state pass's operand
+                                  fragment order: K~ = -diag(beta gamma / ||k||) K (fp16,
+                                  17,920 B), Q' = diag(gamma / ||q||) Q + P' K~ (fp16, 17,920 B),
+                                  P'' = P T diag(beta) as a bf16 hi and a bf16 lo part (7,680 B
+                                  each), 128 fp32 chunk scalars (beta[80], gamma_n), and
+                                  M = K^T diag(s) T (fp16, 17,920 B).  The chunks run in ranges
+                                  of first_range, then range_cap chunks; range j's records sit
+                                  in slot j % 2, record (chunk c, unit b*H + h) at index
                                   (c - range start) * B*H + b*H + h.  After a call, the last two
                                   ranges' records remain. */
-    size_t rec_bytes;          /* 26,624 */
+    size_t rec_bytes;          /* 69,632 */
     size_t carry;              /* MFMA kernels: fp32 [B, H, d_v, d_k] state between ranges */
     int32_t range_cap, first_range;
     size_t total;              /* == gdn_workspace_bytes */

@@ -39,21 +39,25 @@ def context_frames(block: int, frames_per_block: int, cached_blocks: int, sink_f
     return sorted(frames)
 
 
-def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None = None) -> np.ndarray:
-    """softmax(q k^T * scale) v for one head: q [Lq, d], k [Lk, d], v [Lk, dv], fp64.
+def softmax_weights(q: np.ndarray, k: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """softmax(q k^T * scale) for one head: q [Lq, d], k [Lk, d] -> [Lq, Lk], fp64.
 
     The row maximum is subtracted before exponentiating (the softmax is
     unchanged by it; it only keeps exp() finite)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
     if scale is None:
         scale = 1.0 / np.sqrt(q.shape[-1])
     s = (q @ k.T) * scale
     s = s - s.max(axis=1, keepdims=True)
     w = np.exp(s)
     w /= w.sum(axis=1, keepdims=True)
-    return w @ v
+    return w
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """softmax(q k^T * scale) v for one head: q [Lq, d], k [Lk, d], v [Lk, dv], fp64."""
+    return softmax_weights(q, k, scale) @ np.asarray(v, np.float64)
 
 
 def stream_block(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, block: int, frame_tokens: int,

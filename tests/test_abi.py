@@ -181,14 +181,16 @@ def test_reverse_flag_and_bidirectional_host_checks(lib):
 
 
 def test_no_alloc_size_checks_before_any_hip_call(lib):
-    # the fixed 64 MiB workspace: B * H = 384 units do not fit even one-chunk
-    # ranges (175,104 B per unit); the fp32 kernels' workspace grows with T
+    # the fixed 64 MiB workspace: B * H = 355 units do not fit even one-chunk
+    # ranges (two 69,632 B records and the 50,176 B carried state per unit);
+    # the fp32 kernels' workspace grows with T
     assert L.GDN_NO_ALLOC_SCRATCH_BYTES == 64 << 20
     vp = ctypes.c_void_p
 
     def call(p):
         return lib.gdn_fwd_no_alloc(ctypes.byref(p), *(vp(0x10000 * (i + 1)) for i in range(8)), None)
-    assert call(_p(num_heads=384)) == L.GDN_ERR_WORKSPACE
+    assert call(_p(num_heads=355)) == L.GDN_ERR_WORKSPACE
+    assert call(_p(batch=5, num_heads=71)) == L.GDN_ERR_WORKSPACE
     assert b"workspace" in lib.gdn_last_error()
     assert call(_p(qkv_dtype=L.GDN_F32, seq_len=27280)) == L.GDN_ERR_WORKSPACE
     assert call(_p(batch=0)) == L.GDN_ERR_INVALID_ARGUMENT

@@ -3,8 +3,11 @@
 
 Bar: max |o - o_ref| <= 1e-2 * rms(o_ref) per block for fp32 o (the bar the
 bf16 GDN path meets).  The kernel takes bf16 inputs exactly, keeps scores and
-the softmax in fp32 and rounds P to bf16 for the P V product (at most a relative 2^-8
-per weight): measured maxima are 5e-3 .. 8.5e-3 of rms(o_ref).  For bf16 o the
+the softmax in fp32 and rounds P to bf16 for the P V product (round to nearest
+even: at most 2^-9 relative per weight): measured maxima are 5e-3 .. 8.5e-3 of
+rms(o_ref).  At the page geometry every head is also held, element by element,
+to the forward error bound that this rounding and the fp32 arithmetic imply
+(bf16_p_bound).  For bf16 o the
 bar adds 2^-8 |o_ref| per element, since rounding an element to bf16 moves it
 by at most 2^-8 of itself.  The stream geometries cover every context shape:
 the first blocks (no sink segment, partial window), steady state (sink frame
@@ -104,9 +107,41 @@ def test_deterministic():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_page_geometry_sampled_heads():
-    # 880-token frames, 3 frames per block, 2 cached blocks, 1 sink frame, 20
-    # heads: block 3 attends 2,640 queries to 8,800 keys; three heads checked
+def bf16_p_bound(q, k, v, o_ref):
+    """Forward error bound of the kernel's o for one head (fp32 o), per element.
+
+    With exact weights p_j = exp(s_j - m) and the kernel's p~_j = p_j (1 + eta_j),
+    where eta_j collects the fp32 score and exp errors (eps_t) and the bf16
+    rounding of P (round to nearest even: 2^-9), numerator and denominator use
+    the same p~_j, so
+
+        o~ - o = sum_j p_j eta_j (v_j - o) / sum_j p~_j
+        |o~ - o| <= eta / (1 - eta) * sum_j w_j |v_j - o| <= eta / (1 - eta) * (W|V| + |o|),
+
+    plus the fp32 accumulation of the n-key sums (gamma_2n on numerator and
+    denominator, rescales included) and the final division (2^-22 |o|).
+    eps_t: the fp32 score q.k rounds to within (d + 8) 2^-24 scale sum_i |q_i k_i|
+    (the scaled score, the subtracted maximum and the exp argument included)
+    and exp adds 2 ulp.  Weights below 2^-126 that flush to zero add at most
+    n 2^-126 max|v|."""
+    d, n = q.shape[1], k.shape[0]
+    u = 2.0 ** -24
+    scale = 1.0 / np.sqrt(d)
+    qk_abs = (np.abs(q) @ np.abs(k).T).max(axis=1, keepdims=True)  # max_j sum_i |q_i k_ji|
+    eps = (d + 8) * u * scale * qk_abs + 2 * 2.0 ** -23
+    eta = (1 + eps) * (1 + 2.0 ** -9) - 1
+    gam = 2 * n * u / (1 - 2 * n * u)
+    W = A.softmax_weights(q, k)
+    WV = W @ np.abs(v)
+    c = (eta + gam) / (1 - eta - gam)
+    return c * (WV + np.abs(o_ref)) + 2.0 ** -22 * np.abs(o_ref) + n * 2.0 ** -126 * np.abs(v).max()
+
+
+def test_page_geometry_all_heads_within_bf16_p_bound():
+    """880-token frames, 3 frames per block, 2 cached blocks, 1 sink frame, 20
+    heads: block 3 attends 2,640 queries to 8,800 keys.  Every head is checked
+    against the oracle at the 1e-2 rms bar and element by element against the
+    forward error bound of rounding P to bf16 (bf16_p_bound)."""
     B, H, ft, fpb, C, S = 1, 20, 880, 3, 2, 1
     blocks = 4
     s = make_attn_stream(B, H, ft, fpb, blocks, 350)
@@ -118,12 +153,18 @@ def test_page_geometry_sampled_heads():
         sl = slice(n * Lb, (n + 1) * Lb)
         o = attn.block_fwd(p, n, q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), cache)
     torch.cuda.synchronize()
-    o = o.float().cpu().numpy()
+    o = o.float().cpu().numpy().astype(np.float64)
     frames = A.context_frames(3, fpb, C, S)
     rows = np.concatenate([np.arange(f * ft, (f + 1) * ft) for f in frames])
     assert len(rows) == 8800
-    for h in (0, 9, 19):
-        ref = A.attention(s.q[0, 3 * Lb:4 * Lb, h].astype(np.float64), s.k[0, rows, h], s.v[0, rows, h])
+    worst_rel, worst_bound = 0.0, 0.0
+    for h in range(H):
+        qh = s.q[0, 3 * Lb:4 * Lb, h].astype(np.float64)
+        kh, vh = s.k[0, rows, h].astype(np.float64), s.v[0, rows, h].astype(np.float64)
+        ref = A.attention(qh, kh, vh)
         err = _rel(o[0, :, h], ref)
-        print(f"head {h}: max err / rms = {err:.2e}", flush=True)
-        assert err <= TOL
+        ratio = float((np.abs(o[0, :, h] - ref) / bf16_p_bound(qh, kh, vh, ref)).max())
+        print(f"head {h}: max err / rms = {err:.2e}; max err / bound = {ratio:.3f}", flush=True)
+        worst_rel, worst_bound = max(worst_rel, err), max(worst_bound, ratio)
+        assert err <= TOL and ratio <= 1.0, (h, err, ratio)
+    print(f"all 20 heads: max err / rms {worst_rel:.2e}, max err / bound {worst_bound:.3f}", flush=True)

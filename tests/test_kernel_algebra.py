@@ -1,14 +1,15 @@
 """The chunk algebra the MFMA kernels implement, checked in fp64 against the
 token-by-token oracle (CPU only).
 
-The intra kernel writes, per chunk of n tokens, the records M and P' and the
-scales; the chain kernel then runs, with S the d_v x d_k state:
+The intra-chunk step writes, per chunk of n tokens, a record of K~, Q', P''
+and M and the scales; the state pass then runs, with S the d_v x d_k state:
 
     A_ri = beta_r rk_r rk_i e^(G_r - G_i) (k_r . k_i)    (i < r),   T = (I + A)^-1
     P_ri = rq_r rk_i e^(G_r - G_i) (q_r . k_i)          (i <= r),  P' = P T
     M    = K^T diag(rk_i e^(G_n - G_i)) T
-    Y = K S^T,   R = diag(beta) V - diag(beta gamma rk) Y
-    O = diag(gamma rq) Q S^T + P' R,   S^T <- gamma_n S^T + M R
+    K~   = -diag(beta gamma rk) K,   Q' = diag(gamma rq) Q + P' K~,   P'' = P' diag(beta)
+    R    = diag(beta) V + K~ S^T,    S^T <- gamma_n S^T + M R
+    O    = Q' S^T + P'' V            (= diag(gamma rq) Q S^T + P' R)
 
 with raw (unnormalised) K, Q, V rows, rk = 1/|k|, rq = 1/|q|, G the chunk's
 inclusive cumulative log-decay (floored at -80) and gamma = e^G.  This is a
@@ -46,10 +47,14 @@ def _chunk_form(q, k, v, g, beta, state_in, C):
         P = np.where(incl, r_q[:, None] * r_k[None, :] * dec * (Q @ K.T), 0.0)
         Pp = P @ Tm
         M = K.T @ ((r_k * np.exp(G[-1] - G))[:, None] * Tm)
+        Kt = -(b * gam * r_k)[:, None] * K
+        Qp = (gam * r_q)[:, None] * Q + Pp @ Kt
+        Ppp = Pp * b[None, :]
         St = S.T                                    # [dk, dv]
-        Y = K @ St
-        R = b[:, None] * V - (b * gam * r_k)[:, None] * Y
-        o[sl] = (gam * r_q)[:, None] * (Q @ St) + Pp @ R
+        R = b[:, None] * V + Kt @ St
+        o[sl] = Qp @ St + Ppp @ V
+        # the textbook output form gives the same rows
+        assert np.allclose(o[sl], (gam * r_q)[:, None] * (Q @ St) + Pp @ R, rtol=0, atol=1e-12 * (1 + np.abs(o[sl]).max()))
         S = (gam[-1] * St + M @ R).T
     return o, S
 
@@ -74,7 +79,7 @@ def test_chunk_algebra_equals_recurrence(T, C, d):
 
 
 def test_chunk_algebra_records_have_the_stated_shapes():
-    # M is d_k x n and P' lower triangular n x n: what the intra kernel stores
+    # M is d_k x n and P' lower triangular n x n: what the intra-chunk step stores
     r = np.random.default_rng(3)
     n, d = 80, 112
     K, Q = r.standard_normal((n, d)), r.standard_normal((n, d))
