@@ -221,8 +221,13 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
     const char *buf = lds + (c & 1) * G::kBytes;
     const float *cs = reinterpret_cast<const float *>(buf + kRecCs);
     compute_barrier();  // X(c)
-    // R's accumulators start at a V 2^-sS, the update's at gamma_n S^T: the
-    // products then add K~ S'^T and M R' to them
+    // ---- Y = K~ S'^T from zero accumulators, so that the products wait only
+    // for the K~ fragments (read first), not for the V rows
+    f32x4 Y[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) Y[t] = zero4();
+    rows_times_S(buf + kRecK, lane, Sop, Y);
+    // ---- R = a V + 2^sS Y
     f32x4 Racc[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
@@ -246,18 +251,14 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
 #pragma unroll
       for (int i = 0; i < NT; ++i) St[i] = St[i] * gamma_n;
     }
-    // ---- R = a V + 2^sS K~ S'^T
     GDN_RARELY(sS) {
-      f32x4 Y[CT];
-#pragma unroll
-      for (int t = 0; t < CT; ++t) Y[t] = zero4();
-      rows_times_S(buf + kRecK, lane, Sop, Y);
 #pragma unroll
       for (int t = 0; t < CT; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) Racc[t][e] += __builtin_ldexpf(Y[t][e], sS);
     } else {
-      rows_times_S(buf + kRecK, lane, Sop, Racc);
+#pragma unroll
+      for (int t = 0; t < CT; ++t) Racc[t] = Racc[t] + Y[t];
     }
     // M's fragments only now (before Y(c)): read earlier, they would queue in
     // front of K~'s in LDS and hold 84 more registers across the products
