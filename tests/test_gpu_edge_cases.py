@@ -8,7 +8,8 @@ oracle/bidirectional.py).
   decay by at most e^-80 (the state before it is forgotten either way);
 * rows of q or k that are exactly zero (normalised as x / max(||x||, eps):
   the row stays zero, a zero query reads exactly 0);
-* dense per-token gates -softplus(N(0,1) + 2) at the full 241-frame shape;
+* dense per-token gates -softplus(N(0,1) + 2) at the full 241-frame shape,
+  every head;
 * retrieval of a stored value with standard-basis keys, alpha = beta = 1:
   exact, so asserted bit for bit;
 * a NaN gate: the documented reading is that NaN propagates -- every output of
@@ -28,7 +29,7 @@ from hybrid_linear_attention_gdn_amd.inputs import (WORKLOADS, Workload, bf16_bi
                                                     round_bf16_bits)
 from oracle import bidirectional as BD
 from oracle.recurrence import gdn_recurrence
-from tests.helpers import TOL_BF16, TOL_F32, rel_max_err, to_device
+from tests.helpers import TOL_BF16, TOL_F32, rel_max_err, state_err, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +66,7 @@ def _oracle(inp, reverse, heads=None, s_in=None):
 
 def _check(o, st, o_ref, s_ref, fp32, label):
     tol = TOL_F32 if fp32 else TOL_BF16
-    eo, es = rel_max_err(o, o_ref), rel_max_err(st, s_ref)
+    eo, es = rel_max_err(o, o_ref), state_err(st, s_ref)
     _say(f"[{label}] o {eo:.3e} state {es:.3e} (bar {tol:g})")
     assert np.isfinite(o).all() and np.isfinite(st).all()
     assert eo <= tol and es <= tol, (eo, es)
@@ -108,16 +109,15 @@ def test_zero_query_and_key_rows(fp32, reverse):
 @pytest.mark.parametrize("reverse", DIRECTIONS)
 def test_dense_per_token_gates_full_shape(fp32, reverse):
     """Per-token gates -softplus(N(0,1) + 2) (frame length 1) on the 241-frame
-    shape, 27,280 tokens x 20 heads; the oracle checks heads 0, 7 and 19."""
+    shape, 27,280 tokens x 20 heads; the oracle checks every head."""
     w = WORKLOADS["clip_241f"]
     inp = make_inputs(w, frame_tokens=1)
     assert (inp.g < 0).all()
     _say(f"case dense gates 27,280 x 20, fp32 inputs={fp32}, reverse={reverse}")
     o, st = _run(inp, fp32, reverse)
-    heads = [0, 7, 19]
-    o_ref, s_ref = _oracle(inp, reverse, heads=heads)
-    _check(o[:, :, heads], st[:, heads], o_ref, s_ref, fp32, "dense gates, heads 0, 7, 19")
     assert np.isfinite(o).all()
+    o_ref, s_ref = _oracle(inp, reverse)
+    _check(o, st, o_ref, s_ref, fp32, "dense gates, all 20 heads")
 
 
 @pytest.mark.parametrize("fp32", FAMILIES)

@@ -21,6 +21,7 @@ import torch
 from hybrid_linear_attention_gdn_amd import gdn, layer
 from hybrid_linear_attention_gdn_amd.inputs import make_layer_inputs
 from oracle import layer as LY
+from tests.helpers import state_err
 
 pytestmark = pytest.mark.gpu
 
@@ -106,7 +107,7 @@ def test_layer_matches_oracle(bidir):
     _say(f"  against the unrounded fp64 layer: {err_x:.3e}; bf16-storage oracle against it: {storage:.3e}")
     assert err_x <= storage + TOL
     if not bidir:
-        es = np.abs(st.cpu().numpy() - s_ref).max() / np.sqrt(np.mean(s_ref ** 2))
+        es = state_err(st.cpu().numpy(), s_ref)
         _say(f"exit state: {es:.3e}")
         assert es <= TOL
 

@@ -13,7 +13,7 @@ import torch
 
 from hybrid_linear_attention_gdn_amd import gdn
 from hybrid_linear_attention_gdn_amd.inputs import WORKLOADS, make_inputs
-from tests.helpers import TOL_BF16, TOL_F32, oracle_for, rel_max_err, to_device
+from tests.helpers import TOL_BF16, TOL_F32, oracle_for, rel_max_err, state_err, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def _run(inp, *, fp32=False, o_dtype=torch.float32, state=True):
 
 def _check(inp, o, st, o_ref, s_ref, tol, label):
     eo = rel_max_err(o, o_ref)
-    es = rel_max_err(st, s_ref) if st is not None else 0.0
+    es = state_err(st, s_ref) if st is not None else 0.0
     _say(f"[{label}] max|o-o_ref|/rms = {eo:.3e}   state: {es:.3e}   (bar {tol:g})")
     assert np.isfinite(o).all()
     assert eo <= tol, eo
@@ -127,16 +127,19 @@ def test_streaming_rollout_equals_one_pass():
     _check(inp, o_one.cpu().numpy(), s_one.cpu().numpy(), o_ref, s_ref, TOL_BF16, "stream_3f_x10")
 
 
-def test_minute_cfg_sampled_heads():
-    """B = 2, 106,480 tokens: the GPU runs the full problem; the oracle checks 6 of the 40 (b, h) units."""
+def test_minute_cfg_all_units():
+    """B = 2, 106,480 tokens: the GPU runs the full problem; the oracle checks
+    every one of the 40 (b, h) units, element by element (about a minute of
+    the host's cores)."""
     w = WORKLOADS["minute_cfg"]
     _say("case minute_cfg (2 x 106,480 tokens x 20 heads)")
     inp = make_inputs(w)
     o, st = _run(inp)
-    for b, heads in ((0, [0, 7, 19]), (1, [3, 11, 16])):
-        o_ref, s_ref = oracle_for(inp, heads=heads, batches=[b])
-        _check(inp, o[[b]][:, :, heads], st[[b]][:, heads], o_ref, s_ref, TOL_BF16, f"minute_cfg b={b} h={heads}")
     assert np.isfinite(o).all()
+    for b in range(2):
+        o_ref, s_ref = oracle_for(inp, batches=[b])
+        _check(inp, o[[b]], st[[b]], o_ref, s_ref, TOL_BF16, f"minute_cfg b={b}, all 20 heads")
+        del o_ref, s_ref
 
 
 def test_batch_copies_equal_single_batch():
