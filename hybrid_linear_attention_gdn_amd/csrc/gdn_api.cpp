@@ -243,17 +243,12 @@ gdn_status_t run_bidir(const gdn_problem_t *p, const void *q, const void *k, con
   gdn::Args a{q, k, v, g, beta, nullptr, nullptr, fwd_o, ws, st};
   gdn::Plan R = P;
   R.flags |= GDN_FLAG_REVERSE;
-  // MFMA path, bf16 inputs, fp32 o: the reverse scan adds the forward scan's
-  // output (already in o) as it stores, one fp32 add per element like the
-  // combine kernel, which then does not run
-  R.o_add = P.mfma && !o_bf16 && !P.qkv_fp8;
-  float *rev_dst = R.o_add ? fwd_o : rev_o;
   hipError_t e = enqueue(P, a);
   if (e == hipSuccess) {
-    a.o = rev_dst;
+    a.o = rev_o;
     e = enqueue(R, a);
   }
-  if (e == hipSuccess && !R.o_add) e = gdn::launch_combine(fwd_o, rev_o, o, o_bf16, size_t(P.B) * P.T * P.H * P.dv, st);
+  if (e == hipSuccess) e = gdn::launch_combine(fwd_o, rev_o, o, o_bf16, size_t(P.B) * P.T * P.H * P.dv, st);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
   return GDN_OK;

@@ -83,7 +83,6 @@ struct ScanArgs {
   const float *state_in;  // entry state of the state-pass range (NULL = zero)
   float *state_out;       // exit state of the range (NULL = not written)
   void *o;
-  const float *addend;    // reverse scan of the bidirectional layer: o already holds the forward output
   // state pass over chunks [cb, ce): the record of (u, c) at rec + ((c - cb) * units + u) * kRecBytes
   const char *rec;
   int cb, ce;
@@ -326,7 +325,7 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
 
 // ---------------------------------------------------------------------------
 // Output wave of local tile jl: O = Q' S^T + P'' V.
-template <bool kOutBf16, bool kFp8, bool kRev, bool kAdd>
+template <bool kOutBf16, bool kFp8, bool kRev>
 __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int j, int jl, char *lds) {
   using G = Buf<kFp8>;
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
@@ -345,18 +344,6 @@ __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int
     const int t0 = c * C, nv = min(C, a.T - t0);
     const int p0 = kRev ? a.T - t0 - nv : t0;  // first physical row of the chunk
     const char *buf = lds + (c & 1) * G::kBytes;
-    // kAdd: the forward scan's output at this tile's rows, read early
-    float add[CT][4];
-    if constexpr (kAdd) {
-#pragma unroll
-      for (int t = 0; t < CT; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * t + 4 * lg + e;
-          add[t][e] = r < nv ? a.addend[(size_t(b) * a.T + p0 + (kRev ? nv - 1 - r : r)) * rowstride + h * D + 16 * j + ln]
-                             : 0.f;
-        }
-    }
     compute_barrier();  // X(c)
     F32 Sop[4];
 #pragma unroll
@@ -427,7 +414,6 @@ __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         val[t][e] = O[t][e];
-        if constexpr (kAdd) val[t][e] += add[t][e];
         const int r = 16 * t + 4 * lg + e;
         // rows past the chunk's end are aimed outside the store descriptor and dropped
         const uint32_t oi = uint32_t(kRev ? nv - 1 - r : r) * uint32_t(rowstride) + uint32_t(h) * D + 16u * j + ln;
@@ -561,7 +547,7 @@ __device__ __forceinline__ void idle_role(const ScanArgs &a) {
   }
 }
 
-template <bool kOutBf16, bool kFp8, bool kRev, bool kAdd>
+template <bool kOutBf16, bool kFp8, bool kRev>
 __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanArgs a) {
   extern __shared__ __align__(16) char lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -578,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanArgs a) {
       if (jl >= ntiles)
         idle_role(a);
       else if (wave & 1)
-        output_role<kOutBf16, kFp8, kRev, kAdd>(a, b, h, tile0 + jl, jl, lds);
+        output_role<kOutBf16, kFp8, kRev>(a, b, h, tile0 + jl, jl, lds);
       else
         state_role<kFp8>(a, b, h, tile0 + jl, jl, lds);
     } else if (wave == 4) {
@@ -605,28 +591,25 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanArgs a) {
                     threadIdx.x & 255, valid);
 }
 
-template <bool kOutBf16, bool kFp8, bool kRev, bool kAdd>
+template <bool kOutBf16, bool kFp8, bool kRev>
 hipError_t launch_typed(const ScanArgs &a, unsigned blocks, hipStream_t st) {
   // more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU), once per instantiation
   static const hipError_t lds_ok =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_kernel<kOutBf16, kFp8, kRev, kAdd>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_kernel<kOutBf16, kFp8, kRev>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kScanLds);
   if (lds_ok != hipSuccess) return lds_ok;
-  scan_kernel<kOutBf16, kFp8, kRev, kAdd><<<dim3(blocks), dim3(kThreads), kScanLds, st>>>(a);
+  scan_kernel<kOutBf16, kFp8, kRev><<<dim3(blocks), dim3(kThreads), kScanLds, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_one(const Plan &p, const ScanArgs &a, unsigned blocks, hipStream_t st) {
   const bool rev = p.flags & kReverse;
   if (p.qkv_fp8) {
-    if (rev) return p.o_bf16 ? launch_typed<true, true, true, false>(a, blocks, st) : launch_typed<false, true, true, false>(a, blocks, st);
-    return p.o_bf16 ? launch_typed<true, true, false, false>(a, blocks, st) : launch_typed<false, true, false, false>(a, blocks, st);
+    if (rev) return p.o_bf16 ? launch_typed<true, true, true>(a, blocks, st) : launch_typed<false, true, true>(a, blocks, st);
+    return p.o_bf16 ? launch_typed<true, true, false>(a, blocks, st) : launch_typed<false, true, false>(a, blocks, st);
   }
-  if (rev) {
-    if (p.o_add) return launch_typed<false, false, true, true>(a, blocks, st);
-    return p.o_bf16 ? launch_typed<true, false, true, false>(a, blocks, st) : launch_typed<false, false, true, false>(a, blocks, st);
-  }
-  return p.o_bf16 ? launch_typed<true, false, false, false>(a, blocks, st) : launch_typed<false, false, false, false>(a, blocks, st);
+  if (rev) return p.o_bf16 ? launch_typed<true, false, true>(a, blocks, st) : launch_typed<false, false, true>(a, blocks, st);
+  return p.o_bf16 ? launch_typed<true, false, false>(a, blocks, st) : launch_typed<false, false, false>(a, blocks, st);
 }
 
 }  // namespace
@@ -658,7 +641,6 @@ hipError_t launch_mfma(const Plan &p, const Args &a) {
   sa.g = a.g;
   sa.beta = a.beta;
   sa.o = a.o;
-  sa.addend = p.o_add ? static_cast<const float *>(a.o) : nullptr;
   sa.T = p.T;
   sa.H = p.H;
   sa.units = units;

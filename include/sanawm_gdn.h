@@ -183,9 +183,9 @@ gdn_status_t gdn_fwd_no_alloc(const gdn_problem_t *p, const void *q, const void 
  * may not include GDN_FLAG_REVERSE.  Both scans accumulate in fp32; for bf16
  * o the sum is rounded once; either way each element is one fp32 add of the
  * two scans' outputs.  Size the workspace with
- * gdn_bidir_workspace_bytes: the scan's workspace (twice with the MFMA
- * kernels, whose reverse scan prepares its operands while the forward scan's
- * state pass runs) plus one or two fp32 copies of o.  Same validation, ownership and asynchrony contract as gdn_fwd.
+ * gdn_bidir_workspace_bytes: the scan's workspace (the two scans run one
+ * after the other and share it) plus the reverse scan's fp32 output and, for
+ * bf16 o, the forward scan's.  Same validation, ownership and asynchrony contract as gdn_fwd.
  */
 gdn_status_t gdn_bidir_workspace_bytes(const gdn_problem_t *p, size_t *bytes);
 gdn_status_t gdn_bidir_fwd(const gdn_problem_t *p, const void *q, const void *k, const void *v,
