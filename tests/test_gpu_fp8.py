@@ -5,8 +5,8 @@ reference"), against the fp64 oracle on the decoded values.
 Every E4M3FN value is exact in bf16 and the kernels widen the codes to bf16
 as they load them, so the fp8 path must reproduce the bf16 path fed with the
 same values bit for bit: that equality is checked at a ragged length with an
-initial state, on the chunk-range / two-stream schedule (B = 2 x 20 heads) and
-in streaming.  The parity bar is the bf16 path's, 1e-2 of rms(o_ref)."""
+initial state, at B = 1 and B = 2 x 20 heads (40 units: 160 state-pass
+workgroups beside the intra-chunk blocks) and in streaming.  The parity bar is the bf16 path's, 1e-2 of rms(o_ref)."""
 import sys
 
 import numpy as np
@@ -62,7 +62,8 @@ def test_fp8_ragged_and_small(T, B, H):
 
 @pytest.mark.parametrize("B", [1, 2])
 def test_fp8_equals_bf16_on_the_same_values(B):
-    """B = 2 runs the state pass in chunk ranges beside the intra kernel on a second stream."""
+    """B = 2: 40 (b, h) units, so the state pass takes 160 workgroups and the
+    intra-chunk blocks share the rest of the GPU with it."""
     w = WORKLOADS["clip_241f_fp8"]
     inp = make_inputs(w, seq_len=5063)
     inp.state0 = (0.02 * np.random.default_rng(8).standard_normal((1, 20, 112, 112))).astype(np.float32)
