@@ -13,9 +13,11 @@ constexpr int kChunk = 80;        // tokens per chunk (divides the 880-token lat
 constexpr int kMaxPortableDim = 128;
 constexpr int kMfmaDim = 112;     // head_dim of the SANA-WM DiT (20 heads x 112 = 2240)
 constexpr float kLogDecayFloor = -80.0f;
-// MFMA path: chunks in the first range (its intra-chunk step runs alone) and the
-// default length of the later ranges (the workspace ring holds two ranges)
-constexpr int kFirstRange = 16;
+// MFMA path: chunks in the first range (its intra-chunk step runs alone: 25
+// chunks of 20 heads are 250 blocks of two chunk-heads, one round of a
+// 256-CU GPU) and the default length of the later ranges (the workspace ring
+// holds two ranges)
+constexpr int kFirstRange = 25;
 constexpr int kRangeCap = 48;
 constexpr bool kHaveMfmaPath = true;
 

@@ -66,7 +66,7 @@ def test_workspace_bytes(lib):
     assert lay.total - lay.carry >= 20 * 112 * 112 * 4
     lay_l = L.WorkspaceLayout()
     assert lib.gdn_workspace_layout(ctypes.byref(_p(seq_len=80 * 500)), ctypes.byref(lay_l)) == 0
-    assert lay_l.range_cap == 48 and lay_l.first_range == 16
+    assert lay_l.range_cap == 48 and lay_l.first_range == 25
     assert lay_l.total < 2 * 48 * 20 * lay.rec_bytes + 20 * 112 * 112 * 4 + 4096  # bounded in T
     lay_p = L.WorkspaceLayout()
     assert lib.gdn_workspace_layout(ctypes.byref(_p(qkv_dtype=L.GDN_F32)), ctypes.byref(lay_p)) == 0
