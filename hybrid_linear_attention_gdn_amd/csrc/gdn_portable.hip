@@ -1,7 +1,8 @@
 // Portable kernels: the chunked gated delta rule in fp32 on the vector ALUs.
 //
-// They serve fp32 inputs (and any 1 <= d_k, d_v <= 128) and, on request, bf16
-// inputs as a second, independent evaluation of the MFMA path.  Per (batch,
+// They serve fp32 inputs (any 1 <= d_k, d_v <= 128); fed the values of a bf16
+// workload as fp32, they are a second, independent evaluation of what the
+// MFMA path computes.  Per (batch,
 // head) and per chunk of n <= 80 tokens with entry state S0 (d_v x d_k), the
 // chunked form of the recurrence is (normalised q, k; G = chunk-local
 // inclusive cumsum of the log-decay; gamma = exp(G)):
@@ -42,6 +43,53 @@ __device__ __forceinline__ ChunkIdx chunk_of_block(int H, int N, int T) {
   return r;
 }
 
+// Rows 0 .. rows-1 of an fp32 [*, d] source into LDS rows of stride ld (rows
+// at and past n are zero).  The loads of a batch are all issued before any LDS
+// store, so a block waits for one memory latency per batch rather than one per
+// element; rows of a multiple of 4 floats move as 16-byte loads (the sources
+// are 16-byte aligned).
+template <typename RowPtr>
+__device__ __forceinline__ void stage_rows(float *dst, int ld, int rows, int d, int n, RowPtr rowptr) {
+  constexpr int kBatch = 8;
+  if ((d & 3) == 0) {
+    const int q4 = d >> 2, total = rows * q4;
+    for (int base = threadIdx.x; base < total; base += blockDim.x * kBatch) {
+      float4 t[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int idx = base + int(blockDim.x) * j, r = idx / q4, pc = idx % q4;
+        t[j] = (idx < total && r < n) ? reinterpret_cast<const float4 *>(rowptr(r))[pc] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int idx = base + int(blockDim.x) * j, r = idx / q4, pc = idx % q4;
+        if (idx < total) {
+          float *o = dst + r * ld + 4 * pc;
+          o[0] = t[j].x;
+          o[1] = t[j].y;
+          o[2] = t[j].z;
+          o[3] = t[j].w;
+        }
+      }
+    }
+  } else {
+    const int total = rows * d;
+    for (int base = threadIdx.x; base < total; base += blockDim.x * kBatch) {
+      float t[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int idx = base + int(blockDim.x) * j, r = idx / d;
+        t[j] = (idx < total && r < n) ? rowptr(r)[idx % d] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int idx = base + int(blockDim.x) * j;
+        if (idx < total) dst[(idx / d) * ld + idx % d] = t[j];
+      }
+    }
+  }
+}
+
 // Each kernel first stages the rows it multiplies in LDS (row stride d + 1
 // floats, so that threads walking rows hit distinct banks), then forms its
 // products from LDS; global loads are coalesced row copies.  The reduction
@@ -56,14 +104,21 @@ __host__ __device__ constexpr size_t state_lds_floats(int dk) {
 __host__ __device__ constexpr size_t output_lds_floats(int dk, int dv) {
   return size_t(C) * (dk + 1) + size_t(dv > C ? dv : C) * (dk + 1) + size_t(C) * (C + 1) + C;
 }
+constexpr size_t kLdsFloats = 160 * 1024 / 4;  // one CU's LDS
+// the output kernel also stages the chunk's U rows when they fit
+__host__ __device__ constexpr bool output_u_in_lds(int dk, int dv) {
+  return output_lds_floats(dk, dv) + size_t(C) * (dv + 1) <= kLdsFloats;
+}
+__host__ __device__ constexpr size_t output_lds_launch_floats(int dk, int dv) {
+  return output_lds_floats(dk, dv) + (output_u_in_lds(dk, dv) ? size_t(C) * (dv + 1) : 0);
+}
 static_assert(C % 16 == 0, "the blocked solve works on 16 x 16 blocks");
 static_assert(intra_lds_floats(kMaxPortableDim, kMaxPortableDim) * 4 <= 160 * 1024 &&
                   state_lds_floats(kMaxPortableDim) * 4 <= 160 * 1024 &&
                   output_lds_floats(kMaxPortableDim, kMaxPortableDim) * 4 <= 160 * 1024,
               "every portable kernel fits one CU's LDS at the largest head dims");
 
-template <typename TIn>
-__global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, const TIn *__restrict__ v,
+__global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ k, const float *__restrict__ v,
                                                     const float *__restrict__ s_beta,
                                                     const float *__restrict__ s_rk,
                                                     const float *__restrict__ s_gcum, float *__restrict__ W,
@@ -87,26 +142,38 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, c
     cw[r] = ok ? sb[r] * expf(sG[r]) * srk[r] : 0.f;  // beta gamma rk
   }
   auto row = [&](int r, int d) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(d); };
-  for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
-    const int r = idx / dk, d = idx % dk;
-    Ks[r * ldk + d] = r < ci.n ? load_f32(k, row(r, dk) + d) : 0.f;
-  }
-  for (int idx = threadIdx.x; idx < C * dv; idx += blockDim.x) {
-    const int r = idx / dv, e = idx % dv;
-    Vs[r * ldv + e] = r < ci.n ? load_f32(v, row(r, dv) + e) : 0.f;
-  }
+  stage_rows(Ks, ldk, C, dk, ci.n, [&](int r) { return k + row(r, dk); });
+  stage_rows(Vs, ldv, C, dv, ci.n, [&](int r) { return v + row(r, dv); });
   __syncthreads();
-  // A (strictly lower), padded rows/cols are zero
-  for (int idx = threadIdx.x; idx < C * C; idx += blockDim.x) {
-    const int r = idx / C, i = idx % C;
-    float val = 0.f;
-    if (i < r && r < ci.n) {
-      float dot = 0.f;
-      #pragma unroll 8
-      for (int d = 0; d < dk; ++d) dot = fmaf(Ks[r * ldk + d], Ks[i * ldk + d], dot);
-      val = sb[r] * expf(sG[r] - sG[i]) * srk[r] * srk[i] * dot;
+  // A (strictly lower), padded rows/cols are zero.  Thread (rg, ig) forms the
+  // 5 x 5 entries (rg + 16 a, ig + 16 b): ten row reads per step for 25 products
+  {
+    const int rg = threadIdx.x / 16, ig = threadIdx.x % 16;
+    float dot[C / 16][C / 16];
+#pragma unroll
+    for (int a = 0; a < C / 16; ++a)
+#pragma unroll
+      for (int b = 0; b < C / 16; ++b) dot[a][b] = 0.f;
+    #pragma unroll 2
+    for (int d = 0; d < dk; ++d) {
+      float kr[C / 16], ki[C / 16];
+#pragma unroll
+      for (int a = 0; a < C / 16; ++a) {
+        kr[a] = Ks[(rg + 16 * a) * ldk + d];
+        ki[a] = Ks[(ig + 16 * a) * ldk + d];
+      }
+#pragma unroll
+      for (int a = 0; a < C / 16; ++a)
+#pragma unroll
+        for (int b = 0; b < C / 16; ++b) dot[a][b] = fmaf(kr[a], ki[b], dot[a][b]);
     }
-    A[r * ldc + i] = val;
+#pragma unroll
+    for (int a = 0; a < C / 16; ++a)
+#pragma unroll
+      for (int b = 0; b < C / 16; ++b) {
+        const int r = rg + 16 * a, i = ig + 16 * b;
+        A[r * ldc + i] = (i < r && r < ci.n) ? sb[r] * expf(sG[r] - sG[i]) * srk[r] * srk[i] * dot[a][b] : 0.f;
+      }
   }
   __syncthreads();
   // Tm = (I + A)^{-1} by 16 x 16 blocks (A is strictly lower, so Tm is unit
@@ -166,8 +233,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const TIn *__restrict__ k, c
 }
 
 // Sequential state pass: one block per (b, h, 16 rows of the state).
-template <typename TIn>
-__global__ __launch_bounds__(256) void state_kernel(const TIn *__restrict__ k, const float *__restrict__ s_rk,
+__global__ __launch_bounds__(256) void state_kernel(const float *__restrict__ k, const float *__restrict__ s_rk,
                                                     const float *__restrict__ s_gcum,
                                                     const float *__restrict__ W, const float *__restrict__ Ut,
                                                     const float *state_in, float *state_out,
@@ -209,28 +275,36 @@ __global__ __launch_bounds__(256) void state_kernel(const TIn *__restrict__ k, c
       S0[((bh * N + c) * dv + i0 + ii) * dk + d] = S[ii * ldk + d];
     }
     const size_t cb = (bh * N + c) * C;
-    for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
-      const int r = idx / dk, d = idx % dk;
-      const bool ok = r < n;
-      Ws[r * ldk + d] = ok ? W[(cb + r) * dk + d] : 0.f;
-      Ks[r * ldk + d] = ok ? load_f32(k, ((size_t(b) * T + phys_token(t0 + r, T, rev)) * H + h) * size_t(dk) + d) : 0.f;
-    }
+    stage_rows(Ws, ldk, C, dk, n, [&](int r) { return W + (cb + r) * dk; });
+    stage_rows(Ks, ldk, C, dk, n, [&](int r) { return k + ((size_t(b) * T + phys_token(t0 + r, T, rev)) * H + h) * size_t(dk); });
     __syncthreads();
-    // U = Ut - W S0^T for this tile's columns
-    for (int idx = threadIdx.x; idx < C * R; idx += blockDim.x) {
-      const int r = idx / R, ii = idx % R;
-      float u = 0.f;
-      if (r < n && ii < nrows) {
-        float s = 0.f;
-        #pragma unroll 8
-        for (int d = 0; d < dk; ++d) s = fmaf(Ws[r * ldk + d], S[ii * ldk + d], s);
-        u = Ut[(cb + r) * dv + i0 + ii] - s;
-        U[(cb + r) * dv + i0 + ii] = u;
+    // U = Ut - W S0^T for this tile's columns: thread (rg, ii) forms rows
+    // rg, rg + 16, ... of column ii, reading each S element once for five rows
+    {
+      const int ii = threadIdx.x % R, rg = threadIdx.x / R;
+      float acc[C / 16];
+#pragma unroll
+      for (int j = 0; j < C / 16; ++j) acc[j] = 0.f;
+      #pragma unroll 4
+      for (int d = 0; d < dk; ++d) {
+        const float sv = S[ii * ldk + d];
+#pragma unroll
+        for (int j = 0; j < C / 16; ++j) acc[j] = fmaf(Ws[(rg + 16 * j) * ldk + d], sv, acc[j]);
       }
-      Us[r * (R + 1) + ii] = u;
+#pragma unroll
+      for (int j = 0; j < C / 16; ++j) {
+        const int r = rg + 16 * j;
+        float u = 0.f;
+        if (r < n && ii < nrows) {
+          u = Ut[(cb + r) * dv + i0 + ii] - acc[j];
+          U[(cb + r) * dv + i0 + ii] = u;
+        }
+        Us[r * (R + 1) + ii] = u;
+      }
     }
     __syncthreads();
-    // S <- gamma_n S + U^T diag(rk e^{G_n - G}) K_raw
+    // S <- gamma_n S + U^T diag(rk e^{G_n - G}) K_raw, one element per thread step
+    // (a register-blocked form of this product measured slower)
     for (int idx = threadIdx.x; idx < R * dk; idx += blockDim.x) {
       const int ii = idx / dk, d = idx % dk;
       float s = 0.f;
@@ -247,8 +321,8 @@ __global__ __launch_bounds__(256) void state_kernel(const TIn *__restrict__ k, c
     }
 }
 
-template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void output_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k,
+template <typename TOut>
+__global__ __launch_bounds__(256) void output_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                      const float *__restrict__ s_rq,
                                                      const float *__restrict__ s_rk,
                                                      const float *__restrict__ s_gcum,
@@ -264,43 +338,65 @@ __global__ __launch_bounds__(256) void output_kernel(const TIn *__restrict__ q, 
   const ChunkIdx ci = chunk_of_block(H, N, T);
   const size_t sbase = (size_t(ci.b) * H + ci.h) * T + ci.t0;
   auto row = [&](int r, int d) { return ((size_t(ci.b) * T + phys_token(ci.t0 + r, T, rev)) * H + ci.h) * size_t(d); };
-  for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
-    const int r = idx / dk, d = idx % dk;
-    const bool ok = r < ci.n;
-    Qs[r * ldk + d] = ok ? load_f32(q, row(r, dk) + d) : 0.f;
-    KS[r * ldk + d] = ok ? load_f32(k, row(r, dk) + d) : 0.f;
-  }
+  stage_rows(Qs, ldk, C, dk, ci.n, [&](int r) { return q + row(r, dk); });
+  stage_rows(KS, ldk, C, dk, ci.n, [&](int r) { return k + row(r, dk); });
   for (int r = threadIdx.x; r < C; r += blockDim.x)
     sc[r] = r < ci.n ? expf(s_gcum[sbase + r]) * s_rq[sbase + r] : 0.f;
   __syncthreads();
-  for (int idx = threadIdx.x; idx < C * C; idx += blockDim.x) {
-    const int r = idx / C, i = idx % C;
-    float val = 0.f;
-    if (i <= r && r < ci.n) {
-      float dot = 0.f;
-      #pragma unroll 8
-      for (int d = 0; d < dk; ++d) dot = fmaf(Qs[r * ldk + d], KS[i * ldk + d], dot);
-      val = expf(s_gcum[sbase + r] - s_gcum[sbase + i]) * s_rq[sbase + r] * s_rk[sbase + i] * dot;
+  {  // P: thread (rg, ig) forms the 5 x 5 entries (rg + 16 a, ig + 16 b)
+    const int rg = threadIdx.x / 16, ig = threadIdx.x % 16;
+    float dot[C / 16][C / 16];
+#pragma unroll
+    for (int a = 0; a < C / 16; ++a)
+#pragma unroll
+      for (int b = 0; b < C / 16; ++b) dot[a][b] = 0.f;
+    #pragma unroll 2
+    for (int d = 0; d < dk; ++d) {
+      float qr[C / 16], ki[C / 16];
+#pragma unroll
+      for (int a = 0; a < C / 16; ++a) {
+        qr[a] = Qs[(rg + 16 * a) * ldk + d];
+        ki[a] = KS[(ig + 16 * a) * ldk + d];
+      }
+#pragma unroll
+      for (int a = 0; a < C / 16; ++a)
+#pragma unroll
+        for (int b = 0; b < C / 16; ++b) dot[a][b] = fmaf(qr[a], ki[b], dot[a][b]);
     }
-    P[r * ldc + i] = val;
+#pragma unroll
+    for (int a = 0; a < C / 16; ++a)
+#pragma unroll
+      for (int b = 0; b < C / 16; ++b) {
+        const int r = rg + 16 * a, i = ig + 16 * b;
+        P[r * ldc + i] = (i <= r && r < ci.n)
+                             ? expf(s_gcum[sbase + r] - s_gcum[sbase + i]) * s_rq[sbase + r] * s_rk[sbase + i] * dot[a][b]
+                             : 0.f;
+      }
   }
   __syncthreads();  // the k rows are no longer read: the entry state takes their place
   const size_t bhc = (size_t(ci.b) * H + ci.h) * N + ci.c;
   const float *S0c = S0 + bhc * size_t(dv) * dk;
-  for (int idx = threadIdx.x; idx < dv * dk; idx += blockDim.x) {
-    const int e = idx / dk, d = idx % dk;
-    KS[e * ldk + d] = S0c[idx];
-  }
-  __syncthreads();
+  stage_rows(KS, ldk, dv, dk, dv, [&](int e) { return S0c + size_t(e) * dk; });
+  // the chunk's U rows go to LDS too when they fit beside the rest (d_v <= 112
+  // at d_k = d_v); otherwise the products read them from the workspace
   const float *Uc = U + bhc * C * size_t(dv);
+  const bool u_lds = output_u_in_lds(dk, dv);
+  float *Us = sc + C;  // [C][dv + 1] when u_lds
+  if (u_lds) stage_rows(Us, dv + 1, C, dv, ci.n, [&](int i) { return Uc + size_t(i) * dv; });
+  __syncthreads();
   for (int idx = threadIdx.x; idx < ci.n * dv; idx += blockDim.x) {
     const int r = idx / dv, e = idx % dv;
     float qs = 0.f;
     #pragma unroll 8
     for (int d = 0; d < dk; ++d) qs = fmaf(Qs[r * ldk + d], KS[e * ldk + d], qs);
     float acc = sc[r] * qs;
-    #pragma unroll 8
-    for (int i = 0; i <= r; ++i) acc = fmaf(P[r * ldc + i], Uc[size_t(i) * dv + e], acc);
+    if (u_lds) {
+      #pragma unroll 8
+      for (int i = 0; i <= r; ++i) acc = fmaf(P[r * ldc + i], Us[i * (dv + 1) + e], acc);
+    } else {
+      #pragma unroll 8
+      for (int i = 0; i <= r; ++i) acc = fmaf(P[r * ldc + i], Uc[size_t(i) * dv + e], acc);
+    }
     const size_t oi = row(r, dv) + e;
     if constexpr (sizeof(TOut) == 2)
       o[oi] = f32_to_bf16(acc);
@@ -316,10 +412,9 @@ hipError_t allow_lds(F *kernel, size_t floats) {
                              int(floats * sizeof(float)));
 }
 
-template <typename TIn>
-hipError_t launch_typed(const Plan &p, const Args &a) {
-  const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
-            *v = static_cast<const TIn *>(a.v);
+hipError_t launch_fp32(const Plan &p, const Args &a) {
+  const float *q = static_cast<const float *>(a.q), *k = static_cast<const float *>(a.k),
+              *v = static_cast<const float *>(a.v);
   const float *beta = reinterpret_cast<const float *>(a.ws + p.off_beta);
   const float *rq = reinterpret_cast<const float *>(a.ws + p.off_rq);
   const float *rk = reinterpret_cast<const float *>(a.ws + p.off_rk);
@@ -332,25 +427,24 @@ hipError_t launch_typed(const Plan &p, const Args &a) {
   const bool rev = p.flags & kReverse;
   constexpr int kD = kMaxPortableDim;
   static const hipError_t lds_ok[4] = {
-      allow_lds(&intra_kernel<TIn>, intra_lds_floats(kD, kD)), allow_lds(&state_kernel<TIn>, state_lds_floats(kD)),
-      allow_lds(&output_kernel<TIn, uint16_t>, output_lds_floats(kD, kD)),
-      allow_lds(&output_kernel<TIn, float>, output_lds_floats(kD, kD))};
+      allow_lds(&intra_kernel, intra_lds_floats(kD, kD)), allow_lds(&state_kernel, state_lds_floats(kD)),
+      allow_lds(&output_kernel<uint16_t>, kLdsFloats), allow_lds(&output_kernel<float>, kLdsFloats)};
   for (hipError_t le : lds_ok)
     if (le != hipSuccess) return le;
-  intra_kernel<TIn><<<dim3(chunks), dim3(256), intra_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
+  intra_kernel<<<dim3(chunks), dim3(256), intra_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
       k, v, beta, rk, gc, W, Ut, p.T, p.H, p.dk, p.dv, p.N, rev);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned tiles = unsigned(p.B) * p.H * ((p.dv + 15) / 16);
-  state_kernel<TIn><<<dim3(tiles), dim3(256), state_lds_floats(p.dk) * sizeof(float), a.stream>>>(
+  state_kernel<<<dim3(tiles), dim3(256), state_lds_floats(p.dk) * sizeof(float), a.stream>>>(
       k, rk, gc, W, Ut, a.state_in, a.state_out, U, S0, p.T, p.H, p.dk, p.dv, p.N, rev);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.o_bf16)
-    output_kernel<TIn, uint16_t><<<dim3(chunks), dim3(256), output_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
+    output_kernel<uint16_t><<<dim3(chunks), dim3(256), output_lds_launch_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
         q, k, rq, rk, gc, U, S0, static_cast<uint16_t *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
   else
-    output_kernel<TIn, float><<<dim3(chunks), dim3(256), output_lds_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
+    output_kernel<float><<<dim3(chunks), dim3(256), output_lds_launch_floats(p.dk, p.dv) * sizeof(float), a.stream>>>(
         q, k, rq, rk, gc, U, S0, static_cast<float *>(a.o), p.T, p.H, p.dk, p.dv, p.N, rev);
   return hipGetLastError();
 }
@@ -358,7 +452,9 @@ hipError_t launch_typed(const Plan &p, const Args &a) {
 }  // namespace
 
 hipError_t launch_portable(const Plan &p, const Args &a) {
-  return p.qkv_bf16 ? launch_typed<uint16_t>(p, a) : launch_typed<float>(p, a);
+  // bf16 and fp8 inputs always take the MFMA kernels (make_plan): only fp32 here
+  if (p.qkv_bf16 || p.qkv_fp8) return hipErrorInvalidValue;
+  return launch_fp32(p, a);
 }
 
 }  // namespace gdn

@@ -1,5 +1,5 @@
-// K1 "prep": per token-head scalars of the gated delta rule, shared by both
-// kernel families.
+// K1 "prep": per token-head scalars of the gated delta rule for the fp32
+// kernels (the MFMA kernels form them inside their intra-chunk step).
 //
 // For every (b, t, h) it writes, in head-major [B, H, T] fp32 arrays:
 //   beta = sigmoid(beta logit)             (or the input itself: BETA_IS_PROB)
@@ -9,37 +9,36 @@
 // Normalisation, sigmoid and the log-decay are the readings stated in
 // include/sanawm_gdn.h of the gated delta rule the "SANA-WM" cookbook page
 // (table "Architecture & components") names as its attention.  q and k stay
-// raw in HBM: later kernels apply rq / rk as fp32 scales, so the bf16 inputs
-// enter the matrix cores unrounded.
+// raw in HBM: later kernels apply rq / rk as fp32 scales.
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-template <typename TIn>
-__global__ __launch_bounds__(256) void prep_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k,
-                                                   const float *__restrict__ g,
-                                                   const float *__restrict__ beta, float *__restrict__ o_beta,
-                                                   float *__restrict__ o_rq, float *__restrict__ o_rk,
-                                                   float *__restrict__ o_gcum, int T, int H, int dk, int N,
-                                                   uint32_t flags) {
-  const int b = blockIdx.x / N, c = blockIdx.x % N;
+// One block per (b, chunk, h): 16 lanes per token row (coalesced 64-byte
+// pieces, partial sums added by butterfly shuffles), 16 rows at a time; then
+// the chunk's floored decays are scanned in LDS (log-step inclusive scan).
+__global__ __launch_bounds__(256) void prep_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                                                   const float *__restrict__ g, const float *__restrict__ beta,
+                                                   float *__restrict__ o_beta, float *__restrict__ o_rq,
+                                                   float *__restrict__ o_rk, float *__restrict__ o_gcum, int T, int H,
+                                                   int dk, int N, uint32_t flags) {
+  const int h = blockIdx.x % H, c = (blockIdx.x / H) % N, b = blockIdx.x / (H * N);
   const int t0 = c * kChunk;
   const int n = min(kChunk, T - t0);
   const bool rev = flags & kReverse;
-  // 16 lanes per token-head row: lane l sums d = l, l + 16, ... (coalesced 64-byte
-  // pieces), then the 16 partial sums are added by butterfly shuffles
+  const size_t out = (size_t(b) * H + h) * T + t0;
   const int sub = threadIdx.x & 15;
-  for (int idx = threadIdx.x >> 4; idx < n * H; idx += blockDim.x >> 4) {
-    const int tt = idx / H, h = idx % H;
+  for (int tt = threadIdx.x >> 4; tt < n; tt += blockDim.x >> 4) {
     const size_t th = (size_t(b) * T + phys_token(t0 + tt, T, rev)) * H + h;
     float rq = 1.f, rk = 1.f;
     if (!(flags & kQkPrenormalized)) {
       float sq = 0.f, sk = 0.f;
       const size_t row = th * size_t(dk);
+#pragma unroll 8
       for (int d = sub; d < dk; d += 16) {
-        const float a = load_f32(q, row + d), e = load_f32(k, row + d);
-        sq = fmaf(a, a, sq);
+        const float x = q[row + d], e = k[row + d];
+        sq = fmaf(x, x, sq);
         sk = fmaf(e, e, sk);
       }
 #pragma unroll
@@ -52,37 +51,28 @@ __global__ __launch_bounds__(256) void prep_kernel(const TIn *__restrict__ q, co
     }
     if (sub == 0) {
       const float bl = beta[th];
-      const float bt = (flags & kBetaIsProb) ? bl : 1.f / (1.f + expf(-bl));
-      const size_t out = (size_t(b) * H + h) * T + t0 + tt;
-      o_beta[out] = bt;
-      o_rq[out] = rq;
-      o_rk[out] = rk;
+      o_beta[out + tt] = (flags & kBetaIsProb) ? bl : 1.f / (1.f + expf(-bl));
+      o_rq[out + tt] = rq;
+      o_rk[out + tt] = rk;
     }
   }
-  // chunk-local inclusive cumsum of the floored log-decay: the chunk's decays
-  // of up to 64 heads are staged in LDS (coalesced over heads), then one
-  // thread per head scans them.  The reverse scan takes each token's decay
-  // from its successor in the original order (the same frame boundary), and
-  // none for the last token.
-  __shared__ float gs[kChunk][65];
-  for (int h0 = 0; h0 < H; h0 += 64) {
-    const int nh = min(64, H - h0);
-    __syncthreads();  // the previous group's scan is done with gs
-    for (int idx = threadIdx.x; idx < n * nh; idx += blockDim.x) {
-      const int tt = idx / nh, hh = idx % nh, tau = t0 + tt;
-      const float gv = !rev ? g[(size_t(b) * T + tau) * H + h0 + hh]
-                            : (tau > 0 ? g[(size_t(b) * T + T - tau) * H + h0 + hh] : 0.f);
-      gs[tt][hh] = floor_log_decay(gv);
-    }
-    __syncthreads();
-    if (threadIdx.x < nh) {
-      const int h = h0 + threadIdx.x;
-      float G = 0.f;
-      const size_t out = (size_t(b) * H + h) * T + t0;
-      for (int tt = 0; tt < n; ++tt) {
-        G += gs[tt][threadIdx.x];
-        o_gcum[out + tt] = G;
-      }
+  // chunk-local inclusive cumsum of the floored log-decay, summed left to right
+  // by one thread (so that G_r - G_i carries only the rounding of the terms
+  // between i and r, as in a running sum).  The reverse scan takes each token's
+  // decay from its successor in the original order (the same frame boundary),
+  // and none for the last token.
+  __shared__ float gs[kChunk];
+  const int t = threadIdx.x;
+  if (t < n) {
+    const int tau = t0 + t;
+    gs[t] = floor_log_decay(!rev ? g[(size_t(b) * T + tau) * H + h] : (tau > 0 ? g[(size_t(b) * T + T - tau) * H + h] : 0.f));
+  }
+  __syncthreads();
+  if (t == 0) {
+    float G = 0.f;
+    for (int tt = 0; tt < n; ++tt) {
+      G += gs[tt];
+      o_gcum[out + tt] = G;
     }
   }
 }
@@ -125,15 +115,12 @@ hipError_t launch_prep(const Plan &p, const Args &a) {
   float *rq = reinterpret_cast<float *>(a.ws + p.off_rq);
   float *rk = reinterpret_cast<float *>(a.ws + p.off_rk);
   float *gc = reinterpret_cast<float *>(a.ws + p.off_gcum);
-  dim3 grid(unsigned(p.B) * unsigned(p.N)), block(256);
-  if (p.qkv_bf16)
-    prep_kernel<uint16_t><<<grid, block, 0, a.stream>>>(static_cast<const uint16_t *>(a.q),
-                                                        static_cast<const uint16_t *>(a.k), a.g, a.beta, beta,
-                                                        rq, rk, gc, p.T, p.H, p.dk, p.N, p.flags);
-  else
-    prep_kernel<float><<<grid, block, 0, a.stream>>>(static_cast<const float *>(a.q),
-                                                     static_cast<const float *>(a.k), a.g, a.beta, beta, rq,
-                                                     rk, gc, p.T, p.H, p.dk, p.N, p.flags);
+  // the fp32 kernels only (bf16 and fp8 inputs take the MFMA kernels, whose
+  // intra-chunk step forms these scalars itself)
+  if (p.qkv_bf16 || p.qkv_fp8) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(p.B) * unsigned(p.N) * unsigned(p.H)), block(256);
+  prep_kernel<<<grid, block, 0, a.stream>>>(static_cast<const float *>(a.q), static_cast<const float *>(a.k), a.g,
+                                            a.beta, beta, rq, rk, gc, p.T, p.H, p.dk, p.N, p.flags);
   return hipGetLastError();
 }
 
