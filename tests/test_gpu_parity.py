@@ -105,6 +105,30 @@ def test_clip_241f_full_config():
     _check(inp, o, st, o_ref, s_ref, TOL_BF16, "clip_241f")
 
 
+@pytest.mark.parametrize("T, reverse, workload", [(27240, False, "clip_241f"), (27240, True, "clip_241f"),
+                                                   (27223, False, "clip_241f_fp8")])
+def test_ragged_last_chunk_full_width(T, reverse, workload):
+    """340 full chunks and a last chunk of 40 (23) rows, 20 heads: in the last
+    chunk range the state pass's copy waves issue row loads and row touches
+    with lanes past the sequence's end.  Every head against the oracle, and
+    three calls bitwise equal."""
+    from oracle import bidirectional as BD
+    inp = make_inputs(WORKLOADS[workload], seq_len=T)
+    _say(f"case ragged last chunk: {workload} T={T} reverse={reverse}")
+    q, k, v, g, beta, s0 = to_device(inp)
+    runs = []
+    for _ in range(3):
+        o, st = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=reverse)
+        torch.cuda.synchronize()
+        runs.append((o, st))
+    for o, st in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(st, runs[0][1])
+    args = (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0)
+    o_ref, s_ref = BD.reverse_scan(*args) if reverse else oracle_for(inp)
+    _check(inp, runs[0][0].cpu().numpy(), runs[0][1].cpu().numpy(), o_ref, s_ref, TOL_BF16,
+           f"ragged last chunk {workload} T={T} reverse={reverse}")
+
+
 def test_streaming_rollout_equals_one_pass():
     w = WORKLOADS["stream_3f_x10"]
     _say("case stream_3f_x10: 10 chunk steps of 2,640 tokens")
