@@ -434,9 +434,9 @@ __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (kOutBf16)
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val[t][e]), ro, int(ob[t][e]), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val[t][e]), ro, int(ob[t][e]), 0, kStreamStore);
         else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[t][e]), ro, int(ob[t][e]), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[t][e]), ro, int(ob[t][e]), 0, kStreamStore);
       }
     }
   }
