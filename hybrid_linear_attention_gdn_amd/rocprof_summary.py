@@ -3,7 +3,12 @@
 Kernel times of a ``rocprofv3 --kernel-trace --stats`` run::
 
     python -m hybrid_linear_attention_gdn_amd.rocprof_summary stats RUN_DIR \\
-        --command "<the rocprofv3 command>" [--bench-log LOG] > profiles/<kernel>_<workload>_kernel_trace.md
+        --command "<the rocprofv3 command>" [--bench-log LOG] \\
+        [--window KERNEL FIRST COUNT] > profiles/<kernel>_<workload>_kernel_trace.md
+
+``--window`` adds the mean duration of dispatches FIRST .. FIRST + COUNT - 1
+of the kernel, in start order, from the run's kernel_trace.csv: the timed
+steps of a bench run that warms up first.
 
 Per-kernel means of a ``rocprofv3 --pmc`` run of rocprofv3's derived metrics
 (MfmaUtil, LdsBankConflict, ...)::
@@ -123,7 +128,25 @@ def stats(args) -> str:
         elif b:
             out += ["", f"bench.py's own HIP-event timing in the same run: {1e3 * b.get('ms_per_step', 0.0):.1f} us "
                         f"per step ({b.get('value')} {b.get('unit')})."]
+    if args.window:
+        name, first, count = args.window[0], int(args.window[1]), int(args.window[2])
+        mean, total = window_mean_us(args.run_dir, name, first, count)
+        out += ["", f"Dispatches {first} .. {first + count - 1} of {total} of `{name}` in start order (the timed "
+                    f"steps): mean {mean:.1f} us per dispatch."]
     return "\n".join(out) + "\n"
+
+
+def window_mean_us(directory: str, kernel: str, first: int, count: int):
+    """(mean duration in us of dispatches first .. first + count - 1 of the
+    kernels whose name contains `kernel`, ordered by start, number of such
+    dispatches in the run)."""
+    path = _one(directory, "kernel_trace.csv")
+    rows = [r for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    sel = rows[first:first + count]
+    if count <= 0 or len(sel) < count:
+        raise SystemExit(f"{len(rows)} dispatches of {kernel}: no window [{first}, {first + count})")
+    return statistics.mean((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel), len(rows)
 
 
 def counter_by_kernel(directory: str, counter: str):
@@ -237,6 +260,7 @@ def main(argv=None):
     s.add_argument("run_dir")
     s.add_argument("--command", required=True)
     s.add_argument("--bench-log")
+    s.add_argument("--window", nargs=3, metavar=("KERNEL", "FIRST", "COUNT"))
     c = sub.add_parser("counters")
     c.add_argument("run_dir")
     c.add_argument("--command", required=True)

@@ -81,3 +81,25 @@ def test_counters_table(tmp_path, capsys):
     assert "| `scan_kernel<false, false, false, false>` | 2 | 15 | 0.375 |" in out
     assert "neg_kernel" not in out
     assert "MfmaUtil:" in out and "LdsBankConflict:" in out
+
+
+def test_window_mean_takes_the_timed_dispatches_in_start_order(tmp_path):
+    """Dispatches listed out of start order; other kernels interleaved; the
+    window counts only the named kernel's dispatches, ordered by start."""
+    d = tmp_path / "kt"
+    os.makedirs(d)
+    rows = []  # (name, start, end): durations 10, 20, ..., 60 us at starts 0, 100, ..., 500 us
+    for i in range(6):
+        rows.append((CHAIN, 100_000 * i, 100_000 * i + 10_000 * (i + 1)))
+        rows.append((NEG, 100_000 * i + 90_000, 100_000 * i + 95_000))
+    rows.reverse()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for i, (name, s, e) in enumerate(rows):
+            w.writerow(["KERNEL_DISPATCH", i + 1, name, s, e])
+    mean, total = rs.window_mean_us(str(d), "scan_kernel", 2, 3)
+    assert total == 6 and abs(mean - 40.0) < 1e-9  # dispatches 2, 3, 4: 30, 40, 50 us
+    import pytest
+    with pytest.raises(SystemExit):
+        rs.window_mean_us(str(d), "scan_kernel", 4, 3)
