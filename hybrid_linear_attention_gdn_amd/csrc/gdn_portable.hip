@@ -118,6 +118,42 @@ static_assert(intra_lds_floats(kMaxPortableDim, kMaxPortableDim) * 4 <= 160 * 10
                   output_lds_floats(kMaxPortableDim, kMaxPortableDim) * 4 <= 160 * 1024,
               "every portable kernel fits one CU's LDS at the largest head dims");
 
+// out[r][d] = sum_{i <= r, i < n} (L[r][i] w[i]) X[i][d] for the chunk's C rows
+// and the d < nd columns (L lower triangular in LDS, stride ldl; X rows in LDS,
+// stride ldx; out row-major with nd columns).  Thread (rg, dg) forms rows
+// rg + 16 a and columns dg + 16 b (up to 128 columns): per term it reads five
+// L entries and eight X entries for forty products.  Each entry is summed in
+// increasing i, the order of one dot product.
+__device__ __forceinline__ void tri_times_rows(const float *L, int ldl, const float *w, const float *X, int ldx,
+                                               int nd, int n, float *__restrict__ out) {
+  constexpr int RB = C / 16, DB = 8;
+  const int rg = threadIdx.x / 16, dg = threadIdx.x % 16;
+  float acc[RB][DB];
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[a][b] = 0.f;
+  const int iend = min(rg + 16 * (RB - 1) + 1, n);  // the last row's terms
+  for (int i = 0; i < iend; ++i) {
+    float x[DB], l[RB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) x[b] = dg + 16 * b < nd ? X[i * ldx + dg + 16 * b] : 0.f;
+#pragma unroll
+    for (int a = 0; a < RB; ++a) l[a] = L[(rg + 16 * a) * ldl + i] * w[i];
+#pragma unroll
+    for (int a = 0; a < RB; ++a) {
+      const bool in = i <= rg + 16 * a;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) acc[a][b] = in ? fmaf(l[a], x[b], acc[a][b]) : acc[a][b];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+      if (dg + 16 * b < nd) out[(rg + 16 * a) * nd + dg + 16 * b] = acc[a][b];
+}
+
 __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ k, const float *__restrict__ v,
                                                     const float *__restrict__ s_beta,
                                                     const float *__restrict__ s_rk,
@@ -216,20 +252,8 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ k,
   }
   const size_t cbase = ((size_t(ci.b) * H + ci.h) * N + ci.c) * C;
   // W = Tm diag(beta gamma rk) K_raw,  Ut = Tm diag(beta) V
-  for (int idx = threadIdx.x; idx < C * dk; idx += blockDim.x) {
-    const int r = idx / dk, d = idx % dk;
-    float s = 0.f;
-    #pragma unroll 8
-    for (int i = 0; i <= r && i < ci.n; ++i) s = fmaf(Tm[r * ldc + i] * cw[i], Ks[i * ldk + d], s);
-    W[(cbase + r) * dk + d] = s;
-  }
-  for (int idx = threadIdx.x; idx < C * dv; idx += blockDim.x) {
-    const int r = idx / dv, e = idx % dv;
-    float s = 0.f;
-    #pragma unroll 8
-    for (int i = 0; i <= r && i < ci.n; ++i) s = fmaf(Tm[r * ldc + i] * sb[i], Vs[i * ldv + e], s);
-    Ut[(cbase + r) * dv + e] = s;
-  }
+  tri_times_rows(Tm, ldc, cw, Ks, ldk, dk, ci.n, W + cbase * dk);
+  tri_times_rows(Tm, ldc, sb, Vs, ldv, dv, ci.n, Ut + cbase * dv);
 }
 
 // Sequential state pass: one block per (b, h, 16 rows of the state).
@@ -384,6 +408,63 @@ __global__ __launch_bounds__(256) void output_kernel(const float *__restrict__ q
   float *Us = sc + C;  // [C][dv + 1] when u_lds
   if (u_lds) stage_rows(Us, dv + 1, C, dv, ci.n, [&](int i) { return Uc + size_t(i) * dv; });
   __syncthreads();
+  if (u_lds) {
+    // thread (rg, eg) forms rows rg + 16 a and columns eg + 16 b: per term five
+    // reads of one operand and eight of the other for forty products; each
+    // entry is summed in the order of one dot product (over d, then over i)
+    constexpr int RB = C / 16, EB = 8;
+    const int rg = threadIdx.x / 16, eg = threadIdx.x % 16;
+    float acc[RB][EB];
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int b = 0; b < EB; ++b) acc[a][b] = 0.f;
+    for (int d = 0; d < dk; ++d) {
+      float qv[RB], sv[EB];
+#pragma unroll
+      for (int a = 0; a < RB; ++a) qv[a] = Qs[(rg + 16 * a) * ldk + d];
+#pragma unroll
+      for (int b = 0; b < EB; ++b) sv[b] = eg + 16 * b < dv ? KS[(eg + 16 * b) * ldk + d] : 0.f;
+#pragma unroll
+      for (int a = 0; a < RB; ++a)
+#pragma unroll
+        for (int b = 0; b < EB; ++b) acc[a][b] = fmaf(qv[a], sv[b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int b = 0; b < EB; ++b) acc[a][b] = sc[rg + 16 * a] * acc[a][b];
+    const int iend = min(rg + 16 * (RB - 1) + 1, ci.n);
+    for (int i = 0; i < iend; ++i) {
+      float pv[RB], uv[EB];
+#pragma unroll
+      for (int a = 0; a < RB; ++a) pv[a] = P[(rg + 16 * a) * ldc + i];
+#pragma unroll
+      for (int b = 0; b < EB; ++b) uv[b] = eg + 16 * b < dv ? Us[i * (dv + 1) + eg + 16 * b] : 0.f;
+#pragma unroll
+      for (int a = 0; a < RB; ++a) {
+        const bool in = i <= rg + 16 * a;
+#pragma unroll
+        for (int b = 0; b < EB; ++b) acc[a][b] = in ? fmaf(pv[a], uv[b], acc[a][b]) : acc[a][b];
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < RB; ++a) {
+      const int r = rg + 16 * a;
+      if (r >= ci.n) continue;
+#pragma unroll
+      for (int b = 0; b < EB; ++b) {
+        const int e = eg + 16 * b;
+        if (e >= dv) continue;
+        const size_t oi = row(r, dv) + e;
+        if constexpr (sizeof(TOut) == 2)
+          o[oi] = f32_to_bf16(acc[a][b]);
+        else
+          o[oi] = acc[a][b];
+      }
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < ci.n * dv; idx += blockDim.x) {
     const int r = idx / dv, e = idx % dv;
     float qs = 0.f;
