@@ -110,22 +110,6 @@ __device__ __forceinline__ f32x4 mma_h(const F32 &a, const F32 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
                                                 0, 0);
 }
-// A 16-deep fp16 block on the 16x16x16 fp16 instruction: slots 0-3 of each
-// operand (k = 4g..4g+3 of lane group g; the same values the padded 32-deep
-// form holds in its slots 0-3).  Used only for the last product of a chain
-// whose result is next read by vector-ALU code, at least one chunk's work
-// before any product takes it as its accumulator: where a 16x16x32 product
-// reads a 16x16x16 result as its accumulator shortly after, the tails stay
-// padded.
-__device__ __forceinline__ f32x4 mma_h16(const F32 &a, const F32 &b, f32x4 c) {
-  typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-  struct W2 {
-    uint32_t w[2];
-  };
-  const W2 a2{{a.w[0], a.w[1]}}, b2{{b.w[0], b.w[1]}};
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a2), __builtin_bit_cast(f16x4_t, b2), c, 0,
-                                               0, 0);
-}
 // four fp32 -> four fp16 (round to nearest even), element order kept
 __device__ __forceinline__ uint2 pack_f16x4(const f32x4 &v) {
   return make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));

@@ -149,10 +149,8 @@ __device__ __forceinline__ F32 kq_frag(const char *img, int t, int kb, int lane)
 }
 // acc[t] += rows(t) x S'^T over d_k for the five token tiles (fp16 operands):
 // five independent chains of four products (a chain's next product issues
-// five products later, past the instruction's dependent latency).
-// kNativeTail: the 16-deep last block on the 16x16x16 instruction, for callers
-// that read acc with vector-ALU code next.
-template <bool kNativeTail>
+// five products later, past the instruction's dependent latency).  The
+// 16-deep last block runs on the 16x16x32 instruction with zero slots 4-7.
 __device__ __forceinline__ void rows_times_S(const char *img, int lane, const F32 *Sop, f32x4 *acc) {
   F32 f[4][CT];
 #pragma unroll
@@ -163,7 +161,7 @@ __device__ __forceinline__ void rows_times_S(const char *img, int lane, const F3
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int t = 0; t < CT; ++t)
-      acc[t] = (kNativeTail && kb == 3) ? mma_h16(f[kb][t], Sop[kb], acc[t]) : mma_h(f[kb][t], Sop[kb], acc[t]);
+      acc[t] = mma_h(f[kb][t], Sop[kb], acc[t]);
 }
 
 // ---------------------------------------------------------------------------
@@ -228,7 +226,7 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
     f32x4 Y[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) Y[t] = zero4();
-    rows_times_S<true>(buf + kRecK, lane, Sop, Y);  // Y is read by the R sum below
+    rows_times_S(buf + kRecK, lane, Sop, Y);
     // ---- R = a V + 2^sS Y
     f32x4 Racc[CT];
 #pragma unroll
@@ -296,8 +294,8 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
     const F32 Rb1 = f32_of(rw[2].x, rw[2].y, rw[3].x, rw[3].y);
     const F32 Rb2 = f32_of(rw[4].x, rw[4].y, 0u, 0u);
     compute_barrier();  // Y(c): chunk c's record and V are no longer read
-    // ---- S^T <- gamma_n S^T + 2^sR M R': seven chains of three products, the
-    // 16-deep last one on the 16x16x16 instruction (St is next read by build_S)
+    // ---- S^T <- gamma_n S^T + 2^sR M R': seven chains of three products (the
+    // 16-deep last one padded, as everywhere in this kernel)
     GDN_RARELY(sR) {
       f32x4 U[NT];
 #pragma unroll
@@ -306,7 +304,7 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
       for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-          U[i] = kb == 2 ? mma_h16(mf[kb][i], Rb2, U[i]) : mma_h(mf[kb][i], kb == 0 ? Rb0 : Rb1, U[i]);
+          U[i] = mma_h(mf[kb][i], kb == 0 ? Rb0 : kb == 1 ? Rb1 : Rb2, U[i]);
 #pragma unroll
       for (int i = 0; i < NT; ++i)
 #pragma unroll
@@ -316,7 +314,7 @@ __device__ __forceinline__ void state_role(const ScanArgs &a, int b, int h, int 
       for (int kb = 0; kb < 3; ++kb)
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-          St[i] = kb == 2 ? mma_h16(mf[kb][i], Rb2, St[i]) : mma_h(mf[kb][i], kb == 0 ? Rb0 : Rb1, St[i]);
+          St[i] = mma_h(mf[kb][i], kb == 0 ? Rb0 : kb == 1 ? Rb1 : Rb2, St[i]);
     }
     // S of chunk c + 1: the output wave read S of chunk c before Y(c)
     build_S();
@@ -394,7 +392,7 @@ __device__ __forceinline__ void output_role(const ScanArgs &a, int b, int h, int
     f32x4 O[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) O[t] = zero4();
-    rows_times_S<false>(buf + kRecQ, lane, Sop, O);  // O feeds the P'' V products
+    rows_times_S(buf + kRecQ, lane, Sop, O);
     GDN_RARELY(sS) {
 #pragma unroll
       for (int t = 0; t < CT; ++t)
