@@ -129,6 +129,28 @@ def test_ragged_last_chunk_full_width(T, reverse, workload):
            f"ragged last chunk {workload} T={T} reverse={reverse}")
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+def test_more_state_workgroups_than_cus(reverse):
+    """B = 4 x 24 heads: 96 (b, h) units, so 384 state-pass workgroups, more
+    than the 256 CUs, which then do not all run at once (no workgroup waits on
+    another, so the order they run in does not matter).  A ragged 1,999-token
+    sequence with an entry state; every unit against the oracle, and two calls
+    bitwise equal."""
+    from oracle import bidirectional as BD
+    from hybrid_linear_attention_gdn_amd.inputs import Workload
+    w = Workload("wide", 4, 24, 1, 10**9, "bf16", 31, state_std=0.02)
+    inp = make_inputs(w, seq_len=1999, frame_tokens=880)
+    _say(f"case 4 x 24 heads, T=1999, reverse={reverse}")
+    q, k, v, g, beta, s0 = to_device(inp)
+    o1, st1 = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=reverse)
+    o2, st2 = gdn.gdn_fwd(q, k, v, g, beta, s0, reverse=reverse)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(st1, st2)
+    args = (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state0)
+    o_ref, s_ref = BD.reverse_scan(*args) if reverse else oracle_for(inp)
+    _check(inp, o1.cpu().numpy(), st1.cpu().numpy(), o_ref, s_ref, TOL_BF16, f"4 x 24 heads reverse={reverse}")
+
+
 def test_streaming_rollout_equals_one_pass():
     w = WORKLOADS["stream_3f_x10"]
     _say("case stream_3f_x10: 10 chunk steps of 2,640 tokens")
