@@ -85,6 +85,26 @@ def test_fp8_equals_bf16_on_the_same_values(B):
            f"fp8 T=5063 B={B}, heads 0, 19")
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+def test_fp8_equals_bf16_full_shape_dense_gates(reverse):
+    """The fp8 and bf16 instantiations of the kernels are scheduled
+    differently, so bitwise equality of their results on the same values, at
+    the full 27,280 x 20 shape with a gate on every token (every chunk then
+    takes the decay and intra-chunk paths), in both directions and both o
+    types, checks that neither schedule reads a value too early."""
+    w = WORKLOADS["clip_241f_fp8"]
+    inp = make_inputs(w, frame_tokens=1)
+    q, k, v, g, beta, s0 = to_device(inp)
+    _say(f"case fp8 == bf16, 27,280 x 20, dense gates, reverse={reverse}")
+    for o_dtype in (torch.float32, torch.bfloat16):
+        o8, s8 = gdn.gdn_fwd(q, k, v, g, beta, s0, o_dtype=o_dtype, reverse=reverse)
+        o16, s16 = gdn.gdn_fwd(_as_bf16(q), _as_bf16(k), _as_bf16(v), g, beta, s0, o_dtype=o_dtype,
+                               reverse=reverse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o8.float()).all()
+        assert torch.equal(o8, o16) and torch.equal(s8, s16)
+
+
 def test_fp8_streaming_rollout_equals_one_pass():
     w = WORKLOADS["clip_241f_fp8"]
     Tc, calls = 2640, 4
