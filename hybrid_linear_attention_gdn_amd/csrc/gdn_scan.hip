@@ -464,9 +464,12 @@ __device__ __forceinline__ void copy_role(const ScanArgs &a, int b, int h, int t
   const uint32_t head_off = uint32_t(h) * D * G::kElem;
   constexpr int kLast = kCopyWaves - 1;
   // record pieces of this wave per chunk, the first kA of them in part A;
-  // part B holds the rest and (L == 3) the V rows.
+  // part B holds the rest and (L == 3) the V rows.  Part A is about a sixth
+  // of the wave's copies (the 241-frame layer measured 0.515 / 0.513 / 0.502 /
+  // 0.502 / 0.503 ms with a half / third / quarter / sixth / none in part A):
+  // copies issued right after Y(c) slow the state waves' update that follows.
   constexpr int kPieces = (kRecInstr - L + kCopyWaves - 1) / kCopyWaves;
-  constexpr int kA = (kPieces + (L == kLast ? G::kVInstr : 0)) / 2;
+  constexpr int kA = (kPieces + (L == kLast ? G::kVInstr : 0)) / 6;
   constexpr int cN = kPieces + (L == kLast ? G::kVInstr : 0);
   static_assert(cN + kA < 64, "vmcnt holds 63");
   // part A (kPart 0) or B (kPart 1) of chunk c's copies
